@@ -1,0 +1,153 @@
+/*
+ * rlk.h -- C ABI of the batch-invariant selected-token log-probability
+ * library for MI355X (gfx950).  Library: invariant_logprob_amd/librlk.so.
+ *
+ * What is computed.  For token row i with logits x_i (length V) and target
+ * t_i:
+ *     lse_i  = log(sum_j exp(x_ij))
+ *     logp_i = x_i[t_i] - lse_i
+ * and for the backward, with upstream gradient g_i of logp_i:
+ *     dlogits_ij = g_i * ([j == t_i] - exp(x_ij - lse_i)).
+ * The pages name this operator -- the selected logprob ("logp /
+ * batch_invariant_logp") and its fusion with the lm_head projection
+ * ("linear_logp") -- in the operator chain of page "docs(ws1):
+ * batch-invariance contract RFC", section "First-Divergence Localization",
+ * and the dense vs indexed selected-logprob paths of page "[RFC]
+ * Batch-Invariant RL Kernel Suite for Train-Inference Consistency", section
+ * "Scope"; they do not write the formula, so the textbook definition above is
+ * used.  Inputs are bf16, every intermediate and every output is fp32 (page
+ * "[WS1 Test] #154 dtype pin + #152 KV path + #153 bwd invariance + #150
+ * chain gate", section "Workstream 1 - #154 dtype coverage", scope table:
+ * BF16 inputs with FP32 accumulation).
+ *
+ * Batch invariance.  Each active row's fp32 outputs are bit-identical
+ * whatever the number of rows N, the row's position, the content of the
+ * other rows, padding rows, varlen packing, or how the rows are split across
+ * calls (page "[RFC] ...", maintainer reply, relation I: bitwise, atol = rtol
+ * = 0; page "docs(ws1): ...", transform classes T1-T6).  Every reduction has
+ * a schedule fixed by V (and H) alone: fixed vocabulary chunks, a fixed
+ * wavefront shuffle tree and LDS combine, partials merged in ascending chunk
+ * order, and no atomics (page "[WS1 Test] ...", section "Workstream 3 -
+ * #153", scope items 2 and 4).  Kernel choice never depends on N.
+ *
+ * Conventions shared by every entry point.
+ *  - All tensor pointers are DEVICE pointers on the current HIP device.
+ *    bf16 tensors are passed as raw 16-bit patterns (const void*).
+ *  - Row-major layouts with an explicit leading dimension in elements.
+ *    bf16 operands need ld % 8 == 0 and a 16-byte aligned base; fp32
+ *    gradients need ld_g % 4 == 0 and a 16-byte aligned base.  Otherwise
+ *    RLK_ERR_UNSUPPORTED: the column-to-lane map must not depend on
+ *    alignment, so misaligned heads are never peeled.
+ *  - targets: int64 [N].  mask: uint8 [N], nonzero = active token, NULL =
+ *    every row active.  The mask is the sole authority on which rows count
+ *    (page "docs(ws1): ...", section "InvarianceFixture": the action mask
+ *    defines the active token set).  An inactive row's logits, hidden row
+ *    and target are never read for its own outputs; its outputs are +0.0.
+ *    An ACTIVE row whose target lies outside [0, V) gets NaN outputs (logp,
+ *    and every dlogits entry of that row); nothing is read out of bounds.
+ *  - Calls are asynchronous on `stream`; the library never allocates, frees
+ *    or synchronises, holds no mutable state, and is reentrant.  The caller
+ *    owns every buffer.  Outputs are fully overwritten (no accumulation).
+ *  - N == 0 is a no-op returning RLK_OK.  Arguments are validated before any
+ *    launch; on error nothing is launched.
+ *  - There is no fallback path: the kernels exist for gfx950 only.
+ */
+#ifndef RLK_H
+#define RLK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum rlk_status {
+  RLK_OK = 0,
+  RLK_ERR_INVALID_ARG = 1, /* null required pointer, negative or zero size,
+                              ld < V (or < H), workspace too small,
+                              lse missing in the backward */
+  RLK_ERR_UNSUPPORTED = 2, /* alignment / leading-dimension rule violated,
+                              or a size beyond the supported range
+                              (V, H < 2^31, N * ld < 2^62) */
+  RLK_ERR_LAUNCH = 3       /* the HIP runtime reported an error at launch */
+};
+
+/*
+ * Selected-token logprob from materialised logits.
+ *   logits : bf16 [N, ld], row-major, ld >= V, ld % 8 == 0, 16-B aligned.
+ *   targets: int64 [N].  mask: uint8 [N] or NULL.
+ *   logp   : fp32 [N] (required).  lse: fp32 [N] or NULL.
+ * One workgroup per row streams its V logits once from HBM; the row's
+ * reduction schedule depends on V only.
+ */
+int rlk_logp_selected(const void* logits, int64_t ld, const int64_t* targets,
+                      const uint8_t* mask, int64_t N, int64_t V, float* logp,
+                      float* lse, hipStream_t stream);
+
+/*
+ * Bytes of device workspace rlk_linear_logp needs for (N, V, H): one
+ * (max, sum) fp32 pair per row and 256-wide vocabulary chunk, plus one fp32
+ * target logit per row, rounded up to 256 bytes.
+ */
+size_t rlk_linear_logp_workspace_size(int64_t N, int64_t V, int64_t H);
+
+/*
+ * Fused lm_head projection + selected logprob (the pages' "linear_logp"):
+ * z_i = W . h_i computed with bf16 MFMA and fp32 accumulation in a fixed K
+ * order, never rounded to bf16, reduced by an online log-sum-exp per
+ * 256-wide vocabulary chunk; chunk partials are merged per row in ascending
+ * chunk order.
+ *   hidden : bf16 [N, ld_h], ld_h >= H, ld_h % 8 == 0, 16-B aligned.
+ *   weight : bf16 [V, ld_w] (nn.Linear layout, H contiguous), ld_w >= H,
+ *            ld_w % 8 == 0, 16-B aligned.  H % 8 == 0.
+ *   logp   : fp32 [N] (required).  lse: fp32 [N] or NULL.
+ *   workspace: device memory of at least
+ *            rlk_linear_logp_workspace_size(N, V, H) bytes, 16-B aligned;
+ *            its contents on entry are ignored and on return undefined.
+ */
+int rlk_linear_logp(const void* hidden, int64_t ld_h, const void* weight,
+                    int64_t ld_w, const int64_t* targets, const uint8_t* mask,
+                    int64_t N, int64_t V, int64_t H, float* logp, float* lse,
+                    void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/*
+ * Backward of the selected logprob with respect to the logits:
+ *   grad_logits[i, j] = grad_logp[i] * ([j == t_i] - exp(x_ij - lse_i)),
+ * fp32 [N, ld_g] (ld_g >= V, ld_g % 4 == 0, 16-B aligned); columns >= V are
+ * not written.  Inactive rows are written as +0.0.  No reduction is
+ * involved, so each element depends only on its own row (page "[WS1 Test]
+ * ...", section "Workstream 3 - #153": gradient batch invariance).
+ *   Logits mode : `logits` non-NULL (bf16 [N, ld]); hidden/weight ignored.
+ *   Fused mode  : `logits` NULL; x_i = W . h_i is recomputed with exactly
+ *                 the tiles and K order rlk_linear_logp uses (hidden
+ *                 [N, ld_h], weight [V, ld_w], H as there).
+ *   lse        : fp32 [N], required -- the forward's output for these rows.
+ *   grad_logp  : fp32 [N], required (the upstream gradient g).
+ */
+int rlk_logp_backward(const void* logits, int64_t ld, const void* hidden,
+                      int64_t ld_h, const void* weight, int64_t ld_w,
+                      int64_t H, const int64_t* targets, const uint8_t* mask,
+                      const float* lse, const float* grad_logp, int64_t N,
+                      int64_t V, float* grad_logits, int64_t ld_g,
+                      hipStream_t stream);
+
+/* Static string naming a status code ("RLK_OK", ...); "unknown" otherwise. */
+const char* rlk_status_string(int status);
+
+/*
+ * Static string describing this build: library version, target
+ * architecture, source revision and a hash of the kernel constants
+ * (tile and chunk sizes).  Invariance records carry it, since bits are only
+ * promised stable within one build.
+ */
+const char* rlk_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLK_H */

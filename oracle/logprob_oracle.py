@@ -1,0 +1,195 @@
+"""Plain fp64 CPU oracle for the batch-invariant selected-token log-probability.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the test suite, the smoke check and the benchmark's
+CPU-baseline leg use it.  It shares no code, header, table or helper with the
+HIP library; the two meet only at the seeded inputs.
+
+What it computes, and where it comes from
+-----------------------------------------
+The pages name the operator -- "selected logprob" / ``logp`` /
+``batch_invariant_logp`` and the fused ``linear_logp`` (page "docs(ws1):
+batch-invariance contract RFC", section "First-Divergence Localization", the
+operator chain, entries 6-8; page "[RFC] Batch-Invariant RL Kernel Suite for
+Train-Inference Consistency", section "Scope", dense vs indexed
+selected-logprob paths) -- but never write its formula.  The oracle therefore
+uses the textbook definition: for a row of logits ``x`` and a target index
+``t``
+
+    lse(x)  = log( sum_j exp(x_j) )
+    logp    = x_t - lse(x)
+    dlogp/dx_j = [j == t] - exp(x_j - lse(x))          (backward, times g)
+
+Inputs are bf16 (page "[WS1 Test] #154 dtype pin + ...", section "Workstream
+1 - #154 dtype coverage", scope table: BF16 inputs, FP32 accumulation, FP32
+gold).  This oracle is stricter than an fp32 gold: every bf16 value is decoded
+exactly and all arithmetic is float64.
+
+Masked (inactive) rows are excluded from comparisons (page "docs(ws1): ...",
+section "InvarianceFixture", requirement 3; page "[WS1 Test] ...", section
+"Workstream 3 - #153", logical-workload identity: padding tokens are
+excluded); the oracle reports zeros for them, which is also what the library
+writes.
+
+Parity is pinned by ``tests/oracle_pins.py`` (brute force on tiny vocabularies,
+closed forms, invariants, finite differences); every function here has pins.
+"""
+
+import numpy as np
+
+LN2 = float(np.log(2.0))
+
+
+def bf16_to_f64(bits):
+    """Exact bf16 -> float64 decode of raw 16-bit patterns.
+
+    A bf16 value is the upper half of an IEEE float32, so shifting the 16 bits
+    into the high half of a 32-bit word and reinterpreting it is exact.
+    """
+    u16 = np.ascontiguousarray(bits, dtype=np.uint16)
+    u32 = u16.astype(np.uint32) << np.uint32(16)
+    return u32.view(np.float32).astype(np.float64)
+
+
+def _active(mask, n):
+    if mask is None:
+        return np.ones(n, dtype=bool)
+    return np.asarray(mask).astype(bool).reshape(n)
+
+
+def logsumexp_rows(x):
+    """Row-wise natural-log sum of exponentials of a float64 matrix.
+
+    The maximum is subtracted before exponentiating (the usual overflow-safe
+    rewriting; mathematically identical).  -inf entries contribute nothing;
+    a row containing +inf or NaN yields NaN; an all -inf row yields NaN.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m = np.max(x, axis=1)
+    out = np.full(x.shape[0], np.nan)
+    ok = np.isfinite(m) & ~np.isnan(x).any(axis=1)
+    if ok.any():
+        xs = x[ok]
+        mm = m[ok]
+        with np.errstate(invalid="ignore", over="ignore"):
+            s = np.sum(np.exp(xs - mm[:, None]), axis=1)
+        out[ok] = mm + np.log(s)
+    return out
+
+
+def selected_logp_from_f64(x, targets, mask=None):
+    """logp and lse for float64 logits ``x`` [N, V].
+
+    Returns (logp, lse) as float64 [N].  Inactive rows give 0 for both.  An
+    active row whose target is outside [0, V) is an error.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n, v = x.shape
+    t = np.asarray(targets, dtype=np.int64).reshape(n)
+    act = _active(mask, n)
+    logp = np.zeros(n)
+    lse = np.zeros(n)
+    if not act.any():
+        return logp, lse
+    if np.any((t[act] < 0) | (t[act] >= v)):
+        raise ValueError("active row with target outside [0, V)")
+    rows = np.nonzero(act)[0]
+    lse_a = logsumexp_rows(x[rows])
+    lse[rows] = lse_a
+    logp[rows] = x[rows, t[rows]] - lse_a
+    return logp, lse
+
+
+def logp_selected(logits_bits, targets, mask=None, block_rows=256):
+    """Selected-token logprob from bf16 logits given as raw uint16 [N, V].
+
+    Rows are processed in blocks only to bound host memory.
+    """
+    bits = np.asarray(logits_bits, dtype=np.uint16)
+    n, v = bits.shape
+    t = np.asarray(targets, dtype=np.int64).reshape(n)
+    act = _active(mask, n)
+    logp = np.zeros(n)
+    lse = np.zeros(n)
+    for r0 in range(0, n, block_rows):
+        r1 = min(n, r0 + block_rows)
+        lp, ls = selected_logp_from_f64(bf16_to_f64(bits[r0:r1]), t[r0:r1], act[r0:r1])
+        logp[r0:r1] = lp
+        lse[r0:r1] = ls
+    return logp, lse
+
+
+def linear_logits(hidden_bits, weight_bits):
+    """Logits of the lm_head projection, z = h . W^T, in float64.
+
+    ``hidden_bits`` is bf16 [N, H], ``weight_bits`` is bf16 [V, H] (the
+    nn.Linear weight layout: one row per vocabulary entry, H contiguous).
+    Each bf16 x bf16 product is exact in float64; the sum is a float64 BLAS
+    dot product.
+    """
+    h = bf16_to_f64(hidden_bits)
+    w = bf16_to_f64(weight_bits)
+    if h.shape[1] != w.shape[1]:
+        raise ValueError("hidden and weight disagree on H")
+    return h @ w.T
+
+
+def linear_logp(hidden_bits, weight_bits, targets, mask=None, block_rows=256):
+    """Fused lm_head + selected logprob: (logp, lse) float64 [N].
+
+    The logits are never rounded: they stay float64 here (the library keeps
+    them float32 and never rounds them to bf16).
+    """
+    h = np.asarray(hidden_bits, dtype=np.uint16)
+    w = bf16_to_f64(weight_bits)
+    n = h.shape[0]
+    t = np.asarray(targets, dtype=np.int64).reshape(n)
+    act = _active(mask, n)
+    logp = np.zeros(n)
+    lse = np.zeros(n)
+    for r0 in range(0, n, block_rows):
+        r1 = min(n, r0 + block_rows)
+        z = bf16_to_f64(h[r0:r1]) @ w.T
+        lp, ls = selected_logp_from_f64(z, t[r0:r1], act[r0:r1])
+        logp[r0:r1] = lp
+        lse[r0:r1] = ls
+    return logp, lse
+
+
+def logp_backward_from_f64(x, targets, mask, lse, grad_logp):
+    """Gradient of g_i * logp_i with respect to the logits row x_i.
+
+    d[i, j] = g_i * ([j == t_i] - exp(x_ij - lse_i)) for active rows, and 0
+    for inactive rows (page "[WS1 Test] ...", section "Workstream 3 - #153":
+    padding is excluded and the upstream gradients are identical across
+    configurations; the formula itself is the textbook derivative of the
+    definition above).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n, v = x.shape
+    t = np.asarray(targets, dtype=np.int64).reshape(n)
+    act = _active(mask, n)
+    g = np.asarray(grad_logp, dtype=np.float64).reshape(n)
+    ls = np.asarray(lse, dtype=np.float64).reshape(n)
+    d = np.zeros((n, v))
+    rows = np.nonzero(act)[0]
+    if rows.size:
+        if np.any((t[rows] < 0) | (t[rows] >= v)):
+            raise ValueError("active row with target outside [0, V)")
+        p = np.exp(x[rows] - ls[rows, None])
+        onehot = np.zeros((rows.size, v))
+        onehot[np.arange(rows.size), t[rows]] = 1.0
+        d[rows] = g[rows, None] * (onehot - p)
+    return d
+
+
+def logp_backward(logits_bits, targets, mask, lse, grad_logp):
+    """Backward from bf16 logits (raw uint16 [N, V]); float64 [N, V]."""
+    return logp_backward_from_f64(bf16_to_f64(logits_bits), targets, mask, lse, grad_logp)
+
+
+def linear_logp_backward(hidden_bits, weight_bits, targets, mask, lse, grad_logp):
+    """Backward of the fused path with respect to the (never materialised)
+    logits z = h . W^T; float64 [N, V]."""
+    z = linear_logits(hidden_bits, weight_bits)
+    return logp_backward_from_f64(z, targets, mask, lse, grad_logp)

@@ -1,0 +1,364 @@
+"""Pins for the fp64 oracle: facts that hold independently of its code.
+
+Each pin takes an oracle-like object ``o`` (the real ``oracle`` package, or a
+deliberately broken copy in the mutant tests) and raises AssertionError when
+``o`` disagrees with something fixed by mathematics rather than by the
+oracle's own implementation:
+
+* brute force on tiny vocabularies, through a separate pure-Python path
+  (``math.exp`` + ``math.fsum``, no max shift);
+* closed forms: uniform rows give -ln V, V = 2 gives -log1p(exp(x1 - x0)),
+  one peaked entry gives -ln(1 + (V - 1) e^{-L});
+* invariants: sum_t exp(logp_t) = 1, logp_t - logp_u = x_t - x_u, shift
+  invariance, sum_j dlogits_ij = 0;
+* special cases of the projection: one-hot hidden picks a weight column, a
+  zero hidden row gives uniform logits, identical weight rows give uniform
+  logits, and exact-sum spot checks of z;
+* central finite differences of the forward for the backward.
+
+The bf16 test values used here are chosen to be exactly representable, so the
+pins do not depend on any rounding routine.
+"""
+
+import math
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# small exact bf16 helpers (test side; independent of the oracle's decoder)
+
+
+def to_bf16_bits_exact(values):
+    """Encode float values that are exactly representable in bf16."""
+    f32 = np.asarray(values, dtype=np.float32)
+    u32 = f32.view(np.uint32)
+    if np.any(u32 & np.uint32(0xFFFF)):
+        raise ValueError("value not exactly representable in bf16")
+    return (u32 >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_rne_bits(values):
+    """Round float32 values to bf16 (round to nearest even), as raw bits."""
+    u32 = np.asarray(values, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u32 + 0x7FFF + ((u32 >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bits_to_float(bits):
+    """Test-side bf16 decode through Python floats (struct-free)."""
+    u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u32.view(np.float32).astype(np.float64)
+
+
+def grid_values(rng, shape, lo=-8.0, hi=8.0, step=0.125):
+    """Random values on a grid that bf16 represents exactly."""
+    k = rng.integers(int(lo / step), int(hi / step) + 1, size=shape)
+    return k.astype(np.float64) * step
+
+
+def brute_logp(row, t):
+    """log softmax(row)[t] through math.exp/math.fsum, no max shift."""
+    total = math.fsum(math.exp(v) for v in row)
+    return row[t] - math.log(total)
+
+
+# ---------------------------------------------------------------------------
+# forward pins
+
+
+def pin_brute_force_tiny(o):
+    rng = np.random.default_rng(11)
+    for v in range(1, 17):
+        vals = grid_values(rng, (6, v))
+        bits = to_bf16_bits_exact(vals)
+        t = rng.integers(0, v, size=6)
+        logp, lse = o.logp_selected(bits, t)
+        for i in range(6):
+            row = [float(a) for a in vals[i]]
+            ref = brute_logp(row, int(t[i]))
+            assert abs(logp[i] - ref) <= 1e-13, (v, i, logp[i], ref)
+            ref_lse = math.log(math.fsum(math.exp(a) for a in row))
+            assert abs(lse[i] - ref_lse) <= 1e-13, (v, i, lse[i], ref_lse)
+
+
+def pin_uniform_rows(o):
+    for v in (1, 2, 3, 1024, 32000):
+        for c in (0.0, 1.5, -37.0, 1000.0, -1000.0):
+            bits = to_bf16_bits_exact(np.full((2, v), c))
+            t = np.array([0, v - 1])
+            logp, lse = o.logp_selected(bits, t)
+            tol = 8 * np.finfo(np.float64).eps * (abs(c) + math.log(v) + 1)
+            assert np.all(np.abs(logp + math.log(v)) <= tol), (v, c, logp)
+            assert np.all(np.abs(lse - (c + math.log(v))) <= tol), (v, c, lse)
+            if v == 1:
+                assert np.all(logp == 0.0), (c, logp)
+
+
+def pin_uniform_large_vocab(o):
+    # the two vocabularies of the workloads, through the f64 entry point
+    for v in (128256, 151936):
+        x = np.full((1, v), -2.5)
+        logp, _ = o.selected_logp_from_f64(x, [v // 3])
+        assert abs(logp[0] + math.log(v)) <= 1e-12, (v, logp)
+
+
+def pin_two_entries(o):
+    rng = np.random.default_rng(12)
+    vals = grid_values(rng, (40, 2), -16, 16, 0.25)
+    bits = to_bf16_bits_exact(vals)
+    logp, _ = o.logp_selected(bits, np.zeros(40, dtype=np.int64))
+    ref = -np.log1p(np.exp(vals[:, 1] - vals[:, 0]))
+    assert np.max(np.abs(logp - ref)) <= 1e-14, np.max(np.abs(logp - ref))
+    logp1, _ = o.logp_selected(bits, np.ones(40, dtype=np.int64))
+    ref1 = -np.log1p(np.exp(vals[:, 0] - vals[:, 1]))
+    assert np.max(np.abs(logp1 - ref1)) <= 1e-14
+
+
+def pin_peaked_row(o):
+    for v in (2, 17, 1000):
+        for L in (0.5, 4.0, 20.0):
+            row = np.full(v, 1.0)
+            k = v // 2
+            row[k] += L
+            bits = to_bf16_bits_exact(row[None, :])
+            logp_peak, _ = o.logp_selected(bits, [k])
+            ref = -math.log1p((v - 1) * math.exp(-L))
+            assert abs(logp_peak[0] - ref) <= 1e-13, (v, L, logp_peak, ref)
+            other = (k + 1) % v
+            logp_other, _ = o.logp_selected(bits, [other])
+            assert abs(logp_other[0] - (ref - L)) <= 1e-13, (v, L)
+
+
+def pin_probabilities_sum_to_one(o):
+    rng = np.random.default_rng(13)
+    v = 97
+    vals = grid_values(rng, (1, v), -12, 12, 0.0625)
+    bits = np.repeat(to_bf16_bits_exact(vals), v, axis=0)
+    logp, _ = o.logp_selected(bits, np.arange(v))
+    total = math.fsum(math.exp(a) for a in logp)
+    assert abs(total - 1.0) <= 1e-12, total
+
+
+def pin_differences_are_logit_differences(o):
+    rng = np.random.default_rng(14)
+    v = 300
+    vals = grid_values(rng, (1, v), -20, 20, 0.25)
+    bits = np.repeat(to_bf16_bits_exact(vals), 5, axis=0)
+    t = rng.integers(0, v, size=5)
+    logp, _ = o.logp_selected(bits, t)
+    for a in range(5):
+        for b in range(5):
+            d = logp[a] - logp[b]
+            assert abs(d - (vals[0, t[a]] - vals[0, t[b]])) <= 1e-12, (a, b)
+
+
+def pin_shift_invariance(o):
+    rng = np.random.default_rng(15)
+    x = grid_values(rng, (4, 50), -5, 5, 0.5)
+    t = rng.integers(0, 50, size=4)
+    lp0, lse0 = o.selected_logp_from_f64(x, t)
+    lp1, lse1 = o.selected_logp_from_f64(x + 64.0, t)
+    assert np.max(np.abs(lp0 - lp1)) <= 1e-12
+    assert np.max(np.abs((lse1 - lse0) - 64.0)) <= 1e-12
+
+
+def pin_mask_and_targets(o):
+    rng = np.random.default_rng(16)
+    vals = grid_values(rng, (5, 8))
+    bits = to_bf16_bits_exact(vals)
+    t = np.array([1, -100, 3, 999, 0])
+    mask = np.array([1, 0, 1, 0, 1], dtype=np.uint8)
+    logp, lse = o.logp_selected(bits, t, mask)
+    assert logp[1] == 0.0 and lse[1] == 0.0 and logp[3] == 0.0 and lse[3] == 0.0
+    for i in (0, 2, 4):
+        ref = brute_logp([float(a) for a in vals[i]], int(t[i]))
+        assert abs(logp[i] - ref) <= 1e-13
+    try:
+        o.logp_selected(bits, t)  # all rows active: row 1 has target -100
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("active row with an invalid target must raise")
+
+
+def pin_nonfinite(o):
+    ninf = -np.inf
+    x = np.array([[0.0, ninf, 0.0, ninf], [ninf, ninf, ninf, ninf], [1.0, np.inf, 0.0, 0.0],
+                  [np.nan, 0.0, 0.0, 0.0]])
+    logp, lse = o.selected_logp_from_f64(x, [0, 0, 0, 1])
+    assert abs(logp[0] + math.log(2.0)) <= 1e-15, logp[0]
+    assert np.isnan(lse[1]) and np.isnan(lse[2]) and np.isnan(lse[3]), lse
+
+
+# ---------------------------------------------------------------------------
+# projection pins
+
+
+def _rand_bf16(rng, shape, scale):
+    return bf16_rne_bits(rng.standard_normal(shape).astype(np.float32) * np.float32(scale))
+
+
+def pin_projection_spot_checks(o):
+    rng = np.random.default_rng(21)
+    n, v, h = 3, 7, 40   # non-square on purpose: a transposed operand cannot fit
+    hb = _rand_bf16(rng, (n, h), 1.0)
+    wb = _rand_bf16(rng, (v, h), 0.5)
+    z = o.linear_logits(hb, wb)
+    assert z.shape == (n, v), z.shape
+    hf = bits_to_float(hb)
+    wf = bits_to_float(wb)
+    for i in range(n):
+        for j in range(v):
+            ref = math.fsum(float(hf[i, k]) * float(wf[j, k]) for k in range(h))
+            assert abs(z[i, j] - ref) <= 1e-12 * (1 + abs(ref)), (i, j, z[i, j], ref)
+
+
+def pin_projection_one_hot(o):
+    rng = np.random.default_rng(22)
+    v, h = 9, 16
+    wb = _rand_bf16(rng, (v, h), 1.0)
+    hid = np.zeros((h, h))
+    np.fill_diagonal(hid, 1.0)
+    z = o.linear_logits(to_bf16_bits_exact(hid), wb)
+    assert np.array_equal(z, bits_to_float(wb).T), "one-hot hidden must pick weight columns"
+
+
+def pin_projection_zero_hidden_and_equal_rows(o):
+    rng = np.random.default_rng(23)
+    v, h = 33, 24
+    wb = _rand_bf16(rng, (v, h), 1.0)
+    logp, _ = o.linear_logp(np.zeros((2, h), dtype=np.uint16), wb, [0, 5])
+    assert np.max(np.abs(logp + math.log(v))) <= 1e-14
+    row = _rand_bf16(rng, (1, h), 1.0)
+    same = np.repeat(row, v, axis=0)
+    hb = _rand_bf16(rng, (3, h), 1.0)
+    logp2, _ = o.linear_logp(hb, same, [1, 2, 3])
+    assert np.max(np.abs(logp2 + math.log(v))) <= 1e-12
+
+
+def pin_fused_matches_brute_force(o):
+    rng = np.random.default_rng(24)
+    n, v, h = 4, 11, 12
+    hb = _rand_bf16(rng, (n, h), 1.0)
+    wb = _rand_bf16(rng, (v, h), 1.0)
+    t = rng.integers(0, v, size=n)
+    mask = np.array([1, 1, 0, 1], dtype=np.uint8)
+    logp, _ = o.linear_logp(hb, wb, t, mask)
+    hf, wf = bits_to_float(hb), bits_to_float(wb)
+    for i in range(n):
+        if not mask[i]:
+            assert logp[i] == 0.0
+            continue
+        z = [math.fsum(float(hf[i, k]) * float(wf[j, k]) for k in range(h)) for j in range(v)]
+        assert abs(logp[i] - brute_logp(z, int(t[i]))) <= 1e-13
+
+
+# ---------------------------------------------------------------------------
+# backward pins
+
+
+def pin_backward_rows_sum_to_zero(o):
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((6, 200)) * 3
+    t = rng.integers(0, 200, size=6)
+    g = rng.standard_normal(6)
+    _, lse = o.selected_logp_from_f64(x, t)
+    d = o.logp_backward_from_f64(x, t, None, lse, g)
+    assert np.all(np.abs(d.sum(axis=1)) <= 1e-12 * (1 + np.abs(g)))
+    # the target entry carries g * (1 - p_t) > 0 share of the sign of g
+    for i in range(6):
+        assert np.sign(d[i, t[i]]) == np.sign(g[i])
+
+
+def pin_backward_closed_forms(o):
+    v = 10
+    x = np.full((3, v), 2.0)
+    t = np.array([0, 4, 9])
+    g = np.array([1.5, -0.25, 0.0])
+    _, lse = o.selected_logp_from_f64(x, t)
+    d = o.logp_backward_from_f64(x, t, None, lse, g)
+    for i in range(3):
+        ref = np.full(v, -g[i] / v)
+        ref[t[i]] += g[i]
+        assert np.max(np.abs(d[i] - ref)) <= 1e-15, (i, d[i], ref)
+    x1 = np.array([[3.0], [-7.0]])
+    _, lse1 = o.selected_logp_from_f64(x1, [0, 0])
+    d1 = o.logp_backward_from_f64(x1, [0, 0], None, lse1, [2.0, -1.0])
+    assert np.max(np.abs(d1)) <= 1e-15, d1
+
+
+def pin_backward_finite_differences(o):
+    rng = np.random.default_rng(32)
+    for v in (2, 5, 16):
+        x = rng.standard_normal((1, v)) * 2
+        t = [int(rng.integers(0, v))]
+        g = float(rng.standard_normal())
+        _, lse = o.selected_logp_from_f64(x, t)
+        d = o.logp_backward_from_f64(x, t, None, lse, [g])
+        eps = 1e-6
+        for j in range(v):
+            xp = x.copy()
+            xm = x.copy()
+            xp[0, j] += eps
+            xm[0, j] -= eps
+            fp = o.selected_logp_from_f64(xp, t)[0][0]
+            fm = o.selected_logp_from_f64(xm, t)[0][0]
+            fd = g * (fp - fm) / (2 * eps)
+            assert abs(d[0, j] - fd) <= 1e-7 * (1 + abs(g)), (v, j, d[0, j], fd)
+
+
+def pin_backward_mask(o):
+    rng = np.random.default_rng(33)
+    vals = grid_values(rng, (3, 6))
+    bits = to_bf16_bits_exact(vals)
+    t = np.array([2, -100, 5])
+    mask = np.array([1, 0, 1], dtype=np.uint8)
+    _, lse = o.logp_selected(bits, t, mask)
+    d = o.logp_backward(bits, t, mask, lse, [1.0, 3.0, -2.0])
+    assert np.all(d[1] == 0.0)
+    row = [float(a) for a in vals[0]]
+    tot = math.fsum(math.exp(a) for a in row)
+    for j in range(6):
+        ref = (1.0 if j == 2 else 0.0) - math.exp(row[j]) / tot
+        assert abs(d[0, j] - ref) <= 1e-14
+
+
+def pin_linear_backward_matches_brute_force(o):
+    rng = np.random.default_rng(34)
+    n, v, h = 3, 7, 10
+    hb = _rand_bf16(rng, (n, h), 1.0)
+    wb = _rand_bf16(rng, (v, h), 1.0)
+    t = rng.integers(0, v, size=n)
+    g = rng.standard_normal(n)
+    _, lse = o.linear_logp(hb, wb, t)
+    d = o.linear_logp_backward(hb, wb, t, None, lse, g)
+    hf, wf = bits_to_float(hb), bits_to_float(wb)
+    for i in range(n):
+        z = [math.fsum(float(hf[i, k]) * float(wf[j, k]) for k in range(h)) for j in range(v)]
+        tot = math.fsum(math.exp(a) for a in z)
+        for j in range(v):
+            ref = g[i] * ((1.0 if j == t[i] else 0.0) - math.exp(z[j]) / tot)
+            assert abs(d[i, j] - ref) <= 1e-13, (i, j)
+
+
+ALL_PINS = [
+    pin_brute_force_tiny,
+    pin_uniform_rows,
+    pin_uniform_large_vocab,
+    pin_two_entries,
+    pin_peaked_row,
+    pin_probabilities_sum_to_one,
+    pin_differences_are_logit_differences,
+    pin_shift_invariance,
+    pin_mask_and_targets,
+    pin_nonfinite,
+    pin_projection_spot_checks,
+    pin_projection_one_hot,
+    pin_projection_zero_hidden_and_equal_rows,
+    pin_fused_matches_brute_force,
+    pin_backward_rows_sum_to_zero,
+    pin_backward_closed_forms,
+    pin_backward_finite_differences,
+    pin_backward_mask,
+    pin_linear_backward_matches_brute_force,
+]

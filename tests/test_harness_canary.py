@@ -1,0 +1,158 @@
+"""The I-relation runner must pass a batch-invariant model and catch a
+planted batch-dependent one (CPU only).
+
+Two float32 numpy models of the selected logprob stand in for a kernel:
+
+* ``fixed_schedule``: every row is reduced in vocabulary chunks of a fixed
+  size, chunk partials merged in ascending order -- invariant by construction;
+* ``shape_dependent``: the chunk size depends on the number of rows in the
+  call, the reduction-schedule defect the pages describe (page "[RFC] ...",
+  maintainer reply: a tolerance on I would hide the reduction-schedule defect
+  the suite exists to find).
+
+Neither model is the oracle; they only exercise the runner.
+"""
+import numpy as np
+import pytest
+import torch
+
+import invariance as inv
+from invariant_logprob_amd import workloads as wl
+
+
+def _model(chunk_of_n):
+    def run(batch):
+        x = batch["x"].float().numpy().astype(np.float32)
+        t = batch["targets"].numpy()
+        mask = batch["mask"]
+        n, v = x.shape
+        act = np.ones(n, bool) if mask is None else mask.numpy().astype(bool)
+        chunk = chunk_of_n(n)
+        logp = np.zeros(n, np.float32)
+        lse = np.zeros(n, np.float32)
+        for i in range(n):
+            if not act[i]:
+                continue
+            m = np.float32(-np.inf)
+            s = np.float32(0.0)
+            for c0 in range(0, v, chunk):
+                xc = x[i, c0:c0 + chunk]
+                mc = xc.max()
+                sc = np.exp(xc - mc, dtype=np.float32).sum(dtype=np.float32)
+                mn = max(m, mc)
+                s = np.float32(s * np.exp(np.float32(m - mn)) + sc * np.exp(np.float32(mc - mn)))
+                m = mn
+            lse[i] = np.float32(m + np.log(s))
+            logp[i] = np.float32(x[i, t[i]] - lse[i])
+        return {"logp": torch.from_numpy(logp), "lse": torch.from_numpy(lse)}
+    return run
+
+
+fixed_schedule = _model(lambda n: 96)
+shape_dependent = _model(lambda n: 96 if n >= 8 else 40)
+
+
+def _base(n=24, v=700, seed=0, n_masked=4):
+    b = wl.logits_batch(n, v, 3.0, seed=seed, n_masked=n_masked)
+    return {"x": b.logits, "targets": b.targets, "mask": b.mask}
+
+
+def _filler(v):
+    def f(n, seed):
+        x, t = wl.neighbour_rows(n, v, seed)
+        return {"x": x, "targets": t, "mask": torch.ones(n, dtype=torch.uint8)}
+    return f
+
+
+def _cases(base, v):
+    filler = _filler(v)
+    n = inv.nrows(base)
+    yield "T1", dict(size=1), inv.t1_population(base, 1)
+    yield "T1", dict(size=7, start=5), inv.t1_population(base, 7, start=5)
+    yield "T2", dict(seed=3), inv.t2_position(base, 3)
+    yield "T3", dict(keep=[2, 9, 17], seed=5), inv.t3_neighbours(base, [2, 9, 17], filler, 5)
+    yield "T4", dict(left=3, right=5, every=4), inv.t4_padding(base, filler, 11, 3, 5, 4)
+    yield "T5", dict(chunk=1), inv.t5_schedule(base, 1)
+    yield "T5", dict(chunk=5), inv.t5_schedule(base, 5)
+    yield "T6", dict(padded="right"), inv.t6_padded_layout(base, [7, 10, 7], 12, filler, 13, "right")
+    yield "T6", dict(padded="left"), inv.t6_padded_layout(base, [7, 10, 7], 12, filler, 13, "left")
+    yield "T6", dict(compacted=True), inv.t6_compacted(base)
+    assert n == 24
+
+
+def test_fixed_schedule_passes_every_transform():
+    base = _base()
+    base_out = fixed_schedule(base)
+    for cls, params, (calls, row_map) in _cases(base, 700):
+        man = {"operator": "canary_fixed", "transform": {"class": cls, **params}, "seed": 0}
+        recs, _ = inv.check(fixed_schedule, base, calls, row_map, man, base_out)
+        assert recs == [], recs
+
+
+def test_shape_dependent_schedule_is_caught():
+    base = _base()
+    caught = []
+    base_out = shape_dependent(base)
+    for cls, params, (calls, row_map) in _cases(base, 700):
+        man = {"operator": "canary_defect", "chain_index": 8,
+               "transform": {"class": cls, "name": inv.TRANSFORM_NAMES[cls], **params}, "seed": 0}
+        recs, _ = inv.check(shape_dependent, base, calls, row_map, man, base_out)
+        caught += recs
+    assert caught, "planted batch-dependent schedule went unnoticed"
+    classes = {r["transform"]["class"] for r in caught}
+    assert "T1" in classes and "T5" in classes
+    r = caught[0]
+    for key in ("fixture_id", "max_abs_error", "n_mismatched", "first_mismatch", "threshold"):
+        assert key in r
+    assert r["threshold"] == {"atol": 0.0, "rtol": 0.0}
+    assert r["n_mismatched"] > 0
+
+
+def test_compare_is_bitwise():
+    base = _base(n=4, v=50, n_masked=0)
+    out = fixed_schedule(base)
+    flipped = {k: v.clone() for k, v in out.items()}
+    # -0.0 vs +0.0 must count as a mismatch
+    flipped["logp"][1] = -flipped["logp"][1] if flipped["logp"][1] == 0 else flipped["logp"][1]
+    bits = flipped["lse"].view(torch.int32)
+    bits[2] ^= 1   # one ulp
+    recs = inv.compare(out, flipped, torch.arange(4), base["mask"], {"operator": "x"})
+    assert any(r["output"] == "lse" for r in recs)
+
+
+def test_fixture_id_is_content_derived():
+    a = inv.fixture_id({"operator": "logp", "seed": 0, "transform": {"class": "T1"}})
+    b = inv.fixture_id({"operator": "logp", "seed": 1, "transform": {"class": "T1"}})
+    assert a != b and a == inv.fixture_id({"transform": {"class": "T1"}, "seed": 0,
+                                            "operator": "logp"})
+
+
+@pytest.mark.parametrize("builder", [wl.logits_small])
+def test_workload_generators_are_seeded(builder):
+    a = builder(seed=0)
+    b = builder(seed=0)
+    c = builder(seed=1)
+    assert torch.equal(a.logits.view(torch.int16), b.logits.view(torch.int16))
+    assert not torch.equal(a.logits.view(torch.int16), c.logits.view(torch.int16))
+    assert torch.equal(a.targets, b.targets)
+
+
+def test_varlen_recipe():
+    b = wl.logits_varlen(seed=0, v=512)
+    total = sum(b.seq_lens)
+    n = b.logits.shape[0]
+    assert len(b.seq_lens) == 8 and all(64 <= L <= 1024 for L in b.seq_lens)
+    assert n % 128 == 0 and total <= n < total + 128
+    assert int(b.mask.sum()) == total
+    assert bool((b.targets[total:] == -100).all())
+    act = b.targets[:total]
+    assert bool(((act >= 0) & (act < 512)).all())
+    am = torch.argmax(b.logits[:total].float(), dim=1)
+    frac = float((act == am).float().mean())
+    assert 0.4 < frac < 0.65, frac
+
+
+def test_large_recipe_mask_count():
+    b = wl.logits_batch(2000, 8, 4.0, seed=0, n_masked=int(round(0.15 * 2000)))
+    assert int((b.mask == 0).sum()) == 300
+    assert bool((b.targets[b.mask == 0] == -100).all())

@@ -1,0 +1,125 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin.
+
+Each mutant is a fresh copy of the oracle module with one plausible error
+patched in (a dropped term, a wrong sign or index, a transposed operand, a
+wrong logarithm base, an ignored mask).  The real oracle passes every pin
+(test_oracle_pins); these tests show the pins would notice such mistakes.
+"""
+import importlib.util
+import os
+
+import numpy as np
+import pytest
+
+from oracle_pins import ALL_PINS
+
+ORACLE_FILE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                           "oracle", "logprob_oracle.py")
+
+
+def fresh_oracle(tag):
+    spec = importlib.util.spec_from_file_location(f"oracle_mutant_{tag}", ORACLE_FILE)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _lse_factory(variant):
+    def lse(x):
+        x = np.asarray(x, dtype=np.float64)
+        m = np.max(x, axis=1)
+        with np.errstate(all="ignore"):
+            if variant == "sign":
+                return m - np.log(np.sum(np.exp(x - m[:, None]), axis=1))
+            if variant == "no_shift":
+                return np.log(np.sum(np.exp(x), axis=1))
+            if variant == "log2":
+                return m + np.log2(np.sum(np.exp(x - m[:, None]), axis=1))
+            if variant == "drop_max":
+                return np.log(np.sum(np.exp(x - m[:, None]), axis=1))
+            if variant == "mean_not_sum":
+                return m + np.log(np.mean(np.exp(x - m[:, None]), axis=1))
+        raise AssertionError(variant)
+    return lse
+
+
+def make_mutant(name):
+    o = fresh_oracle(name)
+    if name in ("sign", "no_shift", "log2", "drop_max", "mean_not_sum"):
+        o.logsumexp_rows = _lse_factory(name)
+    elif name == "gather_off_by_one":
+        orig = o.selected_logp_from_f64
+
+        def f(x, targets, mask=None):
+            t = np.asarray(targets, dtype=np.int64)
+            v = np.asarray(x).shape[1]
+            return orig(x, (t + 1) % v if v > 1 else t, mask)
+        o.selected_logp_from_f64 = f
+    elif name == "decode_as_fp16":
+        o.bf16_to_f64 = lambda b: np.asarray(b, dtype=np.uint16).view(np.float16).astype(np.float64)
+    elif name == "weight_transposed":
+        def ll(hb, wb):
+            h = o.bf16_to_f64(hb)
+            w = o.bf16_to_f64(wb)
+            v, hh = w.shape
+            return h @ w.reshape(hh, v)  # reads [V,H] memory as if it were [H,V]
+        o.linear_logits = ll
+        orig_lp = o.linear_logp
+
+        def lp(hb, wb, t, mask=None, block_rows=256):
+            return o.selected_logp_from_f64(ll(hb, wb), t, mask)
+        o.linear_logp = lp
+        del orig_lp
+    elif name == "mask_ignored":
+        orig = o.selected_logp_from_f64
+
+        def f(x, targets, mask=None):
+            t = np.asarray(targets, dtype=np.int64).copy()
+            v = np.asarray(x).shape[1]
+            t = np.where((t < 0) | (t >= v), 0, t)
+            return orig(x, t, None)
+        o.selected_logp_from_f64 = f
+    elif name in ("bwd_sign", "bwd_no_g", "bwd_no_onehot", "bwd_no_lse"):
+        def b(x, targets, mask, lse, g):
+            x = np.asarray(x, dtype=np.float64)
+            n, v = x.shape
+            t = np.asarray(targets, dtype=np.int64)
+            act = np.ones(n, bool) if mask is None else np.asarray(mask).astype(bool)
+            g = np.asarray(g, dtype=np.float64).reshape(n)
+            ls = np.asarray(lse, dtype=np.float64).reshape(n)
+            d = np.zeros((n, v))
+            for i in np.nonzero(act)[0]:
+                p = np.exp(x[i] - (0.0 if name == "bwd_no_lse" else ls[i]))
+                oh = np.zeros(v)
+                if name != "bwd_no_onehot":
+                    oh[t[i]] = 1.0
+                gi = 1.0 if name == "bwd_no_g" else g[i]
+                d[i] = gi * ((p - oh) if name == "bwd_sign" else (oh - p))
+            return d
+        o.logp_backward_from_f64 = b
+    else:
+        raise AssertionError(name)
+    return o
+
+
+MUTANTS = ["sign", "no_shift", "log2", "drop_max", "mean_not_sum", "gather_off_by_one",
+           "decode_as_fp16", "weight_transposed", "mask_ignored", "bwd_sign", "bwd_no_g",
+           "bwd_no_onehot", "bwd_no_lse"]
+
+
+@pytest.mark.parametrize("name", MUTANTS)
+def test_mutant_is_caught(name):
+    o = make_mutant(name)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(o)
+        except Exception as e:  # AssertionError, or a crash from the bad code
+            failed.append((pin.__name__, type(e).__name__))
+    assert failed, f"mutant {name} passed every pin"
+
+
+def test_unmutated_copy_passes():
+    o = fresh_oracle("clean")
+    for pin in ALL_PINS:
+        pin(o)
