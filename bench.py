@@ -1,0 +1,228 @@
+"""Benchmark of the batch-invariant selected-token logprob hot path on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one pass of the whole hot path over resident synthetic inputs:
+
+  logits_fwd  selected logprob from bf16 logits, N=16384 rows (2458 masked),
+              V=151936                                    (kernel logp_fwd_rows)
+  logits_bwd  its backward, fp32 dlogits [16384, 151936]  (logp_bwd_rows)
+  fused_fwd   lm_head + selected logprob, hidden [8192, 4096], W [128256, 4096]
+                                                          (linear_tiles + lse_chunk_combine)
+  fused_fb    fused forward + backward, hidden [2048, 5120], W [151936, 5120]
+                                                          (linear_tiles x2 + combine)
+
+The headline value is the selected-logprob throughput at V=151936: active
+tokens per second of the logits forward.  Each leg is timed with HIP events
+on the stream its kernels run on (torch's current stream), and every leg's
+rate is reported beside it.  The CPU baseline is the fp64 oracle on a bounded
+sample of the same logits workload.
+"""
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+METRIC = "tokens/s + HBM GB/s, selected-logp V=152k; fused linear_logp TFLOP/s"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--legs", default="logits_fwd,logits_bwd,fused_fwd,fused_fb")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the hot path is data-parallel over rows and needs no "
+              "collective; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import invariant_logprob_amd as ilp
+    from invariant_logprob_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ilp.load_library()
+    legs = [l for l in args.legs.split(",") if l]
+    t_gen = time.perf_counter()
+
+    # ---- resident inputs and outputs ------------------------------------
+    c3 = wl.logits_large(seed=0, device=dev)
+    n3, v3 = c3.logits.shape
+    act3 = int(c3.mask.sum())
+    logp3 = torch.empty(n3, dtype=torch.float32, device=dev)
+    lse3 = torch.empty(n3, dtype=torch.float32, device=dev)
+    d3 = torch.empty((n3, v3), dtype=torch.float32, device=dev) if "logits_bwd" in legs else None
+    c4 = wl.fused_large(seed=0, device=dev) if "fused_fwd" in legs else None
+    c5 = wl.fused_bwd(seed=0, device=dev) if "fused_fb" in legs else None
+    if c4 is not None:
+        n4, h4 = c4.hidden.shape
+        v4 = c4.weight.shape[0]
+        ws4 = torch.empty(ilp.linear_logp_workspace_size(n4, v4, h4), dtype=torch.uint8, device=dev)
+        logp4 = torch.empty(n4, dtype=torch.float32, device=dev)
+        lse4 = torch.empty(n4, dtype=torch.float32, device=dev)
+    if c5 is not None:
+        n5, h5 = c5.hidden.shape
+        v5 = c5.weight.shape[0]
+        ws5 = torch.empty(ilp.linear_logp_workspace_size(n5, v5, h5), dtype=torch.uint8, device=dev)
+        logp5 = torch.empty(n5, dtype=torch.float32, device=dev)
+        lse5 = torch.empty(n5, dtype=torch.float32, device=dev)
+        d5 = torch.empty((n5, v5), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+
+    def leg_logits_fwd():
+        ilp.logp_selected(c3.logits, c3.targets, c3.mask, logp=logp3, lse=lse3)
+
+    def leg_logits_bwd():
+        ilp.logp_backward(c3.logits, c3.targets, lse3, c3.grad, c3.mask, out=d3)
+
+    def leg_fused_fwd():
+        ilp.linear_logp(c4.hidden, c4.weight, c4.targets, c4.mask, workspace=ws4, logp=logp4,
+                        lse=lse4)
+
+    def leg_fused_fb():
+        ilp.linear_logp(c5.hidden, c5.weight, c5.targets, c5.mask, workspace=ws5, logp=logp5,
+                        lse=lse5)
+        ilp.linear_logp_backward(c5.hidden, c5.weight, c5.targets, lse5, c5.grad, c5.mask, out=d5)
+
+    fns = {"logits_fwd": leg_logits_fwd, "logits_bwd": leg_logits_bwd,
+           "fused_fwd": leg_fused_fwd, "fused_fb": leg_fused_fb}
+    if "logits_bwd" in legs and "logits_fwd" not in legs:
+        leg_logits_fwd()   # the backward needs lse
+
+    for _ in range(args.warmup):
+        for l in legs:
+            fns[l]()
+    torch.cuda.synchronize()
+
+    events = {l: [] for l in legs}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for l in legs:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fns[l]()
+            e1.record()
+            events[l].append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {l: sum(a.elapsed_time(b) for a, b in events[l]) / args.steps for l in legs}
+    ms_per_step = wall * 1e3 / args.steps
+
+    out_legs = {}
+    roofline = None
+    if "logits_fwd" in legs:
+        bytes_fwd = act3 * v3 * 2 + n3 * (8 + 1 + 8)
+        gbs = bytes_fwd / (ms["logits_fwd"] * 1e-3) / 1e9
+        out_legs["logits_fwd"] = {"ms": ms["logits_fwd"], "active_tokens": act3,
+                                  "tokens_per_s": act3 / (ms["logits_fwd"] * 1e-3),
+                                  "algorithmic_bytes": bytes_fwd, "GB_per_s": gbs,
+                                  "hbm_frac": gbs / HBM_PEAK_GBS}
+        roofline = {"kernel": "logp_fwd_rows", "bound": "hbm", "achieved": gbs,
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                    "traffic": None}
+    if "logits_bwd" in legs:
+        bytes_bwd = act3 * v3 * 2 + n3 * v3 * 4 + n3 * (8 + 1 + 4 + 4)
+        gbs = bytes_bwd / (ms["logits_bwd"] * 1e-3) / 1e9
+        out_legs["logits_bwd"] = {"ms": ms["logits_bwd"], "algorithmic_bytes": bytes_bwd,
+                                  "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+    if "fused_fwd" in legs:
+        fl = 2.0 * n4 * v4 * h4
+        tf = fl / (ms["fused_fwd"] * 1e-3) / 1e12
+        out_legs["fused_fwd"] = {"ms": ms["fused_fwd"], "flops": fl, "TFLOP_per_s": tf,
+                                 "mfma_frac": tf / BF16_PEAK_TFLOPS,
+                                 "tokens_per_s": n4 / (ms["fused_fwd"] * 1e-3)}
+    if "fused_fb" in legs:
+        fl = 2 * 2.0 * n5 * v5 * h5
+        tf = fl / (ms["fused_fb"] * 1e-3) / 1e12
+        out_legs["fused_fb"] = {"ms": ms["fused_fb"], "flops": fl, "TFLOP_per_s": tf,
+                                "mfma_frac": tf / BF16_PEAK_TFLOPS,
+                                "dlogits_bytes": n5 * v5 * 4}
+    if roofline is None and "fused_fwd" in legs:
+        f = out_legs["fused_fwd"]
+        roofline = {"kernel": "linear_tiles", "bound": "mfma", "achieved": f["TFLOP_per_s"],
+                    "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": f["mfma_frac"],
+                    "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline and "logits_fwd" in legs:
+        cpu = cpu_baseline(c3, torch)
+
+    value = out_legs["logits_fwd"]["tokens_per_s"] if "logits_fwd" in legs else None
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "selected logprob from bf16 logits N=16384 (2458 masked) V=151936; "
+                        "fused lm_head N=8192 H=4096 V=128256; fused fwd+bwd N=2048 H=5120 "
+                        "V=151936",
+            "legs": legs,
+            "global_batch": n3,
+            "parallelism": "none (1 GPU)",
+        },
+        "legs": out_legs,
+        "roofline": roofline,
+        "fused_roofline": ({"kernel": "linear_tiles", "bound": "mfma",
+                            "achieved": out_legs["fused_fwd"]["TFLOP_per_s"],
+                            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": out_legs["fused_fwd"]["mfma_frac"], "traffic": None}
+                           if "fused_fwd" in out_legs else None),
+        "cpu_baseline": cpu,
+        "build": ilp.build_info(),
+        "device": torch.cuda.get_device_name(dev),
+        "input_generation_s": t_gen,
+    }
+    print(json.dumps(rec))
+
+
+def cpu_baseline(c3, torch):
+    """The fp64 oracle, as it stands, on the first 256 rows of the same
+    logits workload; tokens/s over the active rows of that sample."""
+    import numpy as np
+
+    import oracle
+    rows = 256
+    bits = c3.logits[:rows].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+    t = c3.targets[:rows].cpu().numpy()
+    m = c3.mask[:rows].cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.logp_selected(bits, t, m)
+    dt = time.perf_counter() - t0
+    active = int(m.astype(bool).sum())
+    return {"value": active / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {rows} rows ({active} active) of the N=16384 V=151936 logits "
+                      f"workload, {dt:.1f} s",
+            "host": platform.processor() or platform.machine(), "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

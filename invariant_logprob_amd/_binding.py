@@ -1,6 +1,259 @@
-"""placeholder, replaced by the ctypes binding"""
-def _missing(*a, **k):
-    raise RuntimeError("binding not built yet")
-RlkError = RuntimeError
-build_info = library_path = linear_logp = linear_logp_backward = _missing
-linear_logp_workspace_size = load_library = logp_backward = logp_selected = _missing
+"""ctypes binding over librlk.so (C ABI declared in include/rlk.h).
+
+Argument marshalling only: dtype/device/stride checks, output allocation
+through torch, and the call with raw device pointers on torch's current
+stream.  Every step of the computation runs in the HIP kernels; a missing or
+unloadable library raises RlkError -- there is no fallback.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+_STATUS = {0: "RLK_OK", 1: "RLK_ERR_INVALID_ARG", 2: "RLK_ERR_UNSUPPORTED", 3: "RLK_ERR_LAUNCH"}
+
+
+class RlkError(RuntimeError):
+    """Raised when the library is missing or a call returns a non-zero status."""
+
+    def __init__(self, msg, status=None):
+        super().__init__(msg)
+        self.status = status
+
+
+def library_path():
+    return os.path.join(_HERE, "librlk.so")
+
+
+def load_library():
+    """Load librlk.so once and declare the C signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RlkError(f"HIP library not built: {path} (run python -m invariant_logprob_amd.build)")
+    lib = ctypes.CDLL(path)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    lib.rlk_logp_selected.argtypes = [vp, i64, vp, vp, i64, i64, vp, vp, vp]
+    lib.rlk_logp_selected.restype = ctypes.c_int
+    lib.rlk_linear_logp_workspace_size.argtypes = [i64, i64, i64]
+    lib.rlk_linear_logp_workspace_size.restype = sz
+    lib.rlk_linear_logp.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
+    lib.rlk_linear_logp.restype = ctypes.c_int
+    lib.rlk_logp_backward.argtypes = [vp, i64, vp, i64, vp, i64, i64, vp, vp, vp, vp, i64, i64, vp,
+                                      i64, vp]
+    lib.rlk_logp_backward.restype = ctypes.c_int
+    lib.rlk_status_string.argtypes = [ctypes.c_int]
+    lib.rlk_status_string.restype = ctypes.c_char_p
+    lib.rlk_build_info.argtypes = []
+    lib.rlk_build_info.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def build_info():
+    return load_library().rlk_build_info().decode()
+
+
+def _raise(status, fn):
+    if status != 0:
+        raise RlkError(f"{fn} failed: {_STATUS.get(status, status)}", status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _device_of(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
+    return t.device
+
+
+def _matrix(t, name, dtype):
+    _device_of(t, name)
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit stride along its last dimension")
+    if t.shape[0] > 1:
+        return t.stride(0)
+    # a single row is never addressed through its leading dimension
+    return (t.shape[1] + 7) // 8 * 8
+
+
+def _rows(t, name, n, dtype):
+    _device_of(t, name)
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 1 or t.shape[0] != n:
+        raise ValueError(f"{name} must have shape ({n},), got {tuple(t.shape)}")
+    if n > 1 and t.stride(0) != 1:
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _mask(mask, n):
+    if mask is None:
+        return None
+    if mask.dtype == torch.bool:
+        mask = mask.view(torch.uint8)
+    _rows(mask, "mask", n, torch.uint8)
+    return mask
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"all tensors must be on one device, got {sorted(map(str, devs))}")
+    return devs.pop()
+
+
+def logp_selected(logits, targets, mask=None, *, logp=None, lse=None):
+    """Selected-token logprob from bf16 logits [N, V] (rows may be strided).
+
+    Returns (logp, lse), both float32 [N]; inactive rows get 0.
+    """
+    lib = load_library()
+    ld = _matrix(logits, "logits", torch.bfloat16)
+    n, v = logits.shape
+    _rows(targets, "targets", n, torch.int64)
+    mask = _mask(mask, n)
+    dev = _same_device(logits, targets, mask)
+    if logp is None:
+        logp = torch.empty(n, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(n, dtype=torch.float32, device=dev)
+    _rows(logp, "logp", n, torch.float32)
+    _rows(lse, "lse", n, torch.float32)
+    if n == 0:
+        return logp, lse
+    with torch.cuda.device(dev):
+        st = lib.rlk_logp_selected(_ptr(logits), ld, _ptr(targets), _ptr(mask), n, v, _ptr(logp),
+                                   _ptr(lse), _stream(dev))
+    _raise(st, "rlk_logp_selected")
+    return logp, lse
+
+
+def linear_logp_workspace_size(n, v, h):
+    return int(load_library().rlk_linear_logp_workspace_size(n, v, h))
+
+
+def linear_logp(hidden, weight, targets, mask=None, *, workspace=None, logp=None, lse=None):
+    """Fused lm_head + selected logprob: hidden bf16 [N, H], weight bf16
+    [V, H] (nn.Linear layout).  Returns (logp, lse), float32 [N]."""
+    lib = load_library()
+    ldh = _matrix(hidden, "hidden", torch.bfloat16)
+    ldw = _matrix(weight, "weight", torch.bfloat16)
+    n, h = hidden.shape
+    v, h2 = weight.shape
+    if h != h2:
+        raise ValueError(f"hidden has H={h} but weight has H={h2}")
+    _rows(targets, "targets", n, torch.int64)
+    mask = _mask(mask, n)
+    dev = _same_device(hidden, weight, targets, mask)
+    if logp is None:
+        logp = torch.empty(n, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(n, dtype=torch.float32, device=dev)
+    if n == 0:
+        return logp, lse
+    need = linear_logp_workspace_size(n, v, h)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace too small: need {need} bytes")
+    with torch.cuda.device(dev):
+        st = lib.rlk_linear_logp(_ptr(hidden), ldh, _ptr(weight), ldw, _ptr(targets), _ptr(mask), n,
+                                 v, h, _ptr(logp), _ptr(lse), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(dev))
+    _raise(st, "rlk_linear_logp")
+    return logp, lse
+
+
+def _grad_out(out, n, v, dev):
+    if out is None:
+        ldg = (v + 3) // 4 * 4
+        buf = torch.empty((n, ldg), dtype=torch.float32, device=dev)
+        return buf[:, :v], ldg
+    ldg = _matrix(out, "out", torch.float32)
+    if tuple(out.shape) != (n, v):
+        raise ValueError(f"out must have shape ({n}, {v})")
+    return out, ldg
+
+
+def logp_backward(logits, targets, lse, grad_logp, mask=None, *, out=None):
+    """d(sum_i g_i logp_i)/d logits from bf16 logits [N, V]: float32 [N, V]."""
+    lib = load_library()
+    ld = _matrix(logits, "logits", torch.bfloat16)
+    n, v = logits.shape
+    _rows(targets, "targets", n, torch.int64)
+    _rows(lse, "lse", n, torch.float32)
+    _rows(grad_logp, "grad_logp", n, torch.float32)
+    mask = _mask(mask, n)
+    dev = _same_device(logits, targets, lse, grad_logp, mask)
+    out, ldg = _grad_out(out, n, v, dev)
+    if n == 0:
+        return out
+    with torch.cuda.device(dev):
+        st = lib.rlk_logp_backward(_ptr(logits), ld, None, 0, None, 0, 0, _ptr(targets), _ptr(mask),
+                                   _ptr(lse), _ptr(grad_logp), n, v, _ptr(out), ldg, _stream(dev))
+    _raise(st, "rlk_logp_backward")
+    return out
+
+
+def linear_logp_backward(hidden, weight, targets, lse, grad_logp, mask=None, *, out=None):
+    """Gradient with respect to the logits z = hidden . weight^T, recomputed
+    with the forward's tiles: float32 [N, V]."""
+    lib = load_library()
+    ldh = _matrix(hidden, "hidden", torch.bfloat16)
+    ldw = _matrix(weight, "weight", torch.bfloat16)
+    n, h = hidden.shape
+    v, h2 = weight.shape
+    if h != h2:
+        raise ValueError(f"hidden has H={h} but weight has H={h2}")
+    _rows(targets, "targets", n, torch.int64)
+    _rows(lse, "lse", n, torch.float32)
+    _rows(grad_logp, "grad_logp", n, torch.float32)
+    mask = _mask(mask, n)
+    dev = _same_device(hidden, weight, targets, lse, grad_logp, mask)
+    out, ldg = _grad_out(out, n, v, dev)
+    if n == 0:
+        return out
+    with torch.cuda.device(dev):
+        st = lib.rlk_logp_backward(None, 0, _ptr(hidden), ldh, _ptr(weight), ldw, h, _ptr(targets),
+                                   _ptr(mask), _ptr(lse), _ptr(grad_logp), n, v, _ptr(out), ldg,
+                                   _stream(dev))
+    _raise(st, "rlk_logp_backward")
+    return out
+
+
+class SelectedLogprob(torch.autograd.Function):
+    """Autograd wrapper: forward through rlk_logp_selected, backward through
+    rlk_logp_backward with the saved lse."""
+
+    @staticmethod
+    def forward(ctx, logits, targets, mask=None):
+        logp, lse = logp_selected(logits, targets, mask)
+        ctx.save_for_backward(logits, targets, lse, mask if mask is not None else torch.empty(0))
+        ctx.has_mask = mask is not None
+        return logp
+
+    @staticmethod
+    def backward(ctx, grad):
+        logits, targets, lse, mask = ctx.saved_tensors
+        g = grad.contiguous().to(torch.float32)
+        d = logp_backward(logits, targets, lse, g, mask if ctx.has_mask else None)
+        return d, None, None

@@ -1,0 +1,252 @@
+// Selected-token logprob from materialised bf16 logits, and its backward.
+//
+// Forward (one workgroup per row).  The row is streamed once from HBM in
+// 16-byte vectors of 8 bf16.  Vector k of a row always goes to thread
+// k % kRowThreads and is visited in ascending k, so every lane's partial
+// (M, s) is a function of the row's values and of V alone.  Lanes merge in a
+// fixed wave64 butterfly, waves merge in ascending wave order through LDS.
+// Nothing depends on N, on the row's index or on other rows: the batch
+// invariance of page "[RFC] Batch-Invariant RL Kernel Suite for
+// Train-Inference Consistency" (relation I) holds by construction, and there
+// are no atomics (page "[WS1 Test] #154 dtype pin + ...", section
+// "Workstream 3 - #153", scope item 2).
+//
+// Backward (grid = rows x column blocks).  Elementwise:
+//   d[i, j] = g_i * ([j == t_i] - exp(x_ij - lse_i)),
+// evaluated as fma(-g_i, p_ij, [j == t_i] g_i) with p_ij = 2^(x_ij log2 e -
+// lse_i log2 e).  No reduction, so each element depends on its row only.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rlk_device.hpp"
+#include "rlk_internal.hpp"
+
+namespace rlk {
+
+namespace {
+
+constexpr uint32_t kNegInfPair = 0xff80ff80u;  // two bf16 -inf
+
+struct Vec8 {
+  float v[8];
+};
+
+__device__ __forceinline__ Vec8 decode(const uint4& w) {
+  Vec8 r;
+  r.v[0] = bf16_lo(w.x);
+  r.v[1] = bf16_hi(w.x);
+  r.v[2] = bf16_lo(w.y);
+  r.v[3] = bf16_hi(w.y);
+  r.v[4] = bf16_lo(w.z);
+  r.v[5] = bf16_hi(w.z);
+  r.v[6] = bf16_lo(w.w);
+  r.v[7] = bf16_hi(w.w);
+  return r;
+}
+
+__device__ __forceinline__ float max8(const Vec8& a) {
+  return fmaxf(fmaxf(fmaxf(a.v[0], a.v[1]), fmaxf(a.v[2], a.v[3])),
+               fmaxf(fmaxf(a.v[4], a.v[5]), fmaxf(a.v[6], a.v[7])));
+}
+
+// Sum of the 8 terms in a fixed pairwise tree.
+__device__ __forceinline__ float sum8_terms(const Vec8& a, float Mu) {
+#pragma clang fp contract(off)
+  const float e0 = lse_term(a.v[0], Mu), e1 = lse_term(a.v[1], Mu);
+  const float e2 = lse_term(a.v[2], Mu), e3 = lse_term(a.v[3], Mu);
+  const float e4 = lse_term(a.v[4], Mu), e5 = lse_term(a.v[5], Mu);
+  const float e6 = lse_term(a.v[6], Mu), e7 = lse_term(a.v[7], Mu);
+  return ((e0 + e1) + (e2 + e3)) + ((e4 + e5) + (e6 + e7));
+}
+
+// One block of kUnroll vectors held by a lane: raise the offset to the
+// block maximum, then add the block's terms in ascending vector order.
+template <int U>
+__device__ __forceinline__ void consume(float& M, float& s, const Vec8 (&x)[U]) {
+#pragma clang fp contract(off)
+  float bm = max8(x[0]);
+#pragma unroll
+  for (int u = 1; u < U; ++u) bm = fmaxf(bm, max8(x[u]));
+  const float Mu = lse_raise(M, s, bm);
+#pragma unroll
+  for (int u = 0; u < U; ++u) s = s + sum8_terms(x[u], Mu);
+}
+
+template <int THREADS, int UNROLL>
+__global__ __launch_bounds__(THREADS) void logp_fwd_rows(
+    const uint16_t* __restrict__ logits, int64_t ld, const int64_t* __restrict__ targets,
+    const uint8_t* __restrict__ mask, int V, float* __restrict__ logp, float* __restrict__ lse) {
+  constexpr int kWaves = THREADS / 64;
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (mask != nullptr && mask[row] == 0) {
+    if (tid == 0) {
+      logp[row] = 0.0f;
+      if (lse != nullptr) lse[row] = 0.0f;
+    }
+    return;
+  }
+  const uint16_t* rowp = logits + row * ld;
+  const uint4* vp = reinterpret_cast<const uint4*>(rowp);
+  const int nfull = V >> 3;                 // vectors lying wholly inside [0, V)
+  const int nvec = (V + 7) >> 3;
+  constexpr int kStep = THREADS * UNROLL;
+  const int nmain = (nfull / kStep) * kStep;  // unguarded part
+
+  float M = neg_inf();
+  float s = 0.0f;
+  for (int base = 0; base < nmain; base += kStep) {
+    uint4 w[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) w[u] = load16_stream(vp + base + u * THREADS + tid);
+    Vec8 x[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) x[u] = decode(w[u]);
+    consume<UNROLL>(M, s, x);
+  }
+  if (nmain < nvec) {
+    // guarded tail: same lane map (vector k -> thread k % THREADS)
+    Vec8 x[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int k = nmain + u * THREADS + tid;
+      uint4 w = make_uint4(kNegInfPair, kNegInfPair, kNegInfPair, kNegInfPair);
+      if (k < nvec) w = vp[k];
+      x[u] = decode(w);
+      if (k == nfull) {  // the one vector straddling V (only when V % 8 != 0)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (8 * k + e >= V) x[u].v[e] = neg_inf();
+      }
+    }
+    consume<UNROLL>(M, s, x);
+  }
+
+  wave_lse_allreduce(M, s);
+  __shared__ float sM[kWaves];
+  __shared__ float sS[kWaves];
+  const int wave = tid >> 6;
+  if ((tid & 63) == 0) {
+    sM[wave] = M;
+    sS[wave] = s;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float Mt = sM[0];
+    float st = sS[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) lse_merge(Mt, st, sM[w], sS[w]);
+    const float l = lse_finish(Mt, st);
+    const int64_t t = targets[row];
+    float lp;
+    if (t >= 0 && t < V) {
+      lp = bf16_to_f32(rowp[t]) - l;
+    } else {
+      lp = __builtin_nanf("");
+    }
+    logp[row] = lp;
+    if (lse != nullptr) lse[row] = l;
+  }
+}
+
+template <int THREADS, int UNROLL>
+__global__ __launch_bounds__(THREADS) void logp_bwd_rows(
+    const uint16_t* __restrict__ logits, int64_t ld, const int64_t* __restrict__ targets,
+    const uint8_t* __restrict__ mask, const float* __restrict__ lse,
+    const float* __restrict__ grad, int V, float* __restrict__ dl, int64_t ldg) {
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nvec = (V + 7) >> 3;
+  const int kbase = blockIdx.y * (THREADS * UNROLL);
+  float* outp = dl + row * ldg;
+  const bool active = (mask == nullptr) || (mask[row] != 0);
+  if (!active) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int k = kbase + u * THREADS + tid;
+      if (k >= nvec) break;
+      const int j = 8 * k;
+      if (j + 8 <= V) {
+        store16_stream(outp + j, 0.f, 0.f, 0.f, 0.f);
+        store16_stream(outp + j + 4, 0.f, 0.f, 0.f, 0.f);
+      } else {
+        for (int e = 0; j + e < V; ++e) outp[j + e] = 0.0f;
+      }
+    }
+    return;
+  }
+  const int64_t t = targets[row];
+  const bool tvalid = (t >= 0 && t < V);
+  const float g = grad[row];
+  const float off = lse[row] * kLog2e;
+  const float ng = -g;
+  const float nan = __builtin_nanf("");
+  const uint4* vp = reinterpret_cast<const uint4*>(logits + row * ld);
+  uint4 w[UNROLL];
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const int k = kbase + u * THREADS + tid;
+    w[u] = make_uint4(kNegInfPair, kNegInfPair, kNegInfPair, kNegInfPair);
+    if (k < nvec) w[u] = load16_stream(vp + k);
+  }
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const int k = kbase + u * THREADS + tid;
+    if (k >= nvec) break;
+    const int j = 8 * k;
+    const Vec8 x = decode(w[u]);
+    float d[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = ng * fast_exp2(__builtin_fmaf(x.v[e], kLog2e, -off));
+    if (t >= j && t < j + 8) {
+      const int e = static_cast<int>(t - j);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q == e) d[q] = __builtin_fmaf(ng, fast_exp2(__builtin_fmaf(x.v[q], kLog2e, -off)), g);
+    }
+    if (!tvalid) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) d[q] = nan;
+    }
+    if (j + 8 <= V) {
+      store16_stream(outp + j, d[0], d[1], d[2], d[3]);
+      store16_stream(outp + j + 4, d[4], d[5], d[6], d[7]);
+    } else {
+      for (int e = 0; j + e < V; ++e) outp[j + e] = d[e];
+    }
+  }
+}
+
+}  // namespace
+
+// Compile-time schedule of the logits path.  These constants fix every row's
+// reduction order; they are part of the build identity.
+constexpr int kRowThreads = 256;
+constexpr int kRowUnroll = 8;
+constexpr int kBwdThreads = 256;
+constexpr int kBwdUnroll = 4;
+
+int logits_schedule_threads() { return kRowThreads; }
+int logits_schedule_unroll() { return kRowUnroll; }
+
+hipError_t launch_logp_fwd_rows(const uint16_t* logits, int64_t ld, const int64_t* targets,
+                                const uint8_t* mask, int64_t N, int V, float* logp, float* lse,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL((logp_fwd_rows<kRowThreads, kRowUnroll>), dim3(static_cast<uint32_t>(N)),
+                     dim3(kRowThreads), 0, stream, logits, ld, targets, mask, V, logp, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_logp_bwd_rows(const uint16_t* logits, int64_t ld, const int64_t* targets,
+                                const uint8_t* mask, const float* lse, const float* grad, int64_t N,
+                                int V, float* dl, int64_t ldg, hipStream_t stream) {
+  const int nvec = (V + 7) / 8;
+  const int per_block = kBwdThreads * kBwdUnroll;
+  const int nblk = (nvec + per_block - 1) / per_block;
+  hipLaunchKernelGGL((logp_bwd_rows<kBwdThreads, kBwdUnroll>),
+                     dim3(static_cast<uint32_t>(N), static_cast<uint32_t>(nblk)), dim3(kBwdThreads),
+                     0, stream, logits, ld, targets, mask, lse, grad, V, dl, ldg);
+  return hipGetLastError();
+}
+
+}  // namespace rlk

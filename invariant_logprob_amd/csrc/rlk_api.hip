@@ -1,0 +1,147 @@
+// C ABI of the batch-invariant selected-token logprob library (include/rlk.h).
+//
+// Host side only: argument validation, then launches on the caller's
+// stream.  The kernel and its schedule are chosen from V (and H) only, never
+// from N, so the batch shape cannot change how a row is reduced (page "[RFC]
+// Batch-Invariant RL Kernel Suite for Train-Inference Consistency", section
+// "Problem": dispatch by shape is one of the named drift sources).  No
+// allocation, no synchronisation, no mutable state.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/rlk.h"
+#include "rlk_internal.hpp"
+
+#ifndef RLK_GIT_REV
+#define RLK_GIT_REV "unknown"
+#endif
+
+namespace {
+
+constexpr int64_t kMaxV = int64_t(1) << 28;
+constexpr int64_t kMaxH = int64_t(1) << 22;
+constexpr int64_t kMaxN = (int64_t(1) << 31) - 1;
+// The fused tiles address a 256-row slab of W or hidden with 32-bit byte
+// offsets, which bounds the leading dimensions.
+constexpr int64_t kMaxLinearLd = int64_t(1) << 22;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? RLK_OK : RLK_ERR_LAUNCH; }
+
+int check_logits(const void* logits, int64_t ld, int64_t N, int64_t V) {
+  if (logits == nullptr) return RLK_ERR_INVALID_ARG;
+  if (ld < V) return RLK_ERR_INVALID_ARG;
+  if ((ld % 8) != 0 || !aligned16(logits)) return RLK_ERR_UNSUPPORTED;
+  if (N > 0 && ld > (int64_t(1) << 62) / N) return RLK_ERR_UNSUPPORTED;
+  return RLK_OK;
+}
+
+int check_linear(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w, int64_t N,
+                 int64_t V, int64_t H) {
+  if (hidden == nullptr || weight == nullptr) return RLK_ERR_INVALID_ARG;
+  if (H < 1) return RLK_ERR_INVALID_ARG;
+  if (ld_h < H || ld_w < H) return RLK_ERR_INVALID_ARG;
+  if (H > kMaxH || ld_h >= kMaxLinearLd || ld_w >= kMaxLinearLd) return RLK_ERR_UNSUPPORTED;
+  if ((H % 8) != 0 || (ld_h % 8) != 0 || (ld_w % 8) != 0) return RLK_ERR_UNSUPPORTED;
+  if (!aligned16(hidden) || !aligned16(weight)) return RLK_ERR_UNSUPPORTED;
+  const int64_t tiles = ((V + rlk::kLinearVocabTile - 1) / rlk::kLinearVocabTile) *
+                        ((N + rlk::kLinearTokenTile - 1) / rlk::kLinearTokenTile);
+  if (tiles > kMaxN) return RLK_ERR_UNSUPPORTED;
+  if (N > 0 && ld_h > (int64_t(1) << 62) / N) return RLK_ERR_UNSUPPORTED;
+  if (ld_w > (int64_t(1) << 62) / V) return RLK_ERR_UNSUPPORTED;
+  return RLK_OK;
+}
+
+int check_sizes(int64_t N, int64_t V) {
+  if (N < 0 || V < 1) return RLK_ERR_INVALID_ARG;
+  if (N > kMaxN || V > kMaxV) return RLK_ERR_UNSUPPORTED;
+  return RLK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rlk_logp_selected(const void* logits, int64_t ld, const int64_t* targets, const uint8_t* mask,
+                      int64_t N, int64_t V, float* logp, float* lse, hipStream_t stream) {
+  int st = check_sizes(N, V);
+  if (st != RLK_OK) return st;
+  if (N == 0) return RLK_OK;
+  if (targets == nullptr || logp == nullptr) return RLK_ERR_INVALID_ARG;
+  st = check_logits(logits, ld, N, V);
+  if (st != RLK_OK) return st;
+  return status_of(rlk::launch_logp_fwd_rows(static_cast<const uint16_t*>(logits), ld, targets,
+                                             mask, N, static_cast<int>(V), logp, lse, stream));
+}
+
+size_t rlk_linear_logp_workspace_size(int64_t N, int64_t V, int64_t H) {
+  (void)H;
+  if (N < 0 || V < 1) return 0;
+  return rlk::linear_workspace_bytes(N, V);
+}
+
+int rlk_linear_logp(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
+                    const int64_t* targets, const uint8_t* mask, int64_t N, int64_t V, int64_t H,
+                    float* logp, float* lse, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  int st = check_sizes(N, V);
+  if (st != RLK_OK) return st;
+  if (N == 0) return RLK_OK;
+  if (targets == nullptr || logp == nullptr || workspace == nullptr) return RLK_ERR_INVALID_ARG;
+  st = check_linear(hidden, ld_h, weight, ld_w, N, V, H);
+  if (st != RLK_OK) return st;
+  if (workspace_bytes < rlk::linear_workspace_bytes(N, V)) return RLK_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return RLK_ERR_UNSUPPORTED;
+  return status_of(rlk::launch_linear_logp(
+      static_cast<const uint16_t*>(hidden), ld_h, static_cast<const uint16_t*>(weight), ld_w,
+      targets, mask, N, static_cast<int>(V), static_cast<int>(H), logp, lse, workspace, stream));
+}
+
+int rlk_logp_backward(const void* logits, int64_t ld, const void* hidden, int64_t ld_h,
+                      const void* weight, int64_t ld_w, int64_t H, const int64_t* targets,
+                      const uint8_t* mask, const float* lse, const float* grad_logp, int64_t N,
+                      int64_t V, float* grad_logits, int64_t ld_g, hipStream_t stream) {
+  int st = check_sizes(N, V);
+  if (st != RLK_OK) return st;
+  if (N == 0) return RLK_OK;
+  if (targets == nullptr || lse == nullptr || grad_logp == nullptr || grad_logits == nullptr)
+    return RLK_ERR_INVALID_ARG;
+  if (ld_g < V) return RLK_ERR_INVALID_ARG;
+  if ((ld_g % 4) != 0 || !aligned16(grad_logits)) return RLK_ERR_UNSUPPORTED;
+  if (ld_g > (int64_t(1) << 62) / N) return RLK_ERR_UNSUPPORTED;
+  if (logits != nullptr) {
+    st = check_logits(logits, ld, N, V);
+    if (st != RLK_OK) return st;
+    return status_of(rlk::launch_logp_bwd_rows(static_cast<const uint16_t*>(logits), ld, targets,
+                                               mask, lse, grad_logp, N, static_cast<int>(V),
+                                               grad_logits, ld_g, stream));
+  }
+  st = check_linear(hidden, ld_h, weight, ld_w, N, V, H);
+  if (st != RLK_OK) return st;
+  return status_of(rlk::launch_linear_dlogits(
+      static_cast<const uint16_t*>(hidden), ld_h, static_cast<const uint16_t*>(weight), ld_w,
+      targets, mask, lse, grad_logp, N, static_cast<int>(V), static_cast<int>(H), grad_logits,
+      ld_g, stream));
+}
+
+const char* rlk_status_string(int status) {
+  switch (status) {
+    case RLK_OK: return "RLK_OK";
+    case RLK_ERR_INVALID_ARG: return "RLK_ERR_INVALID_ARG";
+    case RLK_ERR_UNSUPPORTED: return "RLK_ERR_UNSUPPORTED";
+    case RLK_ERR_LAUNCH: return "RLK_ERR_LAUNCH";
+    default: return "unknown";
+  }
+}
+
+#define RLK_STR2(x) #x
+#define RLK_STR(x) RLK_STR2(x)
+
+const char* rlk_build_info(void) {
+  return "rlk 0.1.0; arch=gfx950; rev=" RLK_GIT_REV
+         "; schedule=rows256x8/bwd256x4/tile" RLK_STR(256) "x" RLK_STR(256) "x" RLK_STR(64)
+         "/mfma32x32x16bf16/group8";
+}
+
+}  // extern "C"

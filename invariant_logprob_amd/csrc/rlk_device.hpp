@@ -1,0 +1,102 @@
+// Device-side building blocks shared by the logprob kernels (gfx950).
+//
+// Log-sum-exp state.  A partial reduction over a set of logits is kept as a
+// pair (M, s) in base-2 units:
+//     M = a rounded upper estimate of max(x) * log2(e)   (or -inf if empty)
+//     s = sum_j 2^(x_j * log2(e) - M)                    (fp32)
+// so that log(sum_j exp(x_j)) = ln(2) * (M + log2(s)).  Each term's exponent
+// is formed by one fused multiply-add, x * log2(e) - M, rounded once, and M is
+// the very value used as the offset, so its own rounding cancels out of the
+// result.  Two pairs merge by rescaling to the larger M; the merge below is
+// symmetric in its operands bit for bit (products formed separately, no
+// contraction), so a butterfly leaves every lane with identical bits.
+//
+// Non-finite logits: -inf entries contribute 0 as long as one entry is
+// finite; +inf or NaN anywhere makes the result NaN; an all -inf row gives
+// NaN (log of 0 sum is -inf, and -inf - -inf is NaN in logp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rlk {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load / store (data touched once: non-temporal hint)
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store16_stream(void* p, float a, float b, float c, float d) {
+  f32x4_t v = {a, b, c, d};
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// bf16 pair packed in a 32-bit word -> two exact fp32 values
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Offset used for the exponent of each term: an empty (-inf) state uses 0,
+// so that -inf logits give 2^-inf = 0 instead of NaN.
+__device__ __forceinline__ float lse_offset(float M) { return M == neg_inf() ? 0.0f : M; }
+
+// Symmetric merge of (M, s) with (M2, s2).
+__device__ __forceinline__ void lse_merge(float& M, float& s, float M2, float s2) {
+#pragma clang fp contract(off)
+  const float Mn = fmaxf(M, M2);
+  const float a = (M == Mn) ? 1.0f : fast_exp2(M - Mn);
+  const float b = (M2 == Mn) ? 1.0f : fast_exp2(M2 - Mn);
+  const float p = s * a;
+  const float q = s2 * b;
+  s = p + q;
+  M = Mn;
+}
+
+// Raise the offset of state (M, s) to cover a new block maximum given in
+// natural units; returns the offset to use for the block's terms.
+__device__ __forceinline__ float lse_raise(float& M, float& s, float block_max) {
+  const float Mb = block_max * kLog2e;
+  if (Mb > M) {
+    s = (M == neg_inf()) ? s : s * fast_exp2(M - Mb);
+    M = Mb;
+  }
+  return lse_offset(M);
+}
+
+// Term of the sum for logit x at offset Mu.
+__device__ __forceinline__ float lse_term(float x, float Mu) {
+  return fast_exp2(__builtin_fmaf(x, kLog2e, -Mu));
+}
+
+// Natural-log LSE of a finished state.
+__device__ __forceinline__ float lse_finish(float M, float s) {
+#pragma clang fp contract(off)
+  const float l2 = M + fast_log2(s);
+  return l2 * kLn2;
+}
+
+// Wave64 butterfly: every lane ends with the merge of all 64 lanes, in a
+// fixed pairing order (distance 32, 16, ..., 1).
+__device__ __forceinline__ void wave_lse_allreduce(float& M, float& s) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const float M2 = __shfl_xor(M, d, 64);
+    const float s2 = __shfl_xor(s, d, 64);
+    lse_merge(M, s, M2, s2);
+  }
+}
+
+}  // namespace rlk

@@ -1,0 +1,42 @@
+// Internal launchers behind the C ABI (include/rlk.h) and the compile-time
+// schedule constants that fix every reduction order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rlk {
+
+// Fused path tile schedule: 256 vocabulary entries x 256 tokens per tile,
+// K in stages of 64.  The vocabulary tile is also the log-sum-exp chunk.
+constexpr int kLinearVocabTile = 256;
+constexpr int kLinearTokenTile = 256;
+constexpr int kLinearKStage = 64;
+// Vocabulary tiles grouped together in the launch order (scheduling only).
+constexpr int kLinearVocabGroup = 8;
+
+int logits_schedule_threads();
+int logits_schedule_unroll();
+
+hipError_t launch_logp_fwd_rows(const uint16_t* logits, int64_t ld, const int64_t* targets,
+                                const uint8_t* mask, int64_t N, int V, float* logp, float* lse,
+                                hipStream_t stream);
+
+hipError_t launch_logp_bwd_rows(const uint16_t* logits, int64_t ld, const int64_t* targets,
+                                const uint8_t* mask, const float* lse, const float* grad, int64_t N,
+                                int V, float* dl, int64_t ldg, hipStream_t stream);
+
+size_t linear_workspace_bytes(int64_t N, int64_t V);
+
+hipError_t launch_linear_logp(const uint16_t* hidden, int64_t ldh, const uint16_t* weight,
+                              int64_t ldw, const int64_t* targets, const uint8_t* mask, int64_t N,
+                              int V, int H, float* logp, float* lse, void* workspace,
+                              hipStream_t stream);
+
+hipError_t launch_linear_dlogits(const uint16_t* hidden, int64_t ldh, const uint16_t* weight,
+                                 int64_t ldw, const int64_t* targets, const uint8_t* mask,
+                                 const float* lse, const float* grad, int64_t N, int V, int H,
+                                 float* dl, int64_t ldg, hipStream_t stream);
+
+}  // namespace rlk

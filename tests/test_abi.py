@@ -1,0 +1,113 @@
+"""The C-ABI library loads, exports what include/rlk.h declares, and rejects
+bad arguments before any launch (CPU only: validation never touches the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import invariant_logprob_amd as ilp
+from invariant_logprob_amd import build as rlk_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rlk.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ilp.library_path()):
+        rlk_build.build()
+    return ilp.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rlk_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("rlk_logp_selected", "rlk_linear_logp", "rlk_logp_backward",
+              "rlk_linear_logp_workspace_size", "rlk_status_string", "rlk_build_info"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_build_info_and_status_strings(lib):
+    info = ilp.build_info()
+    assert "gfx950" in info and "rlk" in info
+    assert lib.rlk_status_string(0) == b"RLK_OK"
+    assert lib.rlk_status_string(2) == b"RLK_ERR_UNSUPPORTED"
+    assert lib.rlk_status_string(99) == b"unknown"
+
+
+# Fake device addresses: validation rejects before any launch, so these are
+# never dereferenced.  A16 is 16-byte aligned, A2 is not.
+A16 = ctypes.c_void_p(0x10000)
+A2 = ctypes.c_void_p(0x10002)
+NUL = None
+
+
+def test_logp_selected_validation(lib):
+    f = lib.rlk_logp_selected
+    assert f(A16, 1024, A16, NUL, 0, 1024, A16, NUL, NUL) == OK          # N == 0: no-op
+    assert f(A16, 1024, A16, NUL, -1, 1024, A16, NUL, NUL) == INVALID
+    assert f(A16, 1024, A16, NUL, 4, 0, A16, NUL, NUL) == INVALID        # V < 1
+    assert f(NUL, 1024, A16, NUL, 4, 1024, A16, NUL, NUL) == INVALID     # no logits
+    assert f(A16, 1024, NUL, NUL, 4, 1024, A16, NUL, NUL) == INVALID     # no targets
+    assert f(A16, 1024, A16, NUL, 4, 1024, NUL, NUL, NUL) == INVALID     # no logp
+    assert f(A16, 1000, A16, NUL, 4, 1024, A16, NUL, NUL) == INVALID     # ld < V
+    assert f(A16, 1028, A16, NUL, 4, 1024, A16, NUL, NUL) == UNSUPPORTED  # ld % 8
+    assert f(A2, 1024, A16, NUL, 4, 1024, A16, NUL, NUL) == UNSUPPORTED   # misaligned
+    assert f(A16, 1 << 29, A16, NUL, 4, 1 << 29, A16, NUL, NUL) == UNSUPPORTED  # V too large
+
+
+def test_linear_logp_validation(lib):
+    f = lib.rlk_linear_logp
+    ws = lib.rlk_linear_logp_workspace_size(300, 1000, 64)
+    assert ws >= 4 * 300 * 8 + 300 * 4
+    args = lambda **k: [k.get("h", A16), k.get("ldh", 64), k.get("w", A16), k.get("ldw", 64),
+                        A16, NUL, k.get("n", 300), k.get("v", 1000), k.get("H", 64), A16, NUL,
+                        k.get("ws", A16), k.get("wsb", ws), NUL]
+    assert f(*args(n=0)) == OK
+    assert f(*args(H=0)) == INVALID
+    assert f(*args(ldh=56)) == INVALID                     # ld_h < H
+    assert f(*args(wsb=ws - 1)) == INVALID                 # workspace too small
+    assert f(*args(ws=NUL)) == INVALID
+    assert f(*args(H=60, ldh=64, ldw=64)) == UNSUPPORTED   # H % 8
+    assert f(*args(ldw=68)) == UNSUPPORTED                 # ld_w % 8
+    assert f(*args(w=A2)) == UNSUPPORTED
+    assert f(*args(ws=A2)) == UNSUPPORTED
+
+
+def test_backward_validation(lib):
+    f = lib.rlk_logp_backward
+    base = dict(lg=A16, ld=1024, h=NUL, ldh=0, w=NUL, ldw=0, H=0, t=A16, m=NUL, lse=A16, g=A16,
+                n=4, v=1024, out=A16, ldg=1024)
+    call = lambda **k: f(*[{**base, **k}[x] for x in ("lg", "ld", "h", "ldh", "w", "ldw", "H", "t",
+                                                      "m", "lse", "g", "n", "v", "out", "ldg")], NUL)
+    assert call(n=0) == OK
+    assert call(lse=NUL) == INVALID
+    assert call(g=NUL) == INVALID
+    assert call(ldg=1000) == INVALID
+    assert call(ldg=1026) == UNSUPPORTED
+    assert call(out=ctypes.c_void_p(0x10008)) == UNSUPPORTED
+    # fused mode (logits NULL) needs hidden and weight
+    assert call(lg=NUL) == INVALID
+    assert call(lg=NUL, h=A16, ldh=64, w=A16, ldw=64, H=0) == INVALID
+    assert call(lg=NUL, h=A16, ldh=64, w=A2, ldw=64, H=64) == UNSUPPORTED
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(2, 8, dtype=torch.bfloat16)
+    t = torch.zeros(2, dtype=torch.int64)
+    with pytest.raises(ValueError):
+        ilp.logp_selected(x, t)

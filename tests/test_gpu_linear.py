@@ -1,0 +1,191 @@
+"""GPU parity and bitwise invariance of the fused lm_head + selected logprob
+(linear_logp, K3 + K4) and of its backward to the logits (K5), through the C
+ABI, against the fp64 oracle."""
+import json
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import invariance as inv
+import invariant_logprob_amd as ilp
+import oracle
+from gpu_util import TOL_BWD, TOL_FUSED, assert_close, bits16, f32bits, require_gpu
+from invariant_logprob_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    d = require_gpu()
+    ilp.load_library()
+    return d
+
+
+def _oracle_fused(hidden, weight, targets, mask=None):
+    return oracle.linear_logp(bits16(hidden), bits16(weight), targets.cpu().numpy(),
+                              None if mask is None else mask.cpu().numpy())
+
+
+@pytest.mark.parametrize("n,v,h", [(1, 256, 64), (37, 1000, 136), (300, 2600, 512), (257, 513, 8)])
+def test_small_parity_fwd_bwd(dev, n, v, h):
+    b = wl.fused_batch(n, v, h, seed=n + v + h, device=dev, w_sigma=0.05, n_masked=n // 10)
+    logp, lse = ilp.linear_logp(b.hidden, b.weight, b.targets, b.mask)
+    torch.cuda.synchronize()
+    rlogp, rlse = _oracle_fused(b.hidden, b.weight, b.targets, b.mask)
+    act = b.mask.cpu().numpy().astype(bool)
+    assert_close(logp.cpu().numpy(), rlogp, TOL_FUSED, f"fused logp {n}x{v}x{h}", act)
+    assert_close(lse.cpu().numpy(), rlse, TOL_FUSED, f"fused lse {n}x{v}x{h}", act)
+    assert bool((f32bits(logp)[~torch.from_numpy(act)] == 0).all())
+    d = ilp.linear_logp_backward(b.hidden, b.weight, b.targets, lse, b.grad, b.mask)
+    torch.cuda.synchronize()
+    rd = oracle.linear_logp_backward(bits16(b.hidden), bits16(b.weight), b.targets.cpu().numpy(),
+                                     b.mask.cpu().numpy(), lse.cpu().numpy(), b.grad.cpu().numpy())
+    assert_close(d.cpu().numpy(), rd, TOL_BWD, f"fused dlogits {n}x{v}x{h}")
+    assert bool((f32bits(d)[~torch.from_numpy(act)] == 0).all())
+
+
+def test_closed_forms(dev):
+    v, h = 700, 128
+    w = (torch.randn((v, h), device=dev) * 0.5).to(torch.bfloat16)
+    hid = torch.zeros((5, h), dtype=torch.bfloat16, device=dev)   # z == 0 exactly
+    t = torch.tensor([0, 1, 2, 3, 699], device=dev)
+    logp, _ = ilp.linear_logp(hid, w, t)
+    assert np.allclose(logp.cpu().numpy(), -math.log(v), atol=1e-5, rtol=0)
+    # identical weight rows: uniform logits for any hidden row
+    w2 = w[:1].repeat(v, 1).contiguous()
+    hid2 = torch.randn((5, h), device=dev).to(torch.bfloat16)
+    logp2, _ = ilp.linear_logp(hid2, w2, t)
+    assert np.allclose(logp2.cpu().numpy(), -math.log(v), atol=1e-4, rtol=0)
+    # invalid target on an active row -> NaN; masked row -> exactly 0
+    t3 = torch.tensor([0, -1, 700, 5, 6], device=dev)
+    mask = torch.tensor([1, 1, 1, 0, 1], dtype=torch.uint8, device=dev)
+    logp3, lse3 = ilp.linear_logp(hid2, w, t3, mask)
+    lp = logp3.cpu().numpy()
+    assert np.isnan(lp[1]) and np.isnan(lp[2]) and not np.isnan(lp[0])
+    assert int(f32bits(logp3)[3]) == 0
+    d = ilp.linear_logp_backward(hid2, w, t3, lse3, torch.ones(5, device=dev), mask)
+    assert bool(torch.isnan(d[1]).all()) and bool((f32bits(d[3]) == 0).all())
+
+
+def _bits_equal(a, b):
+    return torch.equal(f32bits(a), f32bits(b))
+
+
+def test_tile_offset_sweep(dev):
+    """The same token row at every kind of position inside a 256-row token
+    block, among random neighbours, gives the bits it gives alone."""
+    v, h = 1300, 256
+    g = torch.Generator(device=dev).manual_seed(42)
+    w = (torch.randn((v, h), generator=g, device=dev) * 0.05).to(torch.bfloat16)
+    probe = torch.randn((3, h), generator=g, device=dev).to(torch.bfloat16)
+    pt = torch.randint(0, v, (3,), generator=g, device=dev)
+    alone = [ilp.linear_logp(probe[i:i + 1], w, pt[i:i + 1]) for i in range(3)]
+    for off in (0, 1, 5, 31, 32, 33, 63, 64, 127, 128, 200, 255, 256, 300, 511):
+        n = max(off + 1, 257) + 3
+        hid = torch.randn((n, h), generator=g, device=dev).to(torch.bfloat16)
+        tt = torch.randint(0, v, (n,), generator=g, device=dev)
+        for i in range(3):
+            hid[off] = probe[i]
+            tt[off] = pt[i]
+            lp, ls = ilp.linear_logp(hid, w, tt)
+            assert int(f32bits(lp)[off]) == int(f32bits(alone[i][0])[0]), (off, i)
+            assert int(f32bits(ls)[off]) == int(f32bits(alone[i][1])[0]), (off, i)
+
+
+def test_fused_transforms_small(dev):
+    n, v, h = 600, 1500, 192
+    b = wl.fused_batch(n, v, h, seed=5, device=dev, w_sigma=0.05, n_masked=40)
+    w = b.weight
+    base = {"x": b.hidden, "targets": b.targets, "mask": b.mask, "grad": b.grad}
+
+    def run(batch):
+        logp, lse = ilp.linear_logp(batch["x"], w, batch["targets"], batch["mask"])
+        d = ilp.linear_logp_backward(batch["x"], w, batch["targets"], lse, batch["grad"],
+                                     batch["mask"])
+        return {"logp": logp, "lse": lse, "dlogits": d}
+
+    def filler(k, seed):
+        gg = torch.Generator(device=dev).manual_seed(seed)
+        return {"x": (torch.randn((k, h), generator=gg, device=dev) * 3).to(torch.bfloat16),
+                "targets": torch.randint(0, v, (k,), generator=gg, device=dev),
+                "mask": torch.ones(k, dtype=torch.uint8, device=dev),
+                "grad": torch.randn((k,), generator=gg, device=dev)}
+
+    cases = [("T1", {"size": s, "start": st}, inv.t1_population(base, s, st))
+             for s, st in ((1, 0), (33, 5), (257, 100))]
+    cases += [("T2", {"seed": 1}, inv.t2_position(base, 1)),
+              ("T3", {"keep": "every 7th"}, inv.t3_neighbours(base, list(range(0, n, 7)), filler, 2)),
+              ("T4", {"left": 9, "every": 50}, inv.t4_padding(base, filler, 3, left=9, right=4, every=50)),
+              ("T5", {"chunk": 128}, inv.t5_schedule(base, 128)),
+              ("T6", {"compacted": True}, inv.t6_compacted(base))]
+    failures = []
+    base_out = None
+    for cls, params, (calls, row_map) in cases:
+        man = {"operator": "linear_logp", "chain_index": 7, "seed": 5,
+               "transform": {"class": cls, "name": inv.TRANSFORM_NAMES[cls], **params}}
+        recs, base_out = inv.check(run, base, calls, row_map, man, base_out)
+        failures += recs
+    assert not failures, json.dumps(failures[:3], indent=1)
+
+
+def test_fused_large_config(dev):
+    """hidden [8192, 4096], W [128256, 4096]: sampled rows against the oracle,
+    and the same rows bitwise at N = 1, 33 and 8192."""
+    b = wl.fused_large(seed=0, device=dev)
+    logp, lse = ilp.linear_logp(b.hidden, b.weight, b.targets, b.mask)
+    torch.cuda.synchronize()
+    rows = [0, 1, 32, 255, 256, 4097, 8190, 8191]
+    idx = torch.tensor(rows, device=dev)
+    sub_h = b.hidden.index_select(0, idx)
+    sub_t = b.targets.index_select(0, idx)
+    rlogp, rlse = _oracle_fused(sub_h, b.weight, sub_t)
+    assert_close(logp.index_select(0, idx).cpu().numpy(), rlogp, TOL_FUSED, "C4 logp")
+    assert_close(lse.index_select(0, idx).cpu().numpy(), rlse, TOL_FUSED, "C4 lse")
+    for r in rows[:4]:
+        one = ilp.linear_logp(b.hidden[r:r + 1], b.weight, b.targets[r:r + 1])
+        assert _bits_equal(one[0], logp[r:r + 1]) and _bits_equal(one[1], lse[r:r + 1]), r
+    s33 = ilp.linear_logp(b.hidden[4090:4123], b.weight, b.targets[4090:4123])
+    assert _bits_equal(s33[0], logp[4090:4123]) and _bits_equal(s33[1], lse[4090:4123])
+
+
+def test_fused_backward_schedules(dev):
+    """hidden [2048, 5120], W [151936, 5120]: one prefill launch vs 4 chunks
+    of 512 vs 2048 single-row decode launches give identical logp, lse and
+    dlogits bits; sampled rows match the oracle."""
+    b = wl.fused_bwd(seed=0, device=dev)
+    n = b.hidden.shape[0]
+    logp, lse = ilp.linear_logp(b.hidden, b.weight, b.targets, b.mask)
+    d = ilp.linear_logp_backward(b.hidden, b.weight, b.targets, lse, b.grad, b.mask)
+    torch.cuda.synchronize()
+    rows = [0, 5, 511, 512, 1500, 2047]
+    idx = torch.tensor(rows, device=dev)
+    sub_h = b.hidden.index_select(0, idx)
+    sub_t = b.targets.index_select(0, idx)
+    rlogp, rlse = _oracle_fused(sub_h, b.weight, sub_t)
+    assert_close(logp.index_select(0, idx).cpu().numpy(), rlogp, TOL_FUSED, "C5 logp")
+    rd = oracle.linear_logp_backward(bits16(sub_h), bits16(b.weight), sub_t.cpu().numpy(), None,
+                                     lse.index_select(0, idx).cpu().numpy(),
+                                     b.grad.index_select(0, idx).cpu().numpy())
+    assert_close(d.index_select(0, idx).cpu().numpy(), rd, TOL_BWD, "C5 dlogits")
+    # 4 chunks of 512
+    for c0 in range(0, n, 512):
+        sl = slice(c0, c0 + 512)
+        lp_c, ls_c = ilp.linear_logp(b.hidden[sl], b.weight, b.targets[sl], b.mask[sl])
+        assert _bits_equal(lp_c, logp[sl]) and _bits_equal(ls_c, lse[sl]), c0
+        d_c = ilp.linear_logp_backward(b.hidden[sl], b.weight, b.targets[sl], ls_c, b.grad[sl],
+                                       b.mask[sl])
+        assert _bits_equal(d_c, d[sl]), c0
+    # one launch per row (decode); the dlogits rows are checked on a subset
+    lp_rows = torch.empty_like(logp)
+    ls_rows = torch.empty_like(lse)
+    for r in range(n):
+        ilp.linear_logp(b.hidden[r:r + 1], b.weight, b.targets[r:r + 1], b.mask[r:r + 1],
+                        logp=lp_rows[r:r + 1], lse=ls_rows[r:r + 1])
+    assert _bits_equal(lp_rows, logp) and _bits_equal(ls_rows, lse)
+    for r in (0, 777, 2047):
+        d_r = ilp.linear_logp_backward(b.hidden[r:r + 1], b.weight, b.targets[r:r + 1],
+                                       lse[r:r + 1], b.grad[r:r + 1], b.mask[r:r + 1])
+        assert _bits_equal(d_r, d[r:r + 1]), r
