@@ -41,7 +41,22 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--legs", default="logits_fwd,logits_bwd,fused_fwd,fused_fb")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="instead of the hot path, run a plain 1 GiB device copy 5 times "
+                        "(reference for hardware traffic counters)")
     return p.parse_args()
+
+
+def calibrate_copy(torch):
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": nbytes,
+                      "bytes_written_per_copy": nbytes, "copies": 5}))
 
 
 def main():
@@ -52,6 +67,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
 
     import invariant_logprob_amd as ilp
     from invariant_logprob_amd import workloads as wl
@@ -204,24 +223,31 @@ def main():
     print(json.dumps(rec))
 
 
-def cpu_baseline(c3, torch):
-    """The fp64 oracle, as it stands, on the first 256 rows of the same
-    logits workload; tokens/s over the active rows of that sample."""
+def cpu_baseline(c3, torch, budget_s=15.0, block=256):
+    """The fp64 oracle, as it stands, on a bounded sample of the same logits
+    workload: consecutive 256-row blocks from the first row until about
+    ``budget_s`` seconds of CPU work; tokens/s over the sample's active rows."""
     import numpy as np
 
     import oracle
-    rows = 256
-    bits = c3.logits[:rows].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
-    t = c3.targets[:rows].cpu().numpy()
-    m = c3.mask[:rows].cpu().numpy()
-    t0 = time.perf_counter()
-    oracle.logp_selected(bits, t, m)
-    dt = time.perf_counter() - t0
-    active = int(m.astype(bool).sum())
-    return {"value": active / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {rows} rows ({active} active) of the N=16384 V=151936 logits "
-                      f"workload, {dt:.1f} s",
-            "host": platform.processor() or platform.machine(), "host_cpus": os.cpu_count()}
+    n = c3.logits.shape[0]
+    done_rows = 0
+    active = 0
+    spent = 0.0
+    while done_rows < n and spent < budget_s:
+        r1 = min(n, done_rows + block)
+        bits = c3.logits[done_rows:r1].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+        t = c3.targets[done_rows:r1].cpu().numpy()
+        m = c3.mask[done_rows:r1].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.logp_selected(bits, t, m)
+        spent += time.perf_counter() - t0
+        active += int(m.astype(bool).sum())
+        done_rows = r1
+    return {"value": active / spent, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done_rows} rows ({active} active) of the N=16384 V=151936 logits "
+                      f"workload, {spent:.1f} s of oracle time (numpy float64, one thread)",
+            "host_cpus": os.cpu_count(), "host": platform.processor() or platform.machine()}
 
 
 if __name__ == "__main__":

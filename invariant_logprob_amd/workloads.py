@@ -116,7 +116,7 @@ def logits_large(seed=0, device="cpu", n=16384, v=151936):
 def logits_varlen(seed=0, device="cpu", n_seqs=8, v=32000, len_lo=64, len_hi=1024,
                   pad_multiple=128, sigma=3.0, peaked_frac=0.05, peak=20.0):
     g = _gen(seed, device)
-    lens = torch.randint(len_lo, len_hi + 1, (n_seqs,), generator=g, device="cpu").tolist()
+    lens = torch.randint(len_lo, len_hi + 1, (n_seqs,), generator=g, device=device).tolist()
     total = sum(lens)
     n = ((total + pad_multiple - 1) // pad_multiple) * pad_multiple
     x = torch.empty((n, v), dtype=torch.bfloat16, device=device)

@@ -123,8 +123,9 @@ def test_large_config_sampled_rows(dev):
 
 
 def test_closed_forms(dev):
-    for v in (1, 1024, 32000, 151936):
-        x = torch.full((3, v), 2.5, dtype=torch.bfloat16, device=dev)
+    for v in (1, 3, 1024, 32000, 151936):
+        ld = (v + 7) // 8 * 8
+        x = padded_bf16(3, v, ld, torch.full((3, v), 2.5, dtype=torch.bfloat16, device=dev))
         t = torch.tensor([0, v // 2, v - 1], device=dev)
         logp, lse = ilp.logp_selected(x, t)
         ref = -math.log(v)
