@@ -47,6 +47,33 @@ def parse():
     return p.parse_args()
 
 
+def source_hash():
+    """Hash of the kernel sources and the C header (identifies a kernel build)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "invariant_logprob_amd", "csrc", "*"))) + \
+            [os.path.join(ROOT, "include", "rlk.h")]:
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    {} when the kernels have changed since those counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hot_path_kernels_hbm_traffic.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return {}
+    if rec.get("source_hash") != source_hash():
+        return {}
+    return {k: v["read_bytes"] + v["write_bytes"] for k, v in rec.get("per_launch", {}).items()}
+
+
 def calibrate_copy(torch):
     nbytes = 1 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
@@ -149,6 +176,7 @@ def main():
 
     out_legs = {}
     roofline = None
+    traffic = measured_traffic()
     if "logits_fwd" in legs:
         bytes_fwd = act3 * v3 * 2 + n3 * (8 + 1 + 8)
         gbs = bytes_fwd / (ms["logits_fwd"] * 1e-3) / 1e9
@@ -158,7 +186,8 @@ def main():
                                   "hbm_frac": gbs / HBM_PEAK_GBS}
         roofline = {"kernel": "logp_fwd_rows", "bound": "hbm", "achieved": gbs,
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                    "traffic": None}
+                    "traffic": traffic.get("logp_fwd_rows"), "traffic_unit": "bytes per launch",
+                    "algorithmic_bytes": bytes_fwd}
     if "logits_bwd" in legs:
         bytes_bwd = act3 * v3 * 2 + n3 * v3 * 4 + n3 * (8 + 1 + 4 + 4)
         gbs = bytes_bwd / (ms["logits_bwd"] * 1e-3) / 1e9
@@ -213,7 +242,9 @@ def main():
         "fused_roofline": ({"kernel": "linear_tiles", "bound": "mfma",
                             "achieved": out_legs["fused_fwd"]["TFLOP_per_s"],
                             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                            "frac": out_legs["fused_fwd"]["mfma_frac"], "traffic": None}
+                            "frac": out_legs["fused_fwd"]["mfma_frac"],
+                            "traffic": traffic.get("linear_tiles_fwd_8192x128256x4096"),
+                            "traffic_unit": "bytes per launch"}
                            if "fused_fwd" in out_legs else None),
         "cpu_baseline": cpu,
         "build": ilp.build_info(),

@@ -9,14 +9,15 @@
 // (tokens) the "N" side, so each lane of the result holds 16 vocabulary
 // entries of one token and a token's log-sum-exp is mostly lane-local.
 //
-// Tile = 256 vocabulary entries x 256 tokens, 4 waves as 2 (vocab) x 2
-// (tokens), each wave 128 x 128 = 4 x 4 MFMA blocks.  A 256-wide vocabulary
+// Tile = 256 vocabulary entries x 256 tokens, 8 waves (two per SIMD, so one
+// wave's MFMAs cover the other's LDS and copy work) as 2 (vocab) x 4
+// (tokens), each wave 128 x 64 = 4 x 2 MFMA blocks.  A 256-wide vocabulary
 // tile is also the reduction chunk: per token, the tile's 256 logits are
 // reduced in a fixed order (lane-local ascending, then the two lane halves,
 // then the two vocabulary waves) to one (M, s) partial, written to the
-// workspace.  A second kernel merges a row's partials in ascending chunk
-// order.  Rows beyond N in the last token block are zero-filled and never
-// written.  The logits stay fp32 and are never rounded to bf16.
+// workspace.  A second kernel merges a row's partials in a fixed order.
+// Rows beyond N in the last token block are zero-filled and never written.
+// The logits stay fp32 and are never rounded to bf16.
 //
 // The pages fix the contract these kernels keep: bitwise batch invariance
 // (page "[RFC] Batch-Invariant RL Kernel Suite for Train-Inference
@@ -45,18 +46,29 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kBV = kLinearVocabTile;   // vocabulary entries per tile (= chunk)
 constexpr int kBT = kLinearTokenTile;   // tokens per tile
 constexpr int kBK = kLinearKStage;      // K per pipeline stage
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;               // 2 (vocabulary) x 4 (tokens), two per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWT = kWaves / 2;         // waves along the token side
+constexpr int kTW = kBT / kWT;          // tokens per wave (64)
+constexpr int kJ = kTW / 32;            // 32-token MFMA blocks per wave (2)
+constexpr int kI = (kBV / 2) / 32;      // 32-entry vocabulary blocks per wave (4)
 constexpr int kRowChunks = kBK / 8;     // 16-byte chunks per tile row per stage
 constexpr int kAVec = kBV * kRowChunks; // uint4 per stage, W side
 constexpr int kBVec = kBT * kRowChunks; // uint4 per stage, hidden side
 constexpr int kStageVec = kAVec + kBVec;
-constexpr int kLoadsPerThread = kAVec / kThreads;   // 8
+constexpr int kBlkPerWave = (kAVec / 64) / kWaves;  // 1 KB copies per wave per operand per stage
+constexpr int kSub = kBK / 16;          // 16-deep MFMA steps per stage
+constexpr int kStageStride = 132;       // floats per staged dlogits row (128 + 4 pad)
+constexpr int kStagingVec = kWaves * 32 * kStageStride / 4;
+constexpr int kSmemVec = (2 * kStageVec > kStagingVec) ? 2 * kStageVec : kStagingVec;
 static_assert(kAVec == kBVec, "loader assumes square tiles");
 static_assert(kRowChunks == 8, "swizzle assumes 8 chunks per row");
-static_assert(kLoadsPerThread * 4 * 8 == kBV, "4 waves x 8 loads x 8 rows cover the tile");
+static_assert(kBlkPerWave % 2 == 0, "a stage's copies are issued in two halves");
+static_assert(kSmemVec * 16 <= 160 * 1024, "LDS budget of one CU");
 
 // Word 3 of a raw buffer resource on gfx9-family parts (data format field)
 constexpr int kBufferResourceWord3 = 0x00020000;
+
 // Raw buffer resource over [base, base + bytes), built from wave-uniform
 // values so that it lives in scalar registers.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const uint16_t* base, int64_t bytes) {
@@ -92,7 +104,7 @@ struct TileArgs {
   int n_vtiles;
   int n_tblocks;
   // forward outputs
-  float2* part;   // [n_vtiles][N] (M, s)
+  float2* part;   // [N][n_vtiles] (M, s)
   float* zt;      // [N] target logit
   // backward inputs / output
   const float* lse;
@@ -122,15 +134,15 @@ __device__ __forceinline__ void tile_coords(int w, int n_vtiles, int n_tblocks, 
 }
 
 template <bool kBackward>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void linear_tiles(TileArgs args) {
-  __shared__ uint4 smem[2 * kStageVec];
+  __shared__ uint4 smem[kSmemVec];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wv = wave >> 1;  // vocabulary half of the tile
-  const int wt = wave & 1;   // token half of the tile
+  const int wv = wave / kWT;  // vocabulary half of the tile
+  const int wt = wave % kWT;  // token quarter of the tile
   int vt, tb;
   tile_coords(blockIdx.x, args.n_vtiles, args.n_tblocks, vt, tb);
   const int vocab0 = vt * kBV;
@@ -141,76 +153,100 @@ void linear_tiles(TileArgs args) {
   const int n_kt = (H + kBK - 1) / kBK;
 
   // Loader: global -> LDS directly (buffer_load ... lds), no staging
-  // registers.  Each wave instruction fills 1 KB of LDS = 8 tile rows of 128
-  // bytes; lane l writes physical chunk (l & 7) of row 8 q + (l >> 3), which
-  // holds logical chunk (l & 7) ^ swizzle(row).  Rows past V (or N) fall
-  // outside the buffer's range and read as zero; chunks past H are forced
-  // out of range the same way.
+  // registers.  One wave instruction fills 1 KB of LDS = 8 tile rows of 128
+  // bytes; lane l writes physical chunk (l & 7) of its row, which holds
+  // logical chunk (l & 7) ^ swizzle(row).  Rows past V (or N) lie outside the
+  // buffer's range and read as zero.  Each lane's byte offset is fixed for
+  // the whole K loop; a stage's K position goes into the scalar offset.  In
+  // a ragged last stage, chunks past H are forced out of range (zero).
   const __amdgpu_buffer_rsrc_t wres =
       uniform_rsrc(args.weight + static_cast<int64_t>(vocab0) * args.ldw, V_tail * args.ldw * 2);
   const __amdgpu_buffer_rsrc_t hres = uniform_rsrc(args.hidden + tok0 * args.ldh, N_tail * args.ldh * 2);
-  const int lrow = lane >> 3;   // row within an 8-row block
-  const int lpc = lane & 7;     // physical chunk this lane fills
-
-  auto issue = [&](int kt, int st) {
+  int voff_w[kBlkPerWave], voff_h[kBlkPerWave], kcol[kBlkPerWave];
+#pragma unroll
+  for (int q = 0; q < kBlkPerWave; ++q) {
+    const int idx = (wave * kBlkPerWave + q) * 64 + lane;
+    const int r = idx / kRowChunks;
+    const int c = (idx % kRowChunks) ^ ((r >> 1) & 7);
+    kcol[q] = 8 * c;
+    voff_w[q] = (r * static_cast<int>(args.ldw) + 8 * c) * 2;
+    voff_h[q] = (r * static_cast<int>(args.ldh) + 8 * c) * 2;
+  }
+  // copies q in [q0, q1) of stage kt into LDS buffer st
+  auto issue = [&](int kt, int st, int q0, int q1) {
     const int k0 = kt * kBK;
+    const bool full = (k0 + kBK) <= H;
     uint4* a = smem + st * kStageVec;
     uint4* b = a + kAVec;
 #pragma unroll
-    for (int q = 0; q < kLoadsPerThread; ++q) {
-      const int blk = wave * kLoadsPerThread + q;     // 8-row block of the tile
-      const int r = blk * 8 + lrow;
-      const int c = lpc ^ ((r >> 1) & 7);
-      const int k = k0 + 8 * c;
-      const int woff = (k < H) ? (r * static_cast<int>(args.ldw) + k) * 2 : kOutOfRange;
-      const int hoff = (k < H) ? (r * static_cast<int>(args.ldh) + k) * 2 : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          wres, to_lds(a + blk * 64), 16, woff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          hres, to_lds(b + blk * 64), 16, hoff, 0, 0, 0);
+    for (int q = q0; q < q1; ++q) {
+      const int blk = wave * kBlkPerWave + q;
+      int vw = voff_w[q], vh = voff_h[q];
+      if (!full && (k0 + kcol[q]) >= H) {
+        vw = kOutOfRange;
+        vh = kOutOfRange;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, to_lds(a + blk * 64), 16, vw, k0 * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(hres, to_lds(b + blk * 64), 16, vh, k0 * 2, 0, 0);
     }
   };
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[kI][kJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  auto compute = [&](int st) {
-    const uint4* a = smem + st * kStageVec;
-    const uint4* b = a + kAVec;
+  // MFMA operands of one 16-deep step: lane supplies row (lane & 31) and
+  // k-chunk (lane >> 5) of each 32-row block
+  auto frag = [&](const uint4* a, const uint4* b, int kk, bf16x8_t (&fa)[kI], bf16x8_t (&fb)[kJ]) {
+    const int c = 2 * kk + (lane >> 5);
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int c = 2 * kk + (lane >> 5);
-      bf16x8_t fa[4], fb[4];
+    for (int i = 0; i < kI; ++i) {
+      const int r = wv * 128 + i * 32 + (lane & 31);
+      fa[i] = __builtin_bit_cast(bf16x8_t, a[r * kRowChunks + swz(r, c)]);
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wv * 128 + i * 32 + (lane & 31);
-        fa[i] = __builtin_bit_cast(bf16x8_t, a[r * kRowChunks + swz(r, c)]);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wt * 128 + j * 32 + (lane & 31);
-        fb[j] = __builtin_bit_cast(bf16x8_t, b[r * kRowChunks + swz(r, c)]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < kJ; ++j) {
+      const int r = wt * kTW + j * 32 + (lane & 31);
+      fb[j] = __builtin_bit_cast(bf16x8_t, b[r * kRowChunks + swz(r, c)]);
     }
   };
+  auto mma = [&](const bf16x8_t (&fa)[kI], const bf16x8_t (&fb)[kJ]) {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int i = 0; i < kI; ++i)
+#pragma unroll
+      for (int j = 0; j < kJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
+  };
 
-  // main loop: K stages in ascending order, two LDS buffers; the next
-  // stage's loads are in flight while the current stage is multiplied
-  issue(0, 0);
+  // Main loop: K stages in ascending order through two LDS buffers.  At the
+  // top of stage kt each wave waits for its own copies of stage kt, and the
+  // barrier makes every wave's copies visible (and frees the other buffer);
+  // stage kt + 1's copies are then issued during the first two MFMA steps.
+  // The wait and the barrier form one asm statement so that no LDS read can
+  // be scheduled between them.
+  issue(0, 0, 0, kBlkPerWave);
   for (int kt = 0; kt < n_kt; ++kt) {
-    __syncthreads();  // stage kt has landed; everyone is done with the other buffer
-    if (kt + 1 < n_kt) issue(kt + 1, (kt + 1) & 1);
-    compute(kt & 1);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    const bool pf = (kt + 1) < n_kt;
+    const uint4* a = smem + (kt & 1) * kStageVec;
+    const uint4* b = a + kAVec;
+    bf16x8_t fa0[kI], fb0[kJ], fa1[kI], fb1[kJ];
+    frag(a, b, 0, fa0, fb0);
+#pragma unroll
+    for (int kk = 0; kk < kSub; kk += 2) {
+      frag(a, b, kk + 1, fa1, fb1);
+      if (pf && kk == 0) issue(kt + 1, (kt + 1) & 1, 0, kBlkPerWave / 2);
+      mma(fa0, fb0);
+      if (kk + 2 < kSub) frag(a, b, kk + 2, fa0, fb0);
+      if (pf && kk == 0) issue(kt + 1, (kt + 1) & 1, kBlkPerWave / 2, kBlkPerWave);
+      mma(fa1, fb1);
+    }
   }
   __syncthreads();
 
@@ -222,12 +258,12 @@ void linear_tiles(TileArgs args) {
   if constexpr (!kBackward) {
     float2* red = reinterpret_cast<float2*>(smem);  // [2][kBT], after the loop's last barrier
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tl = wt * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < kJ; ++j) {
+      const int tl = wt * kTW + j * 32 + (lane & 31);
       const int64_t tok = tok0 + tl;
       float mx = neg_inf();
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kI; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int m = wv * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
@@ -237,7 +273,7 @@ void linear_tiles(TileArgs args) {
       float s = 0.0f;
       const float Mu = lse_raise(M, s, mx);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kI; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int m = wv * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
@@ -257,7 +293,7 @@ void linear_tiles(TileArgs args) {
             const int et = ((rem >> 3) << 2) | (rem & 3);
             float val = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < kI; ++i)
 #pragma unroll
               for (int e = 0; e < 16; ++e)
                 if (i == it && e == et) val = acc[i][j][e];
@@ -271,29 +307,32 @@ void linear_tiles(TileArgs args) {
       if (half == 0) red[wv * kBT + tl] = make_float2(M, s);
     }
     __syncthreads();
-    {
-      const int tl = tid;  // kThreads == kBT
+    if (tid < kBT) {
+      const int tl = tid;
       float2 p0 = red[tl];
       const float2 p1 = red[kBT + tl];
       lse_merge(p0.x, p0.y, p1.x, p1.y);
-      if (tl < N_tail) args.part[static_cast<int64_t>(vt) * args.N + tok0 + tl] = p0;
+      if (tl < N_tail) args.part[(tok0 + tl) * args.n_vtiles + vt] = p0;
     }
   } else {
+    // dlogits tile, staged through LDS one 32-token slice at a time so that
+    // each store instruction writes two 512-byte row segments.
+    float* stage = reinterpret_cast<float*>(smem) + wave * (32 * kStageStride);
     const float nan = __builtin_nanf("");
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tl = wt * 128 + j * 32 + (lane & 31);
-      if (tl >= N_tail) continue;
+    for (int j = 0; j < kJ; ++j) {
+      const int tl = wt * kTW + j * 32 + (lane & 31);
+      const bool have = tl < N_tail;
       const int64_t tok = tok0 + tl;
-      const bool active = (args.mask == nullptr) || (args.mask[tok] != 0);
-      const int64_t t = args.targets[tok];
+      const bool active = have && ((args.mask == nullptr) || (args.mask[tok] != 0));
+      const int64_t t = active ? args.targets[tok] : -1;
       const bool tvalid = (t >= 0 && t < args.V);
       const float g = active ? args.grad[tok] : 0.0f;
       const float ng = -g;
       const float off = active ? args.lse[tok] * kLog2e : 0.0f;
-      float* outp = args.dl + tok * args.ldg + vwave;
+      float* srow = stage + (lane & 31) * kStageStride;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kI; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int m0 = i * 32 + 8 * q + 4 * half;  // relative to vwave
@@ -306,43 +345,79 @@ void linear_tiles(TileArgs args) {
             if (!active) d[e] = 0.0f;
             else if (!tvalid) d[e] = nan;
           }
-          const int mrel = wv * 128 + m0;  // relative to vocab0
+          *reinterpret_cast<float4*>(srow + m0) = make_float4(d[0], d[1], d[2], d[3]);
+        }
+      __syncthreads();
+#pragma unroll 4
+      for (int step = 0; step < 16; ++step) {
+        const int r = 2 * step + (lane >> 5);
+        const int c4 = lane & 31;
+        const int tr = wt * kTW + j * 32 + r;
+        if (tr < N_tail) {
+          const float4 v = *reinterpret_cast<const float4*>(stage + r * kStageStride + 4 * c4);
+          const int mrel = wv * 128 + 4 * c4;  // relative to vocab0
+          float* dst = args.dl + (tok0 + tr) * args.ldg + vocab0 + mrel;
           if (mrel + 4 <= V_tail) {
-            store16_stream(outp + m0, d[0], d[1], d[2], d[3]);
+            store16_stream(dst, v.x, v.y, v.z, v.w);
           } else {
+            const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (mrel + e < V_tail) outp[m0 + e] = d[e];
+              if (mrel + e < V_tail) dst[e] = vv[e];
           }
         }
+      }
+      __syncthreads();
     }
   }
 }
 
-// Per row: merge the chunk partials in ascending chunk order, then finish.
-__global__ __launch_bounds__(256) void lse_chunk_combine(const float2* __restrict__ part,
-                                                         int n_vtiles, const float* __restrict__ zt,
-                                                         const int64_t* __restrict__ targets,
-                                                         const uint8_t* __restrict__ mask,
-                                                         int64_t N, int V, float* __restrict__ logp,
-                                                         float* __restrict__ lse) {
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+// One wave per row: lane l merges the row's chunk partials l, l + 64,
+// l + 128, ... in ascending order, then the 64 lane states merge in the fixed
+// butterfly; the schedule depends on the number of chunks (that is, on V)
+// only.  Partials are row-major, so each step is one coalesced 512-byte load.
+constexpr int kCombineRows = 4;  // rows (waves) per workgroup
+
+__global__ __launch_bounds__(64 * kCombineRows) void lse_chunk_combine(
+    const float2* __restrict__ part, int n_vtiles, const float* __restrict__ zt,
+    const int64_t* __restrict__ targets, const uint8_t* __restrict__ mask, int64_t N, int V,
+    float* __restrict__ logp, float* __restrict__ lse) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kCombineRows + (threadIdx.x >> 6);
   if (row >= N) return;
   if (mask != nullptr && mask[row] == 0) {
-    logp[row] = 0.0f;
-    if (lse != nullptr) lse[row] = 0.0f;
+    if (lane == 0) {
+      logp[row] = 0.0f;
+      if (lse != nullptr) lse[row] = 0.0f;
+    }
     return;
   }
+  const float2* rp = part + row * n_vtiles;
   float M = neg_inf();
   float s = 0.0f;
-  for (int c = 0; c < n_vtiles; ++c) {
-    const float2 p = part[static_cast<int64_t>(c) * N + row];
+  int c = lane;
+  // four loads in flight per lane, merged in ascending chunk order
+  for (; c + 192 < n_vtiles; c += 256) {
+    const float2 p0 = rp[c];
+    const float2 p1 = rp[c + 64];
+    const float2 p2 = rp[c + 128];
+    const float2 p3 = rp[c + 192];
+    lse_merge(M, s, p0.x, p0.y);
+    lse_merge(M, s, p1.x, p1.y);
+    lse_merge(M, s, p2.x, p2.y);
+    lse_merge(M, s, p3.x, p3.y);
+  }
+  for (; c < n_vtiles; c += 64) {
+    const float2 p = rp[c];
     lse_merge(M, s, p.x, p.y);
   }
-  const float l = lse_finish(M, s);
-  const int64_t t = targets[row];
-  logp[row] = (t >= 0 && t < V) ? zt[row] - l : __builtin_nanf("");
-  if (lse != nullptr) lse[row] = l;
+  wave_lse_allreduce(M, s);
+  if (lane == 0) {
+    const float l = lse_finish(M, s);
+    const int64_t t = targets[row];
+    logp[row] = (t >= 0 && t < V) ? zt[row] - l : __builtin_nanf("");
+    if (lse != nullptr) lse[row] = l;
+  }
 }
 
 TileArgs make_args(const uint16_t* hidden, int64_t ldh, const uint16_t* weight, int64_t ldw,
@@ -386,7 +461,9 @@ hipError_t launch_linear_logp(const uint16_t* hidden, int64_t ldh, const uint16_
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lse_chunk_combine, dim3(static_cast<uint32_t>((N + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL(lse_chunk_combine,
+                     dim3(static_cast<uint32_t>((N + kCombineRows - 1) / kCombineRows)),
+                     dim3(64 * kCombineRows), 0,
                      stream, a.part, a.n_vtiles, a.zt, targets, mask, N, V, logp, lse);
   return hipGetLastError();
 }

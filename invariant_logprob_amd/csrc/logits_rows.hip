@@ -11,7 +11,7 @@
 // are no atomics (page "[WS1 Test] #154 dtype pin + ...", section
 // "Workstream 3 - #153", scope item 2).
 //
-// Backward (grid = rows x column blocks).  Elementwise:
+// Backward (grid = rows x column blocks of 8192).  Elementwise:
 //   d[i, j] = g_i * ([j == t_i] - exp(x_ij - lse_i)),
 // evaluated as fma(-g_i, p_ij, [j == t_i] g_i) with p_ij = 2^(x_ij log2 e -
 // lse_i log2 e).  No reduction, so each element depends on its row only.
@@ -149,6 +149,9 @@ __global__ __launch_bounds__(THREADS) void logp_fwd_rows(
   }
 }
 
+// Backward: thread handles groups of 4 columns (an 8-byte bf16 load, a
+// 16-byte fp32 store), so every load and store instruction of a wave covers
+// one contiguous span (512 B read, 1 KB written).
 template <int THREADS, int UNROLL>
 __global__ __launch_bounds__(THREADS) void logp_bwd_rows(
     const uint16_t* __restrict__ logits, int64_t ld, const int64_t* __restrict__ targets,
@@ -156,19 +159,18 @@ __global__ __launch_bounds__(THREADS) void logp_bwd_rows(
     const float* __restrict__ grad, int V, float* __restrict__ dl, int64_t ldg) {
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
-  const int nvec = (V + 7) >> 3;
-  const int kbase = blockIdx.y * (THREADS * UNROLL);
+  const int nq = (V + 3) >> 2;                  // 4-column groups
+  const int qbase = blockIdx.y * (THREADS * UNROLL);
   float* outp = dl + row * ldg;
   const bool active = (mask == nullptr) || (mask[row] != 0);
   if (!active) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      const int k = kbase + u * THREADS + tid;
-      if (k >= nvec) break;
-      const int j = 8 * k;
-      if (j + 8 <= V) {
+      const int q = qbase + u * THREADS + tid;
+      if (q >= nq) break;
+      const int j = 4 * q;
+      if (j + 4 <= V) {
         store16_stream(outp + j, 0.f, 0.f, 0.f, 0.f);
-        store16_stream(outp + j + 4, 0.f, 0.f, 0.f, 0.f);
       } else {
         for (int e = 0; j + e < V; ++e) outp[j + e] = 0.0f;
       }
@@ -181,36 +183,35 @@ __global__ __launch_bounds__(THREADS) void logp_bwd_rows(
   const float off = lse[row] * kLog2e;
   const float ng = -g;
   const float nan = __builtin_nanf("");
-  const uint4* vp = reinterpret_cast<const uint4*>(logits + row * ld);
-  uint4 w[UNROLL];
+  const uint2* vp = reinterpret_cast<const uint2*>(logits + row * ld);
+  uint2 w[UNROLL];
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u) {
-    const int k = kbase + u * THREADS + tid;
-    w[u] = make_uint4(kNegInfPair, kNegInfPair, kNegInfPair, kNegInfPair);
-    if (k < nvec) w[u] = load16_stream(vp + k);
+    const int q = qbase + u * THREADS + tid;
+    w[u] = make_uint2(kNegInfPair, kNegInfPair);
+    if (q < nq) w[u] = load8_stream(vp + q);
   }
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u) {
-    const int k = kbase + u * THREADS + tid;
-    if (k >= nvec) break;
-    const int j = 8 * k;
-    const Vec8 x = decode(w[u]);
-    float d[8];
+    const int q = qbase + u * THREADS + tid;
+    if (q >= nq) break;
+    const int j = 4 * q;
+    const float x[4] = {bf16_lo(w[u].x), bf16_hi(w[u].x), bf16_lo(w[u].y), bf16_hi(w[u].y)};
+    float d[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) d[e] = ng * fast_exp2(__builtin_fmaf(x.v[e], kLog2e, -off));
-    if (t >= j && t < j + 8) {
-      const int e = static_cast<int>(t - j);
+    for (int e = 0; e < 4; ++e) d[e] = ng * fast_exp2(__builtin_fmaf(x[e], kLog2e, -off));
+    if (t >= j && t < j + 4) {
+      const int et = static_cast<int>(t - j);
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (q == e) d[q] = __builtin_fmaf(ng, fast_exp2(__builtin_fmaf(x.v[q], kLog2e, -off)), g);
+      for (int e = 0; e < 4; ++e)
+        if (e == et) d[e] = __builtin_fmaf(ng, fast_exp2(__builtin_fmaf(x[e], kLog2e, -off)), g);
     }
     if (!tvalid) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) d[q] = nan;
+      for (int e = 0; e < 4; ++e) d[e] = nan;
     }
-    if (j + 8 <= V) {
+    if (j + 4 <= V) {
       store16_stream(outp + j, d[0], d[1], d[2], d[3]);
-      store16_stream(outp + j + 4, d[4], d[5], d[6], d[7]);
     } else {
       for (int e = 0; j + e < V; ++e) outp[j + e] = d[e];
     }
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(THREADS) void logp_bwd_rows(
 constexpr int kRowThreads = 256;
 constexpr int kRowUnroll = 8;
 constexpr int kBwdThreads = 256;
-constexpr int kBwdUnroll = 4;
+constexpr int kBwdUnroll = 8;
 
 int logits_schedule_threads() { return kRowThreads; }
 int logits_schedule_unroll() { return kRowUnroll; }
@@ -240,9 +241,9 @@ hipError_t launch_logp_fwd_rows(const uint16_t* logits, int64_t ld, const int64_
 hipError_t launch_logp_bwd_rows(const uint16_t* logits, int64_t ld, const int64_t* targets,
                                 const uint8_t* mask, const float* lse, const float* grad, int64_t N,
                                 int V, float* dl, int64_t ldg, hipStream_t stream) {
-  const int nvec = (V + 7) / 8;
+  const int nq = (V + 3) / 4;
   const int per_block = kBwdThreads * kBwdUnroll;
-  const int nblk = (nvec + per_block - 1) / per_block;
+  const int nblk = (nq + per_block - 1) / per_block;
   hipLaunchKernelGGL((logp_bwd_rows<kBwdThreads, kBwdUnroll>),
                      dim3(static_cast<uint32_t>(N), static_cast<uint32_t>(nblk)), dim3(kBwdThreads),
                      0, stream, logits, ld, targets, mask, lse, grad, V, dl, ldg);

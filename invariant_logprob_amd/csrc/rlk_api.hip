@@ -140,8 +140,8 @@ const char* rlk_status_string(int status) {
 
 const char* rlk_build_info(void) {
   return "rlk 0.1.0; arch=gfx950; rev=" RLK_GIT_REV
-         "; schedule=rows256x8/bwd256x4/tile" RLK_STR(256) "x" RLK_STR(256) "x" RLK_STR(64)
-         "/mfma32x32x16bf16/group8";
+         "; schedule=rows:256thr,8x16B/lane-step; bwd:256thr,8x8B; tile:" RLK_STR(256) "x" RLK_STR(
+             256) "x" RLK_STR(64) ",8waves,mfma32x32x16bf16,2stage,group8; combine:wave-per-row";
 }
 
 }  // extern "C"

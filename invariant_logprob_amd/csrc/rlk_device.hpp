@@ -27,12 +27,17 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // 16-byte streaming load / store (data touched once: non-temporal hint)
 __device__ __forceinline__ uint4 load16_stream(const void* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load8_stream(const void* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
 }
 __device__ __forceinline__ void store16_stream(void* p, float a, float b, float c, float d) {
   f32x4_t v = {a, b, c, d};
