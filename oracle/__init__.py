@@ -2,6 +2,10 @@
 from .logprob_oracle import (  # noqa: F401
     LN2,
     bf16_to_f64,
+    entropy,
+    entropy_from_f64,
+    log_softmax,
+    log_softmax_from_f64,
     linear_logits,
     linear_logp,
     linear_logp_backward,

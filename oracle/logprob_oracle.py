@@ -193,3 +193,62 @@ def linear_logp_backward(hidden_bits, weight_bits, targets, mask, lse, grad_logp
     logits z = h . W^T; float64 [N, V]."""
     z = linear_logits(hidden_bits, weight_bits)
     return logp_backward_from_f64(z, targets, mask, lse, grad_logp)
+
+
+# ---------------------------------------------------------------------------
+# Dense outputs from the same log-sum-exp: the full log-softmax row and the
+# per-row entropy.  The pages contrast dense and indexed selected-logprob
+# paths (page "[RFC] Batch-Invariant RL Kernel Suite for Train-Inference
+# Consistency", section "Scope"); the dense path computes every
+# log-probability of the row, x_j - lse.  The entropy is the textbook
+# H = -sum_j p_j log p_j with p_j = exp(x_j - lse), i.e. lse - sum_j p_j x_j,
+# where entries with p_j = 0 (x_j = -inf) contribute nothing.
+
+
+def log_softmax_from_f64(x, mask=None):
+    """Dense log-softmax rows x_j - lse (float64 [N, V]); inactive rows 0."""
+    x = np.asarray(x, dtype=np.float64)
+    n, v = x.shape
+    act = _active(mask, n)
+    out = np.zeros((n, v))
+    rows = np.nonzero(act)[0]
+    if rows.size:
+        lse = logsumexp_rows(x[rows])
+        with np.errstate(invalid="ignore"):
+            out[rows] = x[rows] - lse[:, None]
+    return out
+
+
+def log_softmax(logits_bits, mask=None):
+    return log_softmax_from_f64(bf16_to_f64(logits_bits), mask)
+
+
+def entropy_from_f64(x, mask=None):
+    """Per-row entropy -sum_j p_j log p_j (float64 [N]); inactive rows 0."""
+    x = np.asarray(x, dtype=np.float64)
+    n, v = x.shape
+    act = _active(mask, n)
+    ent = np.zeros(n)
+    rows = np.nonzero(act)[0]
+    if rows.size:
+        xs = x[rows]
+        lse = logsumexp_rows(xs)
+        with np.errstate(invalid="ignore", over="ignore"):
+            logp = xs - lse[:, None]
+            p = np.exp(logp)
+            terms = np.where(p > 0, p * logp, 0.0)
+        h = -np.sum(terms, axis=1)
+        h[~np.isfinite(lse)] = np.nan
+        ent[rows] = h
+    return ent
+
+
+def entropy(logits_bits, mask=None, block_rows=256):
+    bits = np.asarray(logits_bits, dtype=np.uint16)
+    n = bits.shape[0]
+    act = _active(mask, n)
+    out = np.zeros(n)
+    for r0 in range(0, n, block_rows):
+        r1 = min(n, r0 + block_rows)
+        out[r0:r1] = entropy_from_f64(bf16_to_f64(bits[r0:r1]), act[r0:r1])
+    return out

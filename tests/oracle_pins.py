@@ -362,3 +362,67 @@ ALL_PINS = [
     pin_backward_mask,
     pin_linear_backward_matches_brute_force,
 ]
+
+
+# ---------------------------------------------------------------------------
+# dense log-softmax and entropy pins
+
+
+def pin_entropy_brute_force(o):
+    rng = np.random.default_rng(41)
+    for v in range(1, 13):
+        vals = grid_values(rng, (4, v))
+        h = o.entropy(to_bf16_bits_exact(vals))
+        for i in range(4):
+            row = [float(a) for a in vals[i]]
+            tot = math.fsum(math.exp(a) for a in row)
+            ps = [math.exp(a) / tot for a in row]
+            ref = -math.fsum(p * math.log(p) for p in ps if p > 0)
+            assert abs(h[i] - ref) <= 1e-13, (v, i, h[i], ref)
+
+
+def pin_entropy_closed_forms(o):
+    for v in (1, 2, 1000, 151936):
+        h = o.entropy_from_f64(np.full((1, v), 3.25))
+        assert abs(h[0] - math.log(v)) <= 1e-12, (v, h)
+    # two entries: binary entropy of sigmoid(x0 - x1)
+    rng = np.random.default_rng(42)
+    x = rng.standard_normal((20, 2)) * 4
+    h = o.entropy_from_f64(x)
+    p = 1.0 / (1.0 + np.exp(x[:, 1] - x[:, 0]))
+    ref = -(p * np.log(p) + (1 - p) * np.log1p(-p))
+    assert np.max(np.abs(h - ref)) <= 1e-12
+    # -inf entries contribute nothing: [0, -inf, 0] has entropy ln 2
+    h2 = o.entropy_from_f64(np.array([[0.0, -np.inf, 0.0]]))
+    assert abs(h2[0] - math.log(2.0)) <= 1e-15
+    # masked rows are zero
+    h3 = o.entropy_from_f64(np.ones((2, 5)), np.array([0, 1], dtype=np.uint8))
+    assert h3[0] == 0.0 and abs(h3[1] - math.log(5)) <= 1e-15
+
+
+def pin_entropy_bounds(o):
+    rng = np.random.default_rng(43)
+    x = rng.standard_normal((50, 300)) * rng.uniform(0.1, 20, size=(50, 1))
+    h = o.entropy_from_f64(x)
+    assert np.all(h >= -1e-12) and np.all(h <= math.log(300) + 1e-12)
+    # sharper rows have lower entropy (scaling the logits up by 2)
+    h2 = o.entropy_from_f64(2 * x)
+    assert np.all(h2 <= h + 1e-12)
+
+
+def pin_log_softmax_rows(o):
+    rng = np.random.default_rng(44)
+    vals = grid_values(rng, (3, 40), -10, 10, 0.25)
+    ls = o.log_softmax(to_bf16_bits_exact(vals), np.array([1, 0, 1], dtype=np.uint8))
+    assert np.all(ls[1] == 0.0)
+    for i in (0, 2):
+        row = [float(a) for a in vals[i]]
+        lse = math.log(math.fsum(math.exp(a) for a in row))
+        assert np.max(np.abs(ls[i] - (vals[i] - lse))) <= 1e-13
+        assert abs(math.fsum(math.exp(a) for a in ls[i]) - 1.0) <= 1e-13
+    u = o.log_softmax_from_f64(np.full((1, 64), -7.0))
+    assert np.max(np.abs(u + math.log(64))) <= 1e-15
+
+
+ALL_PINS += [pin_entropy_brute_force, pin_entropy_closed_forms, pin_entropy_bounds,
+             pin_log_softmax_rows]

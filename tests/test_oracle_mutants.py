@@ -97,14 +97,34 @@ def make_mutant(name):
                 d[i] = gi * ((p - oh) if name == "bwd_sign" else (oh - p))
             return d
         o.logp_backward_from_f64 = b
+    elif name == "entropy_sign":
+        clean = fresh_oracle("clean_entropy")
+        o.entropy_from_f64 = lambda x, mask=None: -clean.entropy_from_f64(x, mask)
+        o.entropy = lambda b, mask=None, block_rows=256: -clean.entropy(b, mask)
+    elif name == "entropy_no_p":
+        def ent(x, mask=None):
+            x = np.asarray(x, dtype=np.float64)
+            n = x.shape[0]
+            act = np.ones(n, bool) if mask is None else np.asarray(mask).astype(bool)
+            out = np.zeros(n)
+            lse = o.logsumexp_rows(x)
+            with np.errstate(all="ignore"):
+                out[act] = -np.sum(x[act] - lse[act, None], axis=1) / x.shape[1]
+            return out
+        o.entropy_from_f64 = ent
+        o.entropy = lambda b, mask=None, block_rows=256: ent(o.bf16_to_f64(b), mask)
+    elif name == "log_softmax_no_lse":
+        o.log_softmax_from_f64 = lambda x, mask=None: np.asarray(x, dtype=np.float64) - np.max(x, axis=1, keepdims=True)
+        o.log_softmax = lambda b, mask=None: o.log_softmax_from_f64(o.bf16_to_f64(b), mask)
     else:
         raise AssertionError(name)
     return o
 
 
+
 MUTANTS = ["sign", "no_shift", "log2", "drop_max", "mean_not_sum", "gather_off_by_one",
            "decode_as_fp16", "weight_transposed", "mask_ignored", "bwd_sign", "bwd_no_g",
-           "bwd_no_onehot", "bwd_no_lse"]
+           "bwd_no_onehot", "bwd_no_lse", "entropy_sign", "entropy_no_p", "log_softmax_no_lse"]
 
 
 @pytest.mark.parametrize("name", MUTANTS)
