@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--legs", default="logits_fwd,logits_bwd,fused_fwd,fused_fb")
+    p.add_argument("--extra-legs", default="logits_entropy,log_softmax",
+                   help="rows beyond the hot path, timed after the steps (not part of a step)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="instead of the hot path, run a plain 1 GiB device copy 5 times "
                         "(reference for hardware traffic counters)")
@@ -211,6 +213,34 @@ def main():
                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": f["mfma_frac"],
                     "traffic": None}
 
+    # rows beyond the hot path, on the same logits workload, timed separately
+    extra = {}
+    ent3 = torch.empty(n3, dtype=torch.float32, device=dev)
+    xfns = {
+        "logits_entropy": (lambda: ilp.logp_entropy(c3.logits, c3.targets, c3.mask, logp=logp3,
+                                                    lse=lse3, entropy=ent3),
+                           act3 * v3 * 2 + n3 * (8 + 1 + 12)),
+    }
+    if d3 is not None:
+        xfns["log_softmax"] = (lambda: ilp.log_softmax(c3.logits, lse3, c3.mask, out=d3),
+                               act3 * v3 * 2 + n3 * v3 * 4 + n3 * 5)
+    for name in [x for x in args.extra_legs.split(",") if x in xfns]:
+        fn, nbytes = xfns[name]
+        for _ in range(max(1, args.warmup)):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        xms = e0.elapsed_time(e1) / args.steps
+        xgbs = nbytes / (xms * 1e-3) / 1e9
+        extra[name] = {"ms": xms, "algorithmic_bytes": nbytes, "GB_per_s": xgbs,
+                       "hbm_frac": xgbs / HBM_PEAK_GBS}
+
     cpu = None
     if not args.no_cpu_baseline and "logits_fwd" in legs:
         cpu = cpu_baseline(c3, torch)
@@ -238,6 +268,7 @@ def main():
             "parallelism": "none (1 GPU)",
         },
         "legs": out_legs,
+        "extra_legs": extra,
         "roofline": roofline,
         "fused_roofline": ({"kernel": "linear_tiles", "bound": "mfma",
                             "achieved": out_legs["fused_fwd"]["TFLOP_per_s"],

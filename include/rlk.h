@@ -88,6 +88,35 @@ int rlk_logp_selected(const void* logits, int64_t ld, const int64_t* targets,
                       float* lse, hipStream_t stream);
 
 /*
+ * Selected-token logprob and the row's entropy H_i = -sum_j p_ij log p_ij
+ * (p = softmax of the row), from one pass over the logits: the entropy's
+ * weighted sum sum_j p_ij x_ij rides in the same per-lane state as the
+ * log-sum-exp, so H_i = lse_i - sum_j p_ij x_ij with the same fixed reduction
+ * schedule (hence the same batch invariance).  A statistic of the dense
+ * path: page "[RFC] ...", section "Scope" contrasts dense and indexed
+ * selected-logprob paths.
+ *   Arguments as rlk_logp_selected; entropy: fp32 [N], required.  Inactive
+ *   rows get entropy +0.0.  logp and lse are computed by the same operations
+ *   in the same order as in rlk_logp_selected, so they are bit-identical to
+ *   its outputs.
+ */
+int rlk_logp_entropy(const void* logits, int64_t ld, const int64_t* targets,
+                     const uint8_t* mask, int64_t N, int64_t V, float* logp,
+                     float* lse, float* entropy, hipStream_t stream);
+
+/*
+ * Dense log-softmax rows: out[i, j] = x_ij - lse_i, fp32 [N, ld_out]
+ * (ld_out >= V, ld_out % 4 == 0, 16-B aligned; columns >= V not written),
+ * with lse the forward's output for these rows (every log-probability of the
+ * row: the dense path of page "[RFC] ...", section "Scope").  Inactive rows
+ * are written as +0.0 and their logits are not read.  Elementwise, so each
+ * element depends on its own row only.
+ */
+int rlk_log_softmax(const void* logits, int64_t ld, const uint8_t* mask,
+                    const float* lse, int64_t N, int64_t V, float* out,
+                    int64_t ld_out, hipStream_t stream);
+
+/*
  * Bytes of device workspace rlk_linear_logp needs for (N, V, H): one
  * (max, sum) fp32 pair per row and 256-wide vocabulary chunk, plus one fp32
  * target logit per row, rounded up to 256 bytes.

@@ -13,11 +13,14 @@ from ._binding import (  # noqa: F401
     linear_logp_backward,
     linear_logp_workspace_size,
     load_library,
+    log_softmax,
     logp_backward,
+    logp_entropy,
     logp_selected,
 )
 
 __all__ = [
     "RlkError", "build_info", "library_path", "linear_logp", "linear_logp_backward",
-    "linear_logp_workspace_size", "load_library", "logp_backward", "logp_selected",
+    "linear_logp_workspace_size", "load_library", "log_softmax", "logp_backward", "logp_entropy",
+    "logp_selected",
 ]

@@ -41,6 +41,10 @@ def load_library():
     vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
     lib.rlk_logp_selected.argtypes = [vp, i64, vp, vp, i64, i64, vp, vp, vp]
     lib.rlk_logp_selected.restype = ctypes.c_int
+    lib.rlk_logp_entropy.argtypes = [vp, i64, vp, vp, i64, i64, vp, vp, vp, vp]
+    lib.rlk_logp_entropy.restype = ctypes.c_int
+    lib.rlk_log_softmax.argtypes = [vp, i64, vp, vp, i64, i64, vp, i64, vp]
+    lib.rlk_log_softmax.restype = ctypes.c_int
     lib.rlk_linear_logp_workspace_size.argtypes = [i64, i64, i64]
     lib.rlk_linear_logp_workspace_size.restype = sz
     lib.rlk_linear_logp.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
@@ -145,6 +149,48 @@ def logp_selected(logits, targets, mask=None, *, logp=None, lse=None):
                                    _ptr(lse), _stream(dev))
     _raise(st, "rlk_logp_selected")
     return logp, lse
+
+
+def logp_entropy(logits, targets, mask=None, *, logp=None, lse=None, entropy=None):
+    """Selected-token logprob plus per-row entropy from bf16 logits [N, V],
+    one pass.  Returns (logp, lse, entropy), float32 [N]."""
+    lib = load_library()
+    ld = _matrix(logits, "logits", torch.bfloat16)
+    n, v = logits.shape
+    _rows(targets, "targets", n, torch.int64)
+    mask = _mask(mask, n)
+    dev = _same_device(logits, targets, mask)
+    logp = torch.empty(n, dtype=torch.float32, device=dev) if logp is None else logp
+    lse = torch.empty(n, dtype=torch.float32, device=dev) if lse is None else lse
+    entropy = torch.empty(n, dtype=torch.float32, device=dev) if entropy is None else entropy
+    for t, nm in ((logp, "logp"), (lse, "lse"), (entropy, "entropy")):
+        _rows(t, nm, n, torch.float32)
+    if n == 0:
+        return logp, lse, entropy
+    with torch.cuda.device(dev):
+        st = lib.rlk_logp_entropy(_ptr(logits), ld, _ptr(targets), _ptr(mask), n, v, _ptr(logp),
+                                  _ptr(lse), _ptr(entropy), _stream(dev))
+    _raise(st, "rlk_logp_entropy")
+    return logp, lse, entropy
+
+
+def log_softmax(logits, lse, mask=None, *, out=None):
+    """Dense log-softmax rows x - lse from bf16 logits [N, V] and the
+    forward's lse: float32 [N, V]; inactive rows are zero."""
+    lib = load_library()
+    ld = _matrix(logits, "logits", torch.bfloat16)
+    n, v = logits.shape
+    _rows(lse, "lse", n, torch.float32)
+    mask = _mask(mask, n)
+    dev = _same_device(logits, lse, mask)
+    out, ldo = _grad_out(out, n, v, dev)
+    if n == 0:
+        return out
+    with torch.cuda.device(dev):
+        st = lib.rlk_log_softmax(_ptr(logits), ld, _ptr(mask), _ptr(lse), n, v, _ptr(out), ldo,
+                                 _stream(dev))
+    _raise(st, "rlk_log_softmax")
+    return out
 
 
 def linear_logp_workspace_size(n, v, h):

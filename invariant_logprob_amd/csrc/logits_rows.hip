@@ -72,10 +72,42 @@ __device__ __forceinline__ void consume(float& M, float& s, const Vec8 (&x)[U]) 
   for (int u = 0; u < U; ++u) s = s + sum8_terms(x[u], Mu);
 }
 
-template <int THREADS, int UNROLL>
+// Entropy variant of consume: the same terms also weight the logits.  A -inf
+// logit is clamped to -FLT_MAX for the product, so its zero term adds 0
+// instead of 0 * -inf.
+__device__ __forceinline__ float sum8_weighted(const Vec8& a, float Mu, float& tsum) {
+#pragma clang fp contract(off)
+  float e[8], w[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    e[k] = lse_term(a.v[k], Mu);
+    w[k] = e[k] * fmaxf(a.v[k], -3.402823466e38f);
+  }
+  tsum = ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
+  return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+}
+
+template <int U>
+__device__ __forceinline__ void consume3(float& M, float& s, float& t, const Vec8 (&x)[U]) {
+#pragma clang fp contract(off)
+  float bm = max8(x[0]);
+#pragma unroll
+  for (int u = 1; u < U; ++u) bm = fmaxf(bm, max8(x[u]));
+  const float Mu = lse3_raise(M, s, t, bm);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float tw;
+    const float se = sum8_weighted(x[u], Mu, tw);
+    s = s + se;
+    t = t + tw;
+  }
+}
+
+template <int THREADS, int UNROLL, bool kEntropy>
 __global__ __launch_bounds__(THREADS) void logp_fwd_rows(
     const uint16_t* __restrict__ logits, int64_t ld, const int64_t* __restrict__ targets,
-    const uint8_t* __restrict__ mask, int V, float* __restrict__ logp, float* __restrict__ lse) {
+    const uint8_t* __restrict__ mask, int V, float* __restrict__ logp, float* __restrict__ lse,
+    float* __restrict__ ent) {
   constexpr int kWaves = THREADS / 64;
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -83,6 +115,7 @@ __global__ __launch_bounds__(THREADS) void logp_fwd_rows(
     if (tid == 0) {
       logp[row] = 0.0f;
       if (lse != nullptr) lse[row] = 0.0f;
+      if constexpr (kEntropy) ent[row] = 0.0f;
     }
     return;
   }
@@ -95,6 +128,7 @@ __global__ __launch_bounds__(THREADS) void logp_fwd_rows(
 
   float M = neg_inf();
   float s = 0.0f;
+  float tw = 0.0f;  // entropy variant only
   for (int base = 0; base < nmain; base += kStep) {
     uint4 w[UNROLL];
 #pragma unroll
@@ -102,7 +136,8 @@ __global__ __launch_bounds__(THREADS) void logp_fwd_rows(
     Vec8 x[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) x[u] = decode(w[u]);
-    consume<UNROLL>(M, s, x);
+    if constexpr (kEntropy) consume3<UNROLL>(M, s, tw, x);
+    else consume<UNROLL>(M, s, x);
   }
   if (nmain < nvec) {
     // guarded tail: same lane map (vector k -> thread k % THREADS)
@@ -119,24 +154,36 @@ __global__ __launch_bounds__(THREADS) void logp_fwd_rows(
           if (8 * k + e >= V) x[u].v[e] = neg_inf();
       }
     }
-    consume<UNROLL>(M, s, x);
+    if constexpr (kEntropy) consume3<UNROLL>(M, s, tw, x);
+    else consume<UNROLL>(M, s, x);
   }
 
-  wave_lse_allreduce(M, s);
+  if constexpr (kEntropy) wave_lse3_allreduce(M, s, tw);
+  else wave_lse_allreduce(M, s);
   __shared__ float sM[kWaves];
   __shared__ float sS[kWaves];
+  __shared__ float sT[kWaves];
   const int wave = tid >> 6;
   if ((tid & 63) == 0) {
     sM[wave] = M;
     sS[wave] = s;
+    if constexpr (kEntropy) sT[wave] = tw;
   }
   __syncthreads();
   if (tid == 0) {
     float Mt = sM[0];
     float st = sS[0];
+    float tt = kEntropy ? sT[0] : 0.0f;
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) lse_merge(Mt, st, sM[w], sS[w]);
+    for (int w = 1; w < kWaves; ++w) {
+      if constexpr (kEntropy) lse3_merge(Mt, st, tt, sM[w], sS[w], sT[w]);
+      else lse_merge(Mt, st, sM[w], sS[w]);
+    }
     const float l = lse_finish(Mt, st);
+    if constexpr (kEntropy) {
+#pragma clang fp contract(off)
+      ent[row] = l - tt / st;
+    }
     const int64_t t = targets[row];
     float lp;
     if (t >= 0 && t < V) {
@@ -218,6 +265,43 @@ __global__ __launch_bounds__(THREADS) void logp_bwd_rows(
   }
 }
 
+// Dense log-softmax rows out[i, j] = x_ij - lse_i, with the backward's
+// access pattern (8-byte loads, 16-byte stores, 8192 columns per block).
+template <int THREADS, int UNROLL>
+__global__ __launch_bounds__(THREADS) void log_softmax_rows(
+    const uint16_t* __restrict__ logits, int64_t ld, const uint8_t* __restrict__ mask,
+    const float* __restrict__ lse, int V, float* __restrict__ out, int64_t ldo) {
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nq = (V + 3) >> 2;
+  const int qbase = blockIdx.y * (THREADS * UNROLL);
+  float* outp = out + row * ldo;
+  const bool active = (mask == nullptr) || (mask[row] != 0);
+  const float l = active ? lse[row] : 0.0f;
+  const uint2* vp = reinterpret_cast<const uint2*>(logits + row * ld);
+  uint2 w[UNROLL];
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const int q = qbase + u * THREADS + tid;
+    w[u] = make_uint2(0u, 0u);
+    if (active && q < nq) w[u] = load8_stream(vp + q);
+  }
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const int q = qbase + u * THREADS + tid;
+    if (q >= nq) break;
+    const int j = 4 * q;
+    float d[4] = {bf16_lo(w[u].x) - l, bf16_hi(w[u].x) - l, bf16_lo(w[u].y) - l,
+                  bf16_hi(w[u].y) - l};
+    if (!active) d[0] = d[1] = d[2] = d[3] = 0.0f;
+    if (j + 4 <= V) {
+      store16_stream(outp + j, d[0], d[1], d[2], d[3]);
+    } else {
+      for (int e = 0; j + e < V; ++e) outp[j + e] = d[e];
+    }
+  }
+}
+
 }  // namespace
 
 // Compile-time schedule of the logits path.  These constants fix every row's
@@ -232,9 +316,16 @@ int logits_schedule_unroll() { return kRowUnroll; }
 
 hipError_t launch_logp_fwd_rows(const uint16_t* logits, int64_t ld, const int64_t* targets,
                                 const uint8_t* mask, int64_t N, int V, float* logp, float* lse,
-                                hipStream_t stream) {
-  hipLaunchKernelGGL((logp_fwd_rows<kRowThreads, kRowUnroll>), dim3(static_cast<uint32_t>(N)),
-                     dim3(kRowThreads), 0, stream, logits, ld, targets, mask, V, logp, lse);
+                                float* entropy, hipStream_t stream) {
+  if (entropy == nullptr) {
+    hipLaunchKernelGGL((logp_fwd_rows<kRowThreads, kRowUnroll, false>),
+                       dim3(static_cast<uint32_t>(N)), dim3(kRowThreads), 0, stream, logits, ld,
+                       targets, mask, V, logp, lse, nullptr);
+  } else {
+    hipLaunchKernelGGL((logp_fwd_rows<kRowThreads, kRowUnroll, true>),
+                       dim3(static_cast<uint32_t>(N)), dim3(kRowThreads), 0, stream, logits, ld,
+                       targets, mask, V, logp, lse, entropy);
+  }
   return hipGetLastError();
 }
 
@@ -247,6 +338,18 @@ hipError_t launch_logp_bwd_rows(const uint16_t* logits, int64_t ld, const int64_
   hipLaunchKernelGGL((logp_bwd_rows<kBwdThreads, kBwdUnroll>),
                      dim3(static_cast<uint32_t>(N), static_cast<uint32_t>(nblk)), dim3(kBwdThreads),
                      0, stream, logits, ld, targets, mask, lse, grad, V, dl, ldg);
+  return hipGetLastError();
+}
+
+hipError_t launch_log_softmax_rows(const uint16_t* logits, int64_t ld, const uint8_t* mask,
+                                   const float* lse, int64_t N, int V, float* out, int64_t ldo,
+                                   hipStream_t stream) {
+  const int nq = (V + 3) / 4;
+  const int per_block = kBwdThreads * kBwdUnroll;
+  const int nblk = (nq + per_block - 1) / per_block;
+  hipLaunchKernelGGL((log_softmax_rows<kBwdThreads, kBwdUnroll>),
+                     dim3(static_cast<uint32_t>(N), static_cast<uint32_t>(nblk)), dim3(kBwdThreads),
+                     0, stream, logits, ld, mask, lse, V, out, ldo);
   return hipGetLastError();
 }
 

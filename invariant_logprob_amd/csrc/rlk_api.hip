@@ -72,7 +72,37 @@ int rlk_logp_selected(const void* logits, int64_t ld, const int64_t* targets, co
   st = check_logits(logits, ld, N, V);
   if (st != RLK_OK) return st;
   return status_of(rlk::launch_logp_fwd_rows(static_cast<const uint16_t*>(logits), ld, targets,
-                                             mask, N, static_cast<int>(V), logp, lse, stream));
+                                             mask, N, static_cast<int>(V), logp, lse, nullptr,
+                                             stream));
+}
+
+int rlk_logp_entropy(const void* logits, int64_t ld, const int64_t* targets, const uint8_t* mask,
+                     int64_t N, int64_t V, float* logp, float* lse, float* entropy,
+                     hipStream_t stream) {
+  int st = check_sizes(N, V);
+  if (st != RLK_OK) return st;
+  if (N == 0) return RLK_OK;
+  if (targets == nullptr || logp == nullptr || entropy == nullptr) return RLK_ERR_INVALID_ARG;
+  st = check_logits(logits, ld, N, V);
+  if (st != RLK_OK) return st;
+  return status_of(rlk::launch_logp_fwd_rows(static_cast<const uint16_t*>(logits), ld, targets,
+                                             mask, N, static_cast<int>(V), logp, lse, entropy,
+                                             stream));
+}
+
+int rlk_log_softmax(const void* logits, int64_t ld, const uint8_t* mask, const float* lse,
+                    int64_t N, int64_t V, float* out, int64_t ld_out, hipStream_t stream) {
+  int st = check_sizes(N, V);
+  if (st != RLK_OK) return st;
+  if (N == 0) return RLK_OK;
+  if (lse == nullptr || out == nullptr) return RLK_ERR_INVALID_ARG;
+  if (ld_out < V) return RLK_ERR_INVALID_ARG;
+  if ((ld_out % 4) != 0 || !aligned16(out)) return RLK_ERR_UNSUPPORTED;
+  if (ld_out > (int64_t(1) << 62) / N) return RLK_ERR_UNSUPPORTED;
+  st = check_logits(logits, ld, N, V);
+  if (st != RLK_OK) return st;
+  return status_of(rlk::launch_log_softmax_rows(static_cast<const uint16_t*>(logits), ld, mask, lse,
+                                                N, static_cast<int>(V), out, ld_out, stream));
 }
 
 size_t rlk_linear_logp_workspace_size(int64_t N, int64_t V, int64_t H) {

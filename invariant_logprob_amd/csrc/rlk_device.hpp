@@ -19,6 +19,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// No implicit multiply-add contraction anywhere in the kernels: whether the
+// compiler fuses a product into a neighbouring add would otherwise depend on
+// how the surrounding code is laid out, and two kernels computing the same
+// quantity could round it differently.  Fused multiply-adds are written out
+// explicitly (__builtin_fmaf) where they are wanted.
+#pragma clang fp contract(off)
+
 namespace rlk {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -84,6 +91,45 @@ __device__ __forceinline__ float lse_raise(float& M, float& s, float block_max) 
 // Term of the sum for logit x at offset Mu.
 __device__ __forceinline__ float lse_term(float x, float Mu) {
   return fast_exp2(__builtin_fmaf(x, kLog2e, -Mu));
+}
+
+// Entropy-carrying state: t = sum_j 2^(x_j log2 e - M) x_j rides along with
+// s under the same offset, so sum_j p_j x_j = t / s.
+__device__ __forceinline__ void lse3_merge(float& M, float& s, float& t, float M2, float s2, float t2) {
+#pragma clang fp contract(off)
+  const float Mn = fmaxf(M, M2);
+  const float a = (M == Mn) ? 1.0f : fast_exp2(M - Mn);
+  const float b = (M2 == Mn) ? 1.0f : fast_exp2(M2 - Mn);
+  const float p = s * a;
+  const float q = s2 * b;
+  const float u = t * a;
+  const float w = t2 * b;
+  s = p + q;
+  t = u + w;
+  M = Mn;
+}
+
+__device__ __forceinline__ float lse3_raise(float& M, float& s, float& t, float block_max) {
+  const float Mb = block_max * kLog2e;
+  if (Mb > M) {
+    if (M != neg_inf()) {
+      const float f = fast_exp2(M - Mb);
+      s = s * f;
+      t = t * f;
+    }
+    M = Mb;
+  }
+  return lse_offset(M);
+}
+
+__device__ __forceinline__ void wave_lse3_allreduce(float& M, float& s, float& t) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const float M2 = __shfl_xor(M, d, 64);
+    const float s2 = __shfl_xor(s, d, 64);
+    const float t2 = __shfl_xor(t, d, 64);
+    lse3_merge(M, s, t, M2, s2, t2);
+  }
 }
 
 // Natural-log LSE of a finished state.

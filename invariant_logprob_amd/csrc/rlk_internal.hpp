@@ -21,7 +21,11 @@ int logits_schedule_unroll();
 
 hipError_t launch_logp_fwd_rows(const uint16_t* logits, int64_t ld, const int64_t* targets,
                                 const uint8_t* mask, int64_t N, int V, float* logp, float* lse,
-                                hipStream_t stream);
+                                float* entropy, hipStream_t stream);
+
+hipError_t launch_log_softmax_rows(const uint16_t* logits, int64_t ld, const uint8_t* mask,
+                                   const float* lse, int64_t N, int V, float* out, int64_t ldo,
+                                   hipStream_t stream);
 
 hipError_t launch_logp_bwd_rows(const uint16_t* logits, int64_t ld, const int64_t* targets,
                                 const uint8_t* mask, const float* lse, const float* grad, int64_t N,

@@ -111,3 +111,17 @@ def test_python_binding_rejects_cpu_tensors():
     t = torch.zeros(2, dtype=torch.int64)
     with pytest.raises(ValueError):
         ilp.logp_selected(x, t)
+
+
+def test_entropy_and_log_softmax_validation(lib):
+    f = lib.rlk_logp_entropy
+    assert f(A16, 1024, A16, NUL, 0, 1024, A16, NUL, A16, NUL) == OK
+    assert f(A16, 1024, A16, NUL, 4, 1024, A16, NUL, NUL, NUL) == INVALID   # no entropy
+    assert f(A16, 1024, NUL, NUL, 4, 1024, A16, NUL, A16, NUL) == INVALID   # no targets
+    assert f(A16, 1028, A16, NUL, 4, 1024, A16, NUL, A16, NUL) == UNSUPPORTED
+    g = lib.rlk_log_softmax
+    assert g(A16, 1024, NUL, A16, 0, 1024, A16, 1024, NUL) == OK
+    assert g(A16, 1024, NUL, NUL, 4, 1024, A16, 1024, NUL) == INVALID       # no lse
+    assert g(A16, 1024, NUL, A16, 4, 1024, A16, 1000, NUL) == INVALID       # ld_out < V
+    assert g(A16, 1024, NUL, A16, 4, 1024, A16, 1026, NUL) == UNSUPPORTED   # ld_out % 4
+    assert g(A2, 1024, NUL, A16, 4, 1024, A16, 1024, NUL) == UNSUPPORTED
