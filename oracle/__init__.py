@@ -14,4 +14,5 @@ from .logprob_oracle import (  # noqa: F401
     logp_selected,
     logsumexp_rows,
     selected_logp_from_f64,
+    token_losses,
 )

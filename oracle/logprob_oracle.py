@@ -252,3 +252,51 @@ def entropy(logits_bits, mask=None, block_rows=256):
         r1 = min(n, r0 + block_rows)
         out[r0:r1] = entropy_from_f64(bf16_to_f64(bits[r0:r1]), act[r0:r1])
     return out
+
+
+# ---------------------------------------------------------------------------
+# Per-token loss consumers of the selected logprob.  The pages place the loss
+# reductions (grpo_loss, ratio_kl) at the end of the operator chain and ask,
+# for bitwise invariance, that they be per-token outputs rather than batch
+# reductions (page "docs(ws1): batch-invariance contract RFC", section
+# "First-Divergence Localization", the review of the chain's last entry).
+# They do not write the formulas; the textbook GRPO/PPO terms are used:
+#
+#   ratio_i = exp(logp_i - logp_old_i)
+#   surr_i  = -min(ratio_i * A_i, clip(ratio_i, 1 - eps_lo, 1 + eps_hi) * A_i)
+#   kl_i    = exp(ref_i - logp_i) - (ref_i - logp_i) - 1        (k3 estimator)
+#   loss_i  = surr_i + beta * kl_i
+#   grad_i  = d loss_i / d logp_i
+#
+# The clipped branch has zero gradient where it is the one min() selects.
+
+
+def token_losses(logp, logp_old, adv, mask=None, logp_ref=None, eps_lo=0.2, eps_hi=0.2,
+                 beta=0.0):
+    """Per-token ratio, loss, kl and d loss / d logp (float64 [N] each);
+    masked tokens give 0 for every output."""
+    lp = np.asarray(logp, dtype=np.float64)
+    old = np.asarray(logp_old, dtype=np.float64)
+    a = np.asarray(adv, dtype=np.float64)
+    n = lp.shape[0]
+    act = _active(mask, n)
+    ratio = np.exp(lp - old)
+    clipped = np.clip(ratio, 1.0 - eps_lo, 1.0 + eps_hi)
+    unclipped_term = ratio * a
+    clipped_term = clipped * a
+    surr = -np.minimum(unclipped_term, clipped_term)
+    # the unclipped branch is the active one (ties included) unless the
+    # clipped term is strictly smaller
+    use_unclipped = unclipped_term <= clipped_term
+    grad = np.where(use_unclipped, -a * ratio, 0.0)
+    if logp_ref is not None:
+        d = np.asarray(logp_ref, dtype=np.float64) - lp
+        kl = np.exp(d) - d - 1.0
+        grad = grad + beta * (1.0 - np.exp(d))
+    else:
+        kl = np.zeros(n)
+    loss = surr + beta * kl
+    out = {"ratio": ratio, "loss": loss, "kl": kl, "grad": grad}
+    for k in out:
+        out[k] = np.where(act, out[k], 0.0)
+    return out

@@ -426,3 +426,69 @@ def pin_log_softmax_rows(o):
 
 ALL_PINS += [pin_entropy_brute_force, pin_entropy_closed_forms, pin_entropy_bounds,
              pin_log_softmax_rows]
+
+
+# ---------------------------------------------------------------------------
+# per-token loss pins
+
+
+def pin_token_losses_closed_forms(o):
+    # on-policy (logp == logp_old): ratio 1, surrogate -A, gradient -A
+    rng = np.random.default_rng(51)
+    lp = rng.standard_normal(64) * 3 - 5
+    a = rng.standard_normal(64)
+    out = o.token_losses(lp, lp, a)
+    assert np.all(out["ratio"] == 1.0)
+    assert np.max(np.abs(out["loss"] + a)) <= 1e-15
+    assert np.max(np.abs(out["grad"] + a)) <= 1e-15
+    # clipping: with A > 0 and ratio above 1 + eps the loss is -(1+eps) A
+    # and the gradient 0; with A < 0 and ratio below 1 - eps the loss is
+    # -(1-eps) A and the gradient 0
+    out2 = o.token_losses(np.array([0.5, -0.5]), np.array([0.0, 0.0]), np.array([2.0, -3.0]),
+                          eps_lo=0.1, eps_hi=0.3)
+    assert abs(out2["loss"][0] + 1.3 * 2.0) <= 1e-15 and out2["grad"][0] == 0.0
+    assert abs(out2["loss"][1] + 0.9 * -3.0) <= 1e-15 and out2["grad"][1] == 0.0
+    # A > 0 with ratio below 1 - eps is not clipped: loss -ratio A
+    out3 = o.token_losses(np.array([-1.0]), np.array([0.0]), np.array([1.5]), eps_lo=0.2)
+    r = math.exp(-1.0)
+    assert abs(out3["loss"][0] + r * 1.5) <= 1e-15 and abs(out3["grad"][0] + r * 1.5) <= 1e-15
+    # masked tokens are zero
+    out4 = o.token_losses(lp[:3], lp[:3] + 1, a[:3], np.array([1, 0, 1], dtype=np.uint8))
+    for k in ("ratio", "loss", "kl", "grad"):
+        assert out4[k][1] == 0.0
+
+
+def pin_token_kl(o):
+    rng = np.random.default_rng(52)
+    lp = rng.standard_normal(200) * 2 - 4
+    ref = lp + rng.standard_normal(200)
+    out = o.token_losses(lp, lp, np.zeros(200), logp_ref=ref, beta=0.5)
+    d = ref - lp
+    assert np.all(out["kl"] >= -1e-15)                       # e^d - d - 1 >= 0
+    assert np.max(np.abs(out["kl"] - (np.expm1(d) - d))) <= 1e-12
+    same = o.token_losses(lp, lp, np.zeros(200), logp_ref=lp, beta=0.5)
+    assert np.all(same["kl"] == 0.0) and np.all(same["grad"] == 0.0)
+    # small-difference expansion kl ~ d^2 / 2
+    tiny = o.token_losses(np.array([0.0]), np.array([0.0]), np.array([0.0]),
+                          logp_ref=np.array([1e-3]), beta=1.0)
+    assert abs(tiny["kl"][0] - 0.5e-6) <= 1e-9
+
+
+def pin_token_loss_gradient_fd(o):
+    rng = np.random.default_rng(53)
+    lp = rng.standard_normal(40) * 0.5 - 3
+    old = lp + rng.standard_normal(40) * 0.4
+    ref = lp + rng.standard_normal(40) * 0.3
+    a = rng.standard_normal(40)
+    kw = dict(logp_ref=ref, eps_lo=0.2, eps_hi=0.28, beta=0.04)
+    g = o.token_losses(lp, old, a, **kw)["grad"]
+    h = 1e-6
+    fp = o.token_losses(lp + h, old, a, **kw)["loss"]
+    fm = o.token_losses(lp - h, old, a, **kw)["loss"]
+    fd = (fp - fm) / (2 * h)
+    r = np.exp(lp - old)
+    near_edge = (np.abs(r - 0.8) < 1e-4) | (np.abs(r - 1.28) < 1e-4)
+    assert np.max(np.abs((g - fd)[~near_edge])) <= 1e-6
+
+
+ALL_PINS += [pin_token_losses_closed_forms, pin_token_kl, pin_token_loss_gradient_fd]

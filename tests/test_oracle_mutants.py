@@ -116,6 +116,25 @@ def make_mutant(name):
     elif name == "log_softmax_no_lse":
         o.log_softmax_from_f64 = lambda x, mask=None: np.asarray(x, dtype=np.float64) - np.max(x, axis=1, keepdims=True)
         o.log_softmax = lambda b, mask=None: o.log_softmax_from_f64(o.bf16_to_f64(b), mask)
+    elif name in ("loss_max_not_min", "loss_grad_ignores_clip", "kl_sign"):
+        clean = fresh_oracle("clean_loss")
+
+        def tl(logp, logp_old, adv, mask=None, logp_ref=None, eps_lo=0.2, eps_hi=0.2, beta=0.0):
+            out = clean.token_losses(logp, logp_old, adv, mask, logp_ref, eps_lo, eps_hi, beta)
+            lp = np.asarray(logp, dtype=np.float64)
+            r = np.exp(lp - np.asarray(logp_old, dtype=np.float64))
+            a = np.asarray(adv, dtype=np.float64)
+            if name == "loss_max_not_min":
+                out["loss"] = -np.maximum(r * a, np.clip(r, 1 - eps_lo, 1 + eps_hi) * a) + beta * out["kl"]
+            elif name == "loss_grad_ignores_clip":
+                g = -a * r
+                if logp_ref is not None:
+                    g = g + beta * (1 - np.exp(np.asarray(logp_ref) - lp))
+                out["grad"] = g
+            else:
+                out["kl"] = -out["kl"]
+            return out
+        o.token_losses = tl
     else:
         raise AssertionError(name)
     return o
@@ -124,7 +143,8 @@ def make_mutant(name):
 
 MUTANTS = ["sign", "no_shift", "log2", "drop_max", "mean_not_sum", "gather_off_by_one",
            "decode_as_fp16", "weight_transposed", "mask_ignored", "bwd_sign", "bwd_no_g",
-           "bwd_no_onehot", "bwd_no_lse", "entropy_sign", "entropy_no_p", "log_softmax_no_lse"]
+           "bwd_no_onehot", "bwd_no_lse", "entropy_sign", "entropy_no_p", "log_softmax_no_lse",
+           "loss_max_not_min", "loss_grad_ignores_clip", "kl_sign"]
 
 
 @pytest.mark.parametrize("name", MUTANTS)
