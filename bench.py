@@ -41,7 +41,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--legs", default="logits_fwd,logits_bwd,fused_fwd,fused_fb")
-    p.add_argument("--extra-legs", default="logits_entropy,log_softmax",
+    p.add_argument("--extra-legs", default="logits_entropy,log_softmax,token_losses",
                    help="rows beyond the hot path, timed after the steps (not part of a step)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="instead of the hot path, run a plain 1 GiB device copy 5 times "
@@ -221,6 +221,12 @@ def main():
                                                     lse=lse3, entropy=ent3),
                            act3 * v3 * 2 + n3 * (8 + 1 + 12)),
     }
+    g5 = torch.Generator(device=dev).manual_seed(5)
+    old3 = logp3 + 0.2 * torch.randn(n3, generator=g5, device=dev)
+    ref3 = logp3 + 0.2 * torch.randn(n3, generator=g5, device=dev)
+    adv3 = torch.randn(n3, generator=g5, device=dev)
+    xfns["token_losses"] = (lambda: ilp.token_losses(logp3, old3, adv3, c3.mask, ref3, 0.2, 0.28,
+                                                     0.04), n3 * (5 * 4 + 1 + 4 * 4))
     if d3 is not None:
         xfns["log_softmax"] = (lambda: ilp.log_softmax(c3.logits, lse3, c3.mask, out=d3),
                                act3 * v3 * 2 + n3 * v3 * 4 + n3 * 5)

@@ -164,6 +164,30 @@ int rlk_logp_backward(const void* logits, int64_t ld, const void* hidden,
                       int64_t V, float* grad_logits, int64_t ld_g,
                       hipStream_t stream);
 
+/*
+ * Per-token loss terms consuming the selected logprob (the chain's last
+ * entry, grpo_loss / ratio_kl, as per-token outputs so that each token's
+ * values cannot depend on the batch: page "docs(ws1): ...", section
+ * "First-Divergence Localization").  The pages give no formula; the textbook
+ * GRPO / PPO terms are used, per token i:
+ *   ratio = exp(logp - logp_old)
+ *   surr  = -min(ratio A, clip(ratio, 1 - eps_lo, 1 + eps_hi) A)
+ *   kl    = exp(ref - logp) - (ref - logp) - 1          (k3 estimator)
+ *   loss  = surr + beta kl
+ *   grad  = d loss / d logp   (the clipped branch, where min() picks it,
+ *                              contributes 0; feed it to rlk_logp_backward)
+ *   logp, logp_old, advantages: fp32 [N], required.  logp_ref: fp32 [N] or
+ *   NULL (then kl = 0 and beta is unused).  mask: uint8 [N] or NULL.
+ *   eps_lo in [0, 1), eps_hi >= 0, beta >= 0.
+ *   ratio, loss, kl, grad_logp: fp32 [N] outputs, each nullable (at least
+ *   one required).  Masked tokens get +0.0 in every output.
+ */
+int rlk_token_losses(const float* logp, const float* logp_old,
+                     const float* logp_ref, const float* advantages,
+                     const uint8_t* mask, int64_t N, float eps_lo, float eps_hi,
+                     float beta, float* ratio, float* loss, float* kl,
+                     float* grad_logp, hipStream_t stream);
+
 /* Static string naming a status code ("RLK_OK", ...); "unknown" otherwise. */
 const char* rlk_status_string(int status);
 

@@ -17,10 +17,11 @@ from ._binding import (  # noqa: F401
     logp_backward,
     logp_entropy,
     logp_selected,
+    token_losses,
 )
 
 __all__ = [
     "RlkError", "build_info", "library_path", "linear_logp", "linear_logp_backward",
     "linear_logp_workspace_size", "load_library", "log_softmax", "logp_backward", "logp_entropy",
-    "logp_selected",
+    "logp_selected", "token_losses",
 ]

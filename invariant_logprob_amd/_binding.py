@@ -45,6 +45,9 @@ def load_library():
     lib.rlk_logp_entropy.restype = ctypes.c_int
     lib.rlk_log_softmax.argtypes = [vp, i64, vp, vp, i64, i64, vp, i64, vp]
     lib.rlk_log_softmax.restype = ctypes.c_int
+    f32 = ctypes.c_float
+    lib.rlk_token_losses.argtypes = [vp, vp, vp, vp, vp, i64, f32, f32, f32, vp, vp, vp, vp, vp]
+    lib.rlk_token_losses.restype = ctypes.c_int
     lib.rlk_linear_logp_workspace_size.argtypes = [i64, i64, i64]
     lib.rlk_linear_logp_workspace_size.restype = sz
     lib.rlk_linear_logp.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
@@ -190,6 +193,30 @@ def log_softmax(logits, lse, mask=None, *, out=None):
         st = lib.rlk_log_softmax(_ptr(logits), ld, _ptr(mask), _ptr(lse), n, v, _ptr(out), ldo,
                                  _stream(dev))
     _raise(st, "rlk_log_softmax")
+    return out
+
+
+def token_losses(logp, logp_old, advantages, mask=None, logp_ref=None, eps_lo=0.2, eps_hi=0.2,
+                 beta=0.0):
+    """Per-token GRPO/PPO terms from fp32 [N] logprobs: returns a dict of
+    float32 [N] tensors ratio, loss, kl, grad (d loss / d logp)."""
+    lib = load_library()
+    n = logp.shape[0] if logp.dim() == 1 else -1
+    for t, nm in ((logp, "logp"), (logp_old, "logp_old"), (advantages, "advantages")):
+        _rows(t, nm, n, torch.float32)
+    if logp_ref is not None:
+        _rows(logp_ref, "logp_ref", n, torch.float32)
+    mask = _mask(mask, n)
+    dev = _same_device(logp, logp_old, advantages, logp_ref, mask)
+    out = {k: torch.empty(n, dtype=torch.float32, device=dev) for k in ("ratio", "loss", "kl", "grad")}
+    if n == 0:
+        return out
+    with torch.cuda.device(dev):
+        st = lib.rlk_token_losses(_ptr(logp), _ptr(logp_old), _ptr(logp_ref), _ptr(advantages),
+                                  _ptr(mask), n, float(eps_lo), float(eps_hi), float(beta),
+                                  _ptr(out["ratio"]), _ptr(out["loss"]), _ptr(out["kl"]),
+                                  _ptr(out["grad"]), _stream(dev))
+    _raise(st, "rlk_token_losses")
     return out
 
 

@@ -155,6 +155,23 @@ int rlk_logp_backward(const void* logits, int64_t ld, const void* hidden, int64_
       ld_g, stream));
 }
 
+int rlk_token_losses(const float* logp, const float* logp_old, const float* logp_ref,
+                     const float* advantages, const uint8_t* mask, int64_t N, float eps_lo,
+                     float eps_hi, float beta, float* ratio, float* loss, float* kl,
+                     float* grad_logp, hipStream_t stream) {
+  if (N < 0) return RLK_ERR_INVALID_ARG;
+  if (N > kMaxN) return RLK_ERR_UNSUPPORTED;
+  if (N == 0) return RLK_OK;
+  if (logp == nullptr || logp_old == nullptr || advantages == nullptr) return RLK_ERR_INVALID_ARG;
+  if (ratio == nullptr && loss == nullptr && kl == nullptr && grad_logp == nullptr)
+    return RLK_ERR_INVALID_ARG;
+  if (!(eps_lo >= 0.0f && eps_lo < 1.0f) || !(eps_hi >= 0.0f) || !(beta >= 0.0f))
+    return RLK_ERR_INVALID_ARG;
+  rlk::TokenLossArgs a{logp, logp_old, logp_ref, advantages, mask, N, eps_lo, eps_hi, beta,
+                       ratio, loss, kl, grad_logp};
+  return status_of(rlk::launch_token_losses(a, stream));
+}
+
 const char* rlk_status_string(int status) {
   switch (status) {
     case RLK_OK: return "RLK_OK";

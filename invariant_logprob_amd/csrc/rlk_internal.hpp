@@ -33,6 +33,24 @@ hipError_t launch_logp_bwd_rows(const uint16_t* logits, int64_t ld, const int64_
 
 size_t linear_workspace_bytes(int64_t N, int64_t V);
 
+struct TokenLossArgs {
+  const float* logp;
+  const float* logp_old;
+  const float* logp_ref;  // may be null: no KL term
+  const float* adv;
+  const uint8_t* mask;
+  int64_t N;
+  float eps_lo;
+  float eps_hi;
+  float beta;
+  float* ratio;
+  float* loss;
+  float* kl;
+  float* grad;
+};
+
+hipError_t launch_token_losses(const TokenLossArgs& a, hipStream_t stream);
+
 hipError_t launch_linear_logp(const uint16_t* hidden, int64_t ldh, const uint16_t* weight,
                               int64_t ldw, const int64_t* targets, const uint8_t* mask, int64_t N,
                               int V, int H, float* logp, float* lse, void* workspace,

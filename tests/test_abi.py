@@ -125,3 +125,18 @@ def test_entropy_and_log_softmax_validation(lib):
     assert g(A16, 1024, NUL, A16, 4, 1024, A16, 1000, NUL) == INVALID       # ld_out < V
     assert g(A16, 1024, NUL, A16, 4, 1024, A16, 1026, NUL) == UNSUPPORTED   # ld_out % 4
     assert g(A2, 1024, NUL, A16, 4, 1024, A16, 1024, NUL) == UNSUPPORTED
+
+
+def test_token_losses_validation(lib):
+    import ctypes as C
+    f = lib.rlk_token_losses
+    args = lambda **k: [k.get("lp", A16), k.get("old", A16), k.get("ref", NUL), k.get("adv", A16), NUL,
+                        k.get("n", 10), C.c_float(k.get("lo", 0.2)), C.c_float(k.get("hi", 0.2)),
+                        C.c_float(k.get("beta", 0.0)), k.get("r", A16), k.get("l", NUL), NUL, NUL, NUL]
+    assert f(*args(n=0)) == OK
+    assert f(*args(n=-1)) == INVALID
+    assert f(*args(lp=NUL)) == INVALID
+    assert f(*args(adv=NUL)) == INVALID
+    assert f(*args(r=NUL)) == INVALID          # no output at all
+    assert f(*args(lo=1.0)) == INVALID
+    assert f(*args(beta=-0.1)) == INVALID
