@@ -27,9 +27,9 @@
 // accumulation (same page, "Workstream 1 - #154" scope table).  The tile
 // schedule, the MFMA instruction and the K order never depend on N.
 //
-// The backward kernel reruns exactly the forward's main loop (same template,
-// same instruction sequence), so its z is bit-identical to the forward's, and
-// replaces the epilogue by d = g (onehot - 2^(z log2 e - lse log2 e)).
+// The backward kernel runs the same per-tile main loop (same copies, same
+// MFMA sequence), so its z is bit-identical to the forward's, and replaces
+// the epilogue by d = g (onehot - 2^(z log2 e - lse log2 e)).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -133,9 +133,10 @@ __device__ __forceinline__ void tile_coords(int w, int n_vtiles, int n_tblocks, 
   vt = g * kLinearVocabGroup + (rem - tb * gsize);
 }
 
-template <bool kBackward>
+// Backward tile kernel: the forward's per-tile main loop (same copies, same
+// MFMA sequence, hence bit-identical logits), then the dlogits epilogue.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void linear_tiles(TileArgs args) {
+void linear_tiles_bwd(TileArgs args) {
   __shared__ uint4 smem[kSmemVec];
 
   const int tid = threadIdx.x;
@@ -255,66 +256,7 @@ void linear_tiles(TileArgs args) {
   const int half = lane >> 5;
   const int vwave = vocab0 + wv * 128;  // first vocabulary entry of this wave
 
-  if constexpr (!kBackward) {
-    float2* red = reinterpret_cast<float2*>(smem);  // [2][kBT], after the loop's last barrier
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) {
-      const int tl = wt * kTW + j * 32 + (lane & 31);
-      const int64_t tok = tok0 + tl;
-      float mx = neg_inf();
-#pragma unroll
-      for (int i = 0; i < kI; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = wv * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-          if (m < V_tail) mx = fmaxf(mx, acc[i][j][e]);
-        }
-      float M = neg_inf();
-      float s = 0.0f;
-      const float Mu = lse_raise(M, s, mx);
-#pragma unroll
-      for (int i = 0; i < kI; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = wv * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-          if (m < V_tail) {
-#pragma clang fp contract(off)
-            s = s + lse_term(acc[i][j][e], Mu);
-          }
-        }
-      if (tl < N_tail) {
-        const int64_t t = args.targets[tok];
-        const int64_t d = t - vwave;
-        if (d >= 0 && d < 128) {
-          const int dd = static_cast<int>(d);
-          const int rem = dd & 31;
-          if (((rem >> 2) & 1) == half) {
-            const int it = dd >> 5;
-            const int et = ((rem >> 3) << 2) | (rem & 3);
-            float val = 0.0f;
-#pragma unroll
-            for (int i = 0; i < kI; ++i)
-#pragma unroll
-              for (int e = 0; e < 16; ++e)
-                if (i == it && e == et) val = acc[i][j][e];
-            args.zt[tok] = val;
-          }
-        }
-      }
-      const float M2 = __shfl_xor(M, 32, 64);
-      const float s2 = __shfl_xor(s, 32, 64);
-      lse_merge(M, s, M2, s2);
-      if (half == 0) red[wv * kBT + tl] = make_float2(M, s);
-    }
-    __syncthreads();
-    if (tid < kBT) {
-      const int tl = tid;
-      float2 p0 = red[tl];
-      const float2 p1 = red[kBT + tl];
-      lse_merge(p0.x, p0.y, p1.x, p1.y);
-      if (tl < N_tail) args.part[(tok0 + tl) * args.n_vtiles + vt] = p0;
-    }
-  } else {
+  {
     // dlogits tile, staged through LDS one 32-token slice at a time so that
     // each store instruction writes two 512-byte row segments.
     float* stage = reinterpret_cast<float*>(smem) + wave * (32 * kStageStride);
@@ -369,6 +311,214 @@ void linear_tiles(TileArgs args) {
       }
       __syncthreads();
     }
+  }
+}
+
+// Persistent forward: one workgroup per CU walks tiles blockIdx.x,
+// blockIdx.x + gridDim.x, ...; the LDS ring continues across tiles, so the
+// next tile's first K stage is in flight during this tile's last stage and
+// its epilogue.  The per-tile arithmetic (copies, MFMA sequence and K order)
+// is the same as linear_tiles_bwd's, so the backward recomputes the very same
+// logits.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void linear_tiles_fwd_persistent(TileArgs args) {
+  __shared__ uint4 smem[2 * kStageVec];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wv = wave / kWT;
+  const int wt = wave % kWT;
+  const int n_tiles = args.n_vtiles * args.n_tblocks;
+  const int H = args.H;
+  const int n_kt = (H + kBK - 1) / kBK;
+  int voff_w[kBlkPerWave], voff_h[kBlkPerWave], kcol[kBlkPerWave];
+#pragma unroll
+  for (int q = 0; q < kBlkPerWave; ++q) {
+    const int idx = (wave * kBlkPerWave + q) * 64 + lane;
+    const int r = idx / kRowChunks;
+    const int c = (idx % kRowChunks) ^ ((r >> 1) & 7);
+    kcol[q] = 8 * c;
+    voff_w[q] = (r * static_cast<int>(args.ldw) + 8 * c) * 2;
+    voff_h[q] = (r * static_cast<int>(args.ldh) + 8 * c) * 2;
+  }
+  struct Geo {
+    int vt;
+    int vocab0;
+    int64_t tok0;
+    int V_tail;
+    int N_tail;
+    __amdgpu_buffer_rsrc_t wres;
+    __amdgpu_buffer_rsrc_t hres;
+  };
+  auto geo = [&](int t) {
+    Geo g;
+    int vt, tb;
+    tile_coords(t, args.n_vtiles, args.n_tblocks, vt, tb);
+    g.vt = vt;
+    g.vocab0 = vt * kBV;
+    g.tok0 = static_cast<int64_t>(tb) * kBT;
+    g.N_tail = static_cast<int>(min<int64_t>(args.N - g.tok0, kBT));
+    g.V_tail = min(args.V - g.vocab0, kBV);
+    g.wres = uniform_rsrc(args.weight + static_cast<int64_t>(g.vocab0) * args.ldw, g.V_tail * args.ldw * 2);
+    g.hres = uniform_rsrc(args.hidden + g.tok0 * args.ldh, g.N_tail * args.ldh * 2);
+    return g;
+  };
+  auto issue = [&](const Geo& g, int kt, int st, int q0, int q1) {
+    const int k0 = kt * kBK;
+    const bool full = (k0 + kBK) <= H;
+    uint4* a = smem + st * kStageVec;
+    uint4* b = a + kAVec;
+#pragma unroll
+    for (int q = q0; q < q1; ++q) {
+      const int blk = wave * kBlkPerWave + q;
+      int vw = voff_w[q], vh = voff_h[q];
+      if (!full && (k0 + kcol[q]) >= H) {
+        vw = kOutOfRange;
+        vh = kOutOfRange;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(g.wres, to_lds(a + blk * 64), 16, vw, k0 * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(g.hres, to_lds(b + blk * 64), 16, vh, k0 * 2, 0, 0);
+    }
+  };
+  auto frag = [&](const uint4* a, const uint4* b, int kk, bf16x8_t (&fa)[kI], bf16x8_t (&fb)[kJ]) {
+    const int c = 2 * kk + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < kI; ++i) {
+      const int r = wv * 128 + i * 32 + (lane & 31);
+      fa[i] = __builtin_bit_cast(bf16x8_t, a[r * kRowChunks + swz(r, c)]);
+    }
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int r = wt * kTW + j * 32 + (lane & 31);
+      fb[j] = __builtin_bit_cast(bf16x8_t, b[r * kRowChunks + swz(r, c)]);
+    }
+  };
+
+  int tile = blockIdx.x;
+  if (tile >= n_tiles) return;
+  Geo cur = geo(tile);
+  int g0 = 0;  // ring position of the current tile's stage 0
+  issue(cur, 0, 0, 0, kBlkPerWave);
+  for (;;) {
+    const int next = tile + gridDim.x;
+    const bool has_next = next < n_tiles;
+    const Geo nxt = geo(has_next ? next : tile);
+    // targets of this lane's token columns, loaded before any of this tile's
+    // copies so that waiting for them never waits for a copy
+    int64_t tgt[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int tl = wt * kTW + j * 32 + (lane & 31);
+      tgt[j] = (tl < cur.N_tail) ? args.targets[cur.tok0 + tl] : -1;
+    }
+    f32x16_t acc[kI][kJ];
+#pragma unroll
+    for (int i = 0; i < kI; ++i)
+#pragma unroll
+      for (int j = 0; j < kJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    auto mma = [&](const bf16x8_t (&fa)[kI], const bf16x8_t (&fb)[kJ]) {
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int i = 0; i < kI; ++i)
+#pragma unroll
+        for (int j = 0; j < kJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
+    };
+    for (int kt = 0; kt < n_kt; ++kt) {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      const int buf = (g0 + kt) & 1;
+      const int nbuf = buf ^ 1;
+      const bool pf_same = (kt + 1) < n_kt;
+      const bool pf_next = !pf_same && has_next;
+      const uint4* a = smem + buf * kStageVec;
+      const uint4* b = a + kAVec;
+      bf16x8_t fa0[kI], fb0[kJ], fa1[kI], fb1[kJ];
+      frag(a, b, 0, fa0, fb0);
+#pragma unroll
+      for (int kk = 0; kk < kSub; kk += 2) {
+        frag(a, b, kk + 1, fa1, fb1);
+        if (kk == 0) {
+          if (pf_same) issue(cur, kt + 1, nbuf, 0, kBlkPerWave / 2);
+          else if (pf_next) issue(nxt, 0, nbuf, 0, kBlkPerWave / 2);
+        }
+        mma(fa0, fb0);
+        if (kk + 2 < kSub) frag(a, b, kk + 2, fa0, fb0);
+        if (kk == 0) {
+          if (pf_same) issue(cur, kt + 1, nbuf, kBlkPerWave / 2, kBlkPerWave);
+          else if (pf_next) issue(nxt, 0, nbuf, kBlkPerWave / 2, kBlkPerWave);
+        }
+        mma(fa1, fb1);
+      }
+    }
+    // everyone is done reading the last stage's buffer; the next tile's
+    // stage 0 may still be landing in the other one
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int free_buf = (g0 + n_kt - 1) & 1;
+    g0 += n_kt;
+
+    const int half = lane >> 5;
+    const int vwave = cur.vocab0 + wv * 128;
+    float2* red = reinterpret_cast<float2*>(smem + free_buf * kStageVec);
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int tl = wt * kTW + j * 32 + (lane & 31);
+      const int64_t tok = cur.tok0 + tl;
+      float mx = neg_inf();
+#pragma unroll
+      for (int i = 0; i < kI; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = wv * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+          if (m < cur.V_tail) mx = fmaxf(mx, acc[i][j][e]);
+        }
+      float M = neg_inf();
+      float s = 0.0f;
+      const float Mu = lse_raise(M, s, mx);
+#pragma unroll
+      for (int i = 0; i < kI; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = wv * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+          if (m < cur.V_tail) s = s + lse_term(acc[i][j][e], Mu);
+        }
+      if (tl < cur.N_tail) {
+        const int64_t t = tgt[j];
+        const int64_t d = t - vwave;
+        if (d >= 0 && d < 128) {
+          const int dd = static_cast<int>(d);
+          const int rem = dd & 31;
+          if (((rem >> 2) & 1) == half) {
+            const int it = dd >> 5;
+            const int et = ((rem >> 3) << 2) | (rem & 3);
+            float val = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kI; ++i)
+#pragma unroll
+              for (int e = 0; e < 16; ++e)
+                if (i == it && e == et) val = acc[i][j][e];
+            args.zt[tok] = val;
+          }
+        }
+      }
+      const float M2 = __shfl_xor(M, 32, 64);
+      const float s2 = __shfl_xor(s, 32, 64);
+      lse_merge(M, s, M2, s2);
+      if (half == 0) red[wv * kBT + tl] = make_float2(M, s);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (tid < kBT) {
+      const int tl = tid;
+      float2 p0 = red[tl];
+      const float2 p1 = red[kBT + tl];
+      lse_merge(p0.x, p0.y, p1.x, p1.y);
+      if (tl < cur.N_tail) args.part[(cur.tok0 + tl) * args.n_vtiles + cur.vt] = p0;
+    }
+    if (!has_next) break;
+    tile = next;
+    cur = nxt;
   }
 }
 
@@ -456,9 +606,20 @@ hipError_t launch_linear_logp(const uint16_t* hidden, int64_t ldh, const uint16_
   const size_t part_bytes = ((static_cast<size_t>(n_vtiles) * N * sizeof(float2) + 255) / 256) * 256;
   a.part = reinterpret_cast<float2*>(workspace);
   a.zt = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + part_bytes);
+  // persistent forward: one workgroup per compute unit (the count only sets
+  // which workgroup runs which tile, never how a tile is computed)
   const int64_t tiles = static_cast<int64_t>(a.n_vtiles) * a.n_tblocks;
-  hipLaunchKernelGGL((linear_tiles<false>), dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0,
-                     stream, a);
+  int device = 0;
+  int cus = 256;
+  if (hipGetDevice(&device) == hipSuccess) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess &&
+        n > 0)
+      cus = n;
+  }
+  const int64_t grid = tiles < cus ? tiles : cus;
+  hipLaunchKernelGGL(linear_tiles_fwd_persistent, dim3(static_cast<uint32_t>(grid)), dim3(kThreads),
+                     0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(lse_chunk_combine,
@@ -478,7 +639,7 @@ hipError_t launch_linear_dlogits(const uint16_t* hidden, int64_t ldh, const uint
   a.dl = dl;
   a.ldg = ldg;
   const int64_t tiles = static_cast<int64_t>(a.n_vtiles) * a.n_tblocks;
-  hipLaunchKernelGGL((linear_tiles<true>), dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0,
+  hipLaunchKernelGGL(linear_tiles_bwd, dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0,
                      stream, a);
   return hipGetLastError();
 }
