@@ -300,3 +300,37 @@ def token_losses(logp, logp_old, adv, mask=None, logp_ref=None, eps_lo=0.2, eps_
     for k in out:
         out[k] = np.where(act, out[k], 0.0)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Parameter gradients of the fused path.  With D the logits gradient above
+# (D_ij = g_i ([j == t_i] - p_ij), zero rows for inactive tokens) and
+# z = h . W^T, the chain rule gives
+#
+#   grad_hidden = D . W        [N, H]   (row i depends on row i of D only)
+#   grad_weight = D^T . h      [V, H]   (a sum over every active token)
+#
+# The pages ask for gradient batch invariance and say that parameter
+# gradients are compared only over the same complete set of samples (page
+# "[WS1 Test] #154 dtype pin + #152 KV path + #153 bwd invariance + #150
+# chain gate", section "Workstream 3 - #153", scope and logical-workload
+# identity); the formulas are the textbook derivatives of the definition.
+
+
+def linear_param_grads_from_f64(h, w, targets, mask, lse, grad_logp):
+    """(grad_hidden [N, H], grad_weight [V, H]) float64 for float64 h, W.
+
+    ``lse`` is the forward's log-sum-exp per row (an input of the backward,
+    as for the logits gradient)."""
+    h = np.asarray(h, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    if h.shape[1] != w.shape[1]:
+        raise ValueError("hidden and weight disagree on H")
+    d = logp_backward_from_f64(h @ w.T, targets, mask, lse, grad_logp)
+    return d @ w, d.T @ h
+
+
+def linear_param_grads(hidden_bits, weight_bits, targets, mask, lse, grad_logp):
+    """Parameter gradients from bf16 hidden [N, H] and weight [V, H] bits."""
+    return linear_param_grads_from_f64(bf16_to_f64(hidden_bits), bf16_to_f64(weight_bits),
+                                       targets, mask, lse, grad_logp)

@@ -492,3 +492,104 @@ def pin_token_loss_gradient_fd(o):
 
 
 ALL_PINS += [pin_token_losses_closed_forms, pin_token_kl, pin_token_loss_gradient_fd]
+
+
+# ---------------------------------------------------------------------------
+# parameter-gradient pins (grad_hidden = D . W, grad_weight = D^T . h)
+
+
+def _brute_loss(hf, wf, t, g, act):
+    """sum_i g_i logp_i over active rows, through math.fsum/math.exp only."""
+    n, hh = hf.shape
+    v = wf.shape[0]
+    total = []
+    for i in range(n):
+        if not act[i]:
+            continue
+        z = [math.fsum(float(hf[i, k]) * float(wf[j, k]) for k in range(hh)) for j in range(v)]
+        total.append(float(g[i]) * brute_logp(z, int(t[i])))
+    return math.fsum(total)
+
+
+def pin_param_grads_finite_differences(o):
+    rng = np.random.default_rng(41)
+    n, v, hh = 3, 5, 4          # all different, so a transposed operand cannot fit
+    hf = rng.standard_normal((n, hh))
+    wf = rng.standard_normal((v, hh)) * 0.7
+    t = np.array([1, 4, 0])
+    g = rng.standard_normal(n)
+    act = np.array([True, False, True])
+    mask = act.astype(np.uint8)
+    lse = np.zeros(n)
+    for i in range(n):
+        z = [math.fsum(float(hf[i, k]) * float(wf[j, k]) for k in range(hh)) for j in range(v)]
+        lse[i] = math.log(math.fsum(math.exp(a) for a in z))
+    gh, gw = o.linear_param_grads_from_f64(hf, wf, t, mask, lse, g)
+    assert gh.shape == (n, hh) and gw.shape == (v, hh), (gh.shape, gw.shape)
+    eps = 1e-6
+    for arr, grad in ((hf, gh), (wf, gw)):
+        for idx in np.ndindex(arr.shape):
+            keep = arr[idx]
+            arr[idx] = keep + eps
+            fp = _brute_loss(hf, wf, t, g, act)
+            arr[idx] = keep - eps
+            fm = _brute_loss(hf, wf, t, g, act)
+            arr[idx] = keep
+            fd = (fp - fm) / (2 * eps)
+            assert abs(grad[idx] - fd) <= 1e-7 * (1 + abs(fd)), (idx, grad[idx], fd)
+    assert np.all(gh[1] == 0.0), "inactive row must get a zero hidden gradient"
+
+
+def pin_param_grads_closed_forms(o):
+    rng = np.random.default_rng(42)
+    v, hh = 6, 5
+    w = rng.standard_normal((v, hh))
+    # zero hidden rows: z = 0, p = 1/V, so grad_h_i = g_i (W[t_i] - mean_j W_j)
+    # and grad_W = 0 (every product carries a factor h = 0)
+    t = np.array([2, 5])
+    g = np.array([1.25, -0.5])
+    h0 = np.zeros((2, hh))
+    lse0 = np.full(2, math.log(v))
+    gh, gw = o.linear_param_grads_from_f64(h0, w, t, None, lse0, g)
+    for i in range(2):
+        ref = g[i] * (w[t[i]] - w.mean(axis=0))
+        assert np.max(np.abs(gh[i] - ref)) <= 1e-14, (i, gh[i], ref)
+    assert np.max(np.abs(gw)) == 0.0
+    # identical weight rows: logits uniform again; grad_h = g_i (w - w) = 0 and
+    # grad_W_j = sum_i g_i ([j == t_i] - 1/V) h_i
+    same = np.repeat(rng.standard_normal((1, hh)), v, axis=0)
+    h = rng.standard_normal((3, hh))
+    t3 = np.array([0, 3, 3])
+    g3 = np.array([0.5, 2.0, -1.0])
+    lse3 = (h @ same[0]) + math.log(v)
+    gh3, gw3 = o.linear_param_grads_from_f64(h, same, t3, None, lse3, g3)
+    assert np.max(np.abs(gh3)) <= 1e-14, gh3
+    for j in range(v):
+        ref = sum(g3[i] * ((1.0 if j == t3[i] else 0.0) - 1.0 / v) * h[i] for i in range(3))
+        assert np.max(np.abs(gw3[j] - ref)) <= 1e-14, (j, gw3[j], ref)
+
+
+def pin_param_grads_invariants(o):
+    rng = np.random.default_rng(43)
+    n, v, hh = 7, 19, 12
+    hb = _rand_bf16(rng, (n, hh), 1.0)
+    wb = _rand_bf16(rng, (v, hh), 0.5)
+    t = rng.integers(0, v, size=n)
+    g = rng.standard_normal(n)
+    mask = np.array([1, 0, 1, 1, 0, 1, 1], dtype=np.uint8)
+    t[1] = -100           # inactive rows may hold invalid targets
+    _, lse = o.linear_logp(hb, wb, t, mask)
+    gh, gw = o.linear_param_grads(hb, wb, t, mask, lse, g)
+    # every row of D sums to zero, so the rows of grad_W sum to zero
+    assert np.max(np.abs(gw.sum(axis=0))) <= 1e-12
+    # inactive rows: zero hidden gradient, and no share in grad_W: the result
+    # equals the one over the compacted active rows alone
+    assert np.all(gh[mask == 0] == 0.0)
+    keep = np.nonzero(mask)[0]
+    gh_c, gw_c = o.linear_param_grads(hb[keep], wb, t[keep], None, lse[keep], g[keep])
+    assert np.max(np.abs(gh_c - gh[keep])) <= 1e-13
+    assert np.max(np.abs(gw_c - gw)) <= 1e-13
+
+
+ALL_PINS += [pin_param_grads_finite_differences, pin_param_grads_closed_forms,
+             pin_param_grads_invariants]

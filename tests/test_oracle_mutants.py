@@ -135,6 +135,33 @@ def make_mutant(name):
                 out["kl"] = -out["kl"]
             return out
         o.token_losses = tl
+    elif name in ("pgrad_sign", "pgrad_h_rows_reversed", "pgrad_w_no_onehot",
+                  "pgrad_w_mask_ignored"):
+        clean = fresh_oracle("clean_pgrad")
+
+        def pg(h, w, targets, mask, lse, g):
+            h = np.asarray(h, dtype=np.float64)
+            w = np.asarray(w, dtype=np.float64)
+            z = h @ w.T
+            d = clean.logp_backward_from_f64(z, targets, mask, lse, g)
+            if name == "pgrad_sign":
+                return -(d @ w), -(d.T @ h)
+            if name == "pgrad_h_rows_reversed":
+                return d @ w[::-1], d.T @ h
+            if name == "pgrad_w_no_onehot":
+                t = np.asarray(targets, dtype=np.int64)
+                act = np.ones(len(t), bool) if mask is None else np.asarray(mask).astype(bool)
+                d2 = d.copy()
+                for i in np.nonzero(act)[0]:
+                    d2[i, t[i]] -= np.asarray(g, dtype=np.float64)[i]
+                return d @ w, d2.T @ h
+            # mask ignored in grad_W: inactive rows with a valid target contribute
+            t = np.asarray(targets, dtype=np.int64)
+            tv = np.where((t < 0) | (t >= w.shape[0]), 0, t)
+            d_all = clean.logp_backward_from_f64(z, tv, None, lse, g)
+            return d @ w, d_all.T @ h
+        o.linear_param_grads_from_f64 = pg
+        o.linear_param_grads = lambda hb, wb, t, m, l, g: pg(o.bf16_to_f64(hb), o.bf16_to_f64(wb), t, m, l, g)
     else:
         raise AssertionError(name)
     return o
@@ -144,7 +171,8 @@ def make_mutant(name):
 MUTANTS = ["sign", "no_shift", "log2", "drop_max", "mean_not_sum", "gather_off_by_one",
            "decode_as_fp16", "weight_transposed", "mask_ignored", "bwd_sign", "bwd_no_g",
            "bwd_no_onehot", "bwd_no_lse", "entropy_sign", "entropy_no_p", "log_softmax_no_lse",
-           "loss_max_not_min", "loss_grad_ignores_clip", "kl_sign"]
+           "loss_max_not_min", "loss_grad_ignores_clip", "kl_sign", "pgrad_sign",
+           "pgrad_h_rows_reversed", "pgrad_w_no_onehot", "pgrad_w_mask_ignored"]
 
 
 @pytest.mark.parametrize("name", MUTANTS)
