@@ -41,7 +41,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--legs", default="logits_fwd,logits_bwd,fused_fwd,fused_fb")
-    p.add_argument("--extra-legs", default="logits_entropy,log_softmax,token_losses",
+    p.add_argument("--extra-legs",
+                   default="logits_entropy,log_softmax,token_losses,fused_param_grads",
                    help="rows beyond the hot path, timed after the steps (not part of a step)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="instead of the hot path, run a plain 1 GiB device copy 5 times "
@@ -230,6 +231,20 @@ def main():
     if d3 is not None:
         xfns["log_softmax"] = (lambda: ilp.log_softmax(c3.logits, lse3, c3.mask, out=d3),
                                act3 * v3 * 2 + n3 * v3 * 4 + n3 * 5)
+    xflops = {}
+    if c5 is not None and "fused_param_grads" in args.extra_legs.split(","):
+        # parameter gradients of the fused path on the fwd+bwd workload: the
+        # logits recompute plus the two products, 3 x 2 N V H flops
+        gh5 = torch.empty((n5, h5), dtype=torch.float32, device=dev)
+        gw5 = torch.empty((v5, h5), dtype=torch.float32, device=dev)
+        wsg5 = torch.empty(ilp.linear_logp_param_grads_workspace_size(n5, v5, h5),
+                           dtype=torch.uint8, device=dev)
+        xfns["fused_param_grads"] = (
+            lambda: ilp.linear_logp_param_grads(c5.hidden, c5.weight, c5.targets, lse5, c5.grad,
+                                                c5.mask, grad_hidden=gh5, grad_weight=gw5,
+                                                workspace=wsg5),
+            n5 * h5 * 2 + v5 * h5 * 2 + n5 * h5 * 4 + v5 * h5 * 4)
+        xflops["fused_param_grads"] = 3 * 2.0 * n5 * v5 * h5
     for name in [x for x in args.extra_legs.split(",") if x in xfns]:
         fn, nbytes = xfns[name]
         for _ in range(max(1, args.warmup)):
@@ -244,8 +259,13 @@ def main():
         torch.cuda.synchronize()
         xms = e0.elapsed_time(e1) / args.steps
         xgbs = nbytes / (xms * 1e-3) / 1e9
-        extra[name] = {"ms": xms, "algorithmic_bytes": nbytes, "GB_per_s": xgbs,
-                       "hbm_frac": xgbs / HBM_PEAK_GBS}
+        if name in xflops:
+            tf = xflops[name] / (xms * 1e-3) / 1e12
+            extra[name] = {"ms": xms, "flops": xflops[name], "TFLOP_per_s": tf,
+                           "mfma_frac": tf / BF16_PEAK_TFLOPS}
+        else:
+            extra[name] = {"ms": xms, "algorithmic_bytes": nbytes, "GB_per_s": xgbs,
+                           "hbm_frac": xgbs / HBM_PEAK_GBS}
 
     cpu = None
     if not args.no_cpu_baseline and "logits_fwd" in legs:

@@ -165,6 +165,52 @@ int rlk_logp_backward(const void* logits, int64_t ld, const void* hidden,
                       hipStream_t stream);
 
 /*
+ * Bytes of device workspace rlk_linear_logp_param_grads needs for (N, V, H):
+ * the transposed hidden [H, N8] (N8 = N rounded up to 8), one chunk of the
+ * transposed weight [H, C], and one chunk of the logits gradient in bf16 in
+ * both layouts [N, C] and [C, N8], with C = min(16384, V rounded up to 256),
+ * each rounded up to 256 bytes.
+ */
+size_t rlk_linear_logp_param_grads_workspace_size(int64_t N, int64_t V,
+                                                  int64_t H);
+
+/*
+ * Parameter gradients of the fused path: with D the gradient of
+ * sum_i g_i logp_i with respect to the logits z = W . h_i (rlk_logp_backward,
+ * fused mode),
+ *     grad_hidden = D . W   fp32 [N, ld_gh]      (nullable)
+ *     grad_weight = D^T . h fp32 [V, ld_gw]      (nullable; not both NULL)
+ * (page "[WS1 Test] ...", section "Workstream 3 - #153": gradients keep the
+ * invariance contract; parameter gradients are compared over the same
+ * complete sample set).  D is never held whole: the vocabulary is walked in
+ * fixed chunks of 16384 entries; per chunk the logits are recomputed with
+ * exactly the forward's tiles and K order, D is formed in fp32 as in
+ * rlk_logp_backward and rounded once to bf16 -- the MFMA operand type --
+ * and both products run on bf16 MFMA with fp32 accumulation.
+ *   grad_hidden: chunk partial products are added in ascending chunk order,
+ *     so each row depends on its own token only and is bit-identical for any
+ *     batch composition.  Inactive rows are +0.0.
+ *   grad_weight: a sum over all active tokens in ascending row order,
+ *     deterministic for a given batch (not batch-invariant by nature).
+ *     An active row with an invalid target makes it NaN.
+ *   hidden, weight, targets, mask, lse (the forward's), grad_logp, H: as in
+ *   rlk_logp_backward's fused mode.  ld_gh >= H and ld_gw >= H, both % 4 ==
+ *   0 with 16-B aligned bases.  N must stay below 2^22 - 16.
+ *   workspace: >= rlk_linear_logp_param_grads_workspace_size(N, V, H) bytes,
+ *   16-B aligned; contents on entry ignored, on return undefined.
+ *   N == 0: grad_weight (if given) is set to zero; nothing else is read.
+ */
+int rlk_linear_logp_param_grads(const void* hidden, int64_t ld_h,
+                                const void* weight, int64_t ld_w,
+                                const int64_t* targets, const uint8_t* mask,
+                                const float* lse, const float* grad_logp,
+                                int64_t N, int64_t V, int64_t H,
+                                float* grad_hidden, int64_t ld_gh,
+                                float* grad_weight, int64_t ld_gw,
+                                void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
  * Per-token loss terms consuming the selected logprob (the chain's last
  * entry, grpo_loss / ratio_kl, as per-token outputs so that each token's
  * values cannot depend on the batch: page "docs(ws1): ...", section

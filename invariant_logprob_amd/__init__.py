@@ -6,11 +6,15 @@ and streams).  The library is loaded on first use and a missing or unloadable
 library raises: there is no CPU fallback.
 """
 from ._binding import (  # noqa: F401
+    LinearLogprob,
     RlkError,
+    SelectedLogprob,
     build_info,
     library_path,
     linear_logp,
     linear_logp_backward,
+    linear_logp_param_grads,
+    linear_logp_param_grads_workspace_size,
     linear_logp_workspace_size,
     load_library,
     log_softmax,
@@ -21,7 +25,8 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "RlkError", "build_info", "library_path", "linear_logp", "linear_logp_backward",
+    "LinearLogprob", "RlkError", "SelectedLogprob", "build_info", "library_path", "linear_logp",
+    "linear_logp_backward", "linear_logp_param_grads", "linear_logp_param_grads_workspace_size",
     "linear_logp_workspace_size", "load_library", "log_softmax", "logp_backward", "logp_entropy",
     "logp_selected", "token_losses",
 ]

@@ -55,6 +55,11 @@ def load_library():
     lib.rlk_logp_backward.argtypes = [vp, i64, vp, i64, vp, i64, i64, vp, vp, vp, vp, i64, i64, vp,
                                       i64, vp]
     lib.rlk_logp_backward.restype = ctypes.c_int
+    lib.rlk_linear_logp_param_grads_workspace_size.argtypes = [i64, i64, i64]
+    lib.rlk_linear_logp_param_grads_workspace_size.restype = sz
+    lib.rlk_linear_logp_param_grads.argtypes = [vp, i64, vp, i64, vp, vp, vp, vp, i64, i64, i64, vp,
+                                                i64, vp, i64, vp, sz, vp]
+    lib.rlk_linear_logp_param_grads.restype = ctypes.c_int
     lib.rlk_status_string.argtypes = [ctypes.c_int]
     lib.rlk_status_string.restype = ctypes.c_char_p
     lib.rlk_build_info.argtypes = []
@@ -313,6 +318,59 @@ def linear_logp_backward(hidden, weight, targets, lse, grad_logp, mask=None, *, 
     return out
 
 
+def linear_logp_param_grads_workspace_size(n, v, h):
+    return int(load_library().rlk_linear_logp_param_grads_workspace_size(n, v, h))
+
+
+def _param_out(out, rows, cols, dev, name):
+    if out is None:
+        return torch.empty((rows, cols), dtype=torch.float32, device=dev), cols
+    ld = _matrix(out, name, torch.float32)
+    if tuple(out.shape) != (rows, cols):
+        raise ValueError(f"{name} must have shape ({rows}, {cols})")
+    return out, ld
+
+
+def linear_logp_param_grads(hidden, weight, targets, lse, grad_logp, mask=None, *,
+                            want_hidden=True, want_weight=True, grad_hidden=None,
+                            grad_weight=None, workspace=None):
+    """Gradients of sum_i g_i logp_i with respect to hidden [N, H] and weight
+    [V, H] of the fused path: returns (grad_hidden, grad_weight), float32,
+    each None when not requested."""
+    lib = load_library()
+    if not (want_hidden or want_weight):
+        raise ValueError("request at least one of grad_hidden / grad_weight")
+    ldh = _matrix(hidden, "hidden", torch.bfloat16)
+    ldw = _matrix(weight, "weight", torch.bfloat16)
+    n, h = hidden.shape
+    v, h2 = weight.shape
+    if h != h2:
+        raise ValueError(f"hidden has H={h} but weight has H={h2}")
+    _rows(targets, "targets", n, torch.int64)
+    _rows(lse, "lse", n, torch.float32)
+    _rows(grad_logp, "grad_logp", n, torch.float32)
+    mask = _mask(mask, n)
+    dev = _same_device(hidden, weight, targets, lse, grad_logp, mask)
+    gh = gw = None
+    ld_gh = ld_gw = 0
+    if want_hidden:
+        gh, ld_gh = _param_out(grad_hidden, n, h, dev, "grad_hidden")
+    if want_weight:
+        gw, ld_gw = _param_out(grad_weight, v, h, dev, "grad_weight")
+    need = linear_logp_param_grads_workspace_size(n, v, h)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace too small: need {need} bytes")
+    with torch.cuda.device(dev):
+        st = lib.rlk_linear_logp_param_grads(
+            _ptr(hidden), ldh, _ptr(weight), ldw, _ptr(targets), _ptr(mask), _ptr(lse),
+            _ptr(grad_logp), n, v, h, _ptr(gh), ld_gh, _ptr(gw), ld_gw, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(dev))
+    _raise(st, "rlk_linear_logp_param_grads")
+    return gh, gw
+
+
 class SelectedLogprob(torch.autograd.Function):
     """Autograd wrapper: forward through rlk_logp_selected, backward through
     rlk_logp_backward with the saved lse."""
@@ -330,3 +388,27 @@ class SelectedLogprob(torch.autograd.Function):
         g = grad.contiguous().to(torch.float32)
         d = logp_backward(logits, targets, lse, g, mask if ctx.has_mask else None)
         return d, None, None
+
+
+class LinearLogprob(torch.autograd.Function):
+    """Autograd wrapper of the fused path: forward through rlk_linear_logp,
+    backward through rlk_linear_logp_param_grads with the saved lse.  The
+    gradients are float32; autograd casts them to the inputs' dtype."""
+
+    @staticmethod
+    def forward(ctx, hidden, weight, targets, mask=None):
+        logp, lse = linear_logp(hidden, weight, targets, mask)
+        ctx.save_for_backward(hidden, weight, targets, lse,
+                              mask if mask is not None else torch.empty(0))
+        ctx.has_mask = mask is not None
+        return logp
+
+    @staticmethod
+    def backward(ctx, grad):
+        hidden, weight, targets, lse, mask = ctx.saved_tensors
+        g = grad.contiguous().to(torch.float32)
+        gh, gw = linear_logp_param_grads(hidden, weight, targets, lse, g,
+                                         mask if ctx.has_mask else None,
+                                         want_hidden=ctx.needs_input_grad[0],
+                                         want_weight=ctx.needs_input_grad[1])
+        return gh, gw, None, None

@@ -1,0 +1,515 @@
+// Parameter gradients of the fused lm_head + selected logprob (gfx950):
+//
+//   grad_hidden = D . W      [N, H]     grad_weight = D^T . h      [V, H]
+//
+// with D the gradient with respect to the logits z = h . W^T,
+// D_ij = g_i ([j == t_i] - exp(z_ij - lse_i)) (zero rows for inactive
+// tokens).  These are the textbook chain-rule products; the pages ask that
+// gradients keep the batch-invariance contract and that parameter gradients
+// be compared over the same complete set of samples (page "[WS1 Test] #154
+// dtype pin + #152 KV path + #153 bwd invariance + #150 chain gate", section
+// "Workstream 3 - #153").
+//
+// D is never materialised whole.  The vocabulary is walked in fixed chunks
+// of kGradChunk entries (a constant: the chunking depends on V only).  Per
+// chunk c, in ascending c on the caller's stream:
+//   1. grad_dl_tiles recomputes the chunk's logits with the forward's tile
+//      main loop (bit-identical z), forms D in fp32 exactly as the logits
+//      backward does, rounds it once to bf16 (the MFMA operand type) and
+//      writes it in two layouts: D_c [N, chunk] and D_c^T [chunk, N'].
+//   2. transpose_bf16 writes W_c^T [H, chunk] (the contraction over the
+//      vocabulary needs W with the vocabulary contiguous).
+//   3. grad_gemm_tiles runs both products of the chunk in one launch:
+//      grad_hidden (+)= D_c . W_c   (K = the chunk's vocabulary, ascending;
+//                                    chunk 0 writes, later chunks add)
+//      grad_weight[c] = D_c^T . h   (K = tokens, ascending)
+// h^T [H, N'] is written once per call.  N' = N rounded up to 8; padding
+// columns hold zeros.
+//
+// Invariance.  A row of grad_hidden depends on its own row of D and on W
+// only, through a K order fixed by V: bit-identical for any batch.  A row of
+// grad_weight sums over every token of the batch in ascending row order: it
+// is deterministic run to run, but a different batch composition is a
+// different sum (the pages compare parameter gradients only over the same
+// complete sample set).  No atomics anywhere.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rlk_device.hpp"
+#include "rlk_internal.hpp"
+#include "tile_core.hpp"
+
+namespace rlk {
+
+namespace {
+
+using namespace tile;
+
+// LDS staging of a 256 x 256 bf16 tile: rows of 256 entries + 8 pad.
+constexpr int kDlStride = kBP + 8;  // bf16 elements per staged row
+constexpr int kDlStageVec = kBQ * kDlStride * 2 / 16;
+constexpr int kDlSmemVec = (2 * kStageVec > kDlStageVec) ? 2 * kStageVec : kDlStageVec;
+static_assert(kDlSmemVec * 16 <= 160 * 1024, "LDS budget of one CU");
+static_assert((kDlStride * 2) % 16 == 0, "staged rows must stay 16-byte aligned");
+
+// fp32 output staging of the GEMM epilogue: per wave 32 rows of 128 + 4.
+constexpr int kOutStride = 132;
+constexpr int kOutStageVec = kWaves * 32 * kOutStride / 4;
+constexpr int kGemmSmemVec = (2 * kStageVec > kOutStageVec) ? 2 * kStageVec : kOutStageVec;
+static_assert(kGemmSmemVec * 16 <= 160 * 1024, "LDS budget of one CU");
+
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x)));
+}
+
+struct DlArgs {
+  const uint16_t* hidden;
+  int64_t ldh;
+  const uint16_t* weight;
+  int64_t ldw;
+  const int64_t* targets;
+  const uint8_t* mask;
+  const float* lse;
+  const float* grad;
+  int64_t N;
+  int V;
+  int H;
+  int vt0;        // first vocabulary tile of the chunk
+  int n_vt;       // vocabulary tiles in the chunk
+  int n_tblocks;  // 256-token blocks
+  uint16_t* d;    // [N][ldd] bf16, chunk-local columns, or null
+  int64_t ldd;
+  uint16_t* dT;   // [n_vt * 256][ldt] bf16, chunk-local rows, or null
+  int64_t ldt;    // N rounded up to 8
+};
+
+// D for one 256-vocabulary x 256-token tile of the chunk.  The main loop is
+// the forward's (same operands, same K order), so z is bit-identical to the
+// logits the forward reduced; the fp32 D formula is the logits backward's.
+// Entries past V, rows past N and inactive rows are written as zero; an
+// active row with an invalid target gets NaN.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void grad_dl_tiles(DlArgs a) {
+  __shared__ uint4 smem[kDlSmemVec];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wv = wave / kWQ;
+  const int wt = wave % kWQ;
+  int vtl, tb;
+  grouped_coords(blockIdx.x, a.n_vt, a.n_tblocks, kLinearVocabGroup, vtl, tb);
+  const int vocab0 = (a.vt0 + vtl) * kBP;
+  const int64_t tok0 = static_cast<int64_t>(tb) * kBQ;
+  const int N_tail = static_cast<int>(min<int64_t>(a.N - tok0, kBQ));
+  const int V_tail = min(a.V - vocab0, kBP);
+
+  const __amdgpu_buffer_rsrc_t wres =
+      uniform_rsrc(a.weight + static_cast<int64_t>(vocab0) * a.ldw, V_tail * a.ldw * 2);
+  const __amdgpu_buffer_rsrc_t hres = uniform_rsrc(a.hidden + tok0 * a.ldh, N_tail * a.ldh * 2);
+  const Loader ld = make_loader(wave, lane, a.ldw, a.ldh);
+  f32x16_t acc[kI][kJ];
+  mainloop(smem, ld, wave, lane, wv, wt, wres, hres, a.H, acc);
+
+  // Per token column (lane & 31) of MFMA block j: what D needs of the row.
+  const int half = lane >> 5;
+  // rel[j]: the target's offset from this lane's first vocabulary row
+  // (128 wv + 4 (lane >> 5) of the tile), or -1 when outside this wave's rows
+  bool active[kJ], tvalid[kJ];
+  int rel[kJ];
+  float ng[kJ], gg[kJ], off[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int tl = wt * kQW + j * 32 + (lane & 31);
+    const int64_t tok = tok0 + tl;
+    active[j] = (tl < N_tail) && ((a.mask == nullptr) || (a.mask[tok] != 0));
+    const int64_t t = active[j] ? a.targets[tok] : -1;
+    tvalid[j] = (t >= 0 && t < a.V);
+    const int64_t r = t - (vocab0 + wv * 128 + 4 * half);
+    rel[j] = (r >= 0 && r < 128) ? static_cast<int>(r) : -1;
+    gg[j] = active[j] ? a.grad[tok] : 0.0f;
+    ng[j] = -gg[j];
+    off[j] = active[j] ? a.lse[tok] * kLog2e : 0.0f;
+  }
+  // bf16 D of vocabulary rows m0 .. m0 + 3 (m0 = 128 wv + 32 i + 8 q +
+  // 4 (lane >> 5)) of token column j, two entries per word.  Evaluated once
+  // per staging layout rather than held: the accumulators stay the only
+  // large live state.
+  const float nan = __builtin_nanf("");
+  auto dpair = [&](int j, int i, int q) {
+    const int m0 = wv * 128 + i * 32 + 8 * q + 4 * half;
+    uint32_t b[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p = fast_exp2(__builtin_fmaf(acc[i][j][4 * q + e], kLog2e, -off[j]));
+      const float add = (i * 32 + 8 * q + e == rel[j]) ? gg[j] : 0.0f;
+      float d = __builtin_fmaf(ng[j], p, add);
+      if (!active[j] || m0 + e >= V_tail) d = 0.0f;
+      else if (!tvalid[j]) d = nan;
+      b[e] = bf16_bits(d);
+    }
+    return make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+  };
+
+  uint16_t* S = reinterpret_cast<uint16_t*>(smem);
+  // 16-byte pieces of a staged 256 x 256 tile: 32 per row, 16 per thread
+  constexpr int kPieces = kBQ * (kBP / 8) / kThreads;
+
+  if (a.d != nullptr) {
+    // S[token][vocab], then whole 512-byte token rows of D_c
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int tl = wt * kQW + j * 32 + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < kI; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m0 = wv * 128 + i * 32 + 8 * q + 4 * half;
+          *reinterpret_cast<uint2*>(S + tl * kDlStride + m0) = dpair(j, i, q);
+        }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int it = 0; it < kPieces; ++it) {
+      const int idx = it * kThreads + tid;
+      const int r = idx >> 5;
+      const int c = idx & 31;
+      if (r < N_tail) {
+        const uint4 v = *reinterpret_cast<const uint4*>(S + r * kDlStride + 8 * c);
+        *reinterpret_cast<uint4*>(a.d + (tok0 + r) * a.ldd + vtl * kBP + 8 * c) = v;
+      }
+    }
+    __syncthreads();
+  }
+  if (a.dT != nullptr) {
+    // S[vocab][token], then 512-byte vocabulary rows of D_c^T (tokens past N
+    // up to the padded width are zeros)
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int tl = wt * kQW + j * 32 + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < kI; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m0 = wv * 128 + i * 32 + 8 * q + 4 * half;
+          const uint2 v = dpair(j, i, q);
+          S[(m0 + 0) * kDlStride + tl] = static_cast<uint16_t>(v.x);
+          S[(m0 + 1) * kDlStride + tl] = static_cast<uint16_t>(v.x >> 16);
+          S[(m0 + 2) * kDlStride + tl] = static_cast<uint16_t>(v.y);
+          S[(m0 + 3) * kDlStride + tl] = static_cast<uint16_t>(v.y >> 16);
+        }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int it = 0; it < kPieces; ++it) {
+      const int idx = it * kThreads + tid;
+      const int m = idx >> 5;
+      const int c = idx & 31;
+      if (tok0 + 8 * c < a.ldt) {
+        const uint4 v = *reinterpret_cast<const uint4*>(S + m * kDlStride + 8 * c);
+        *reinterpret_cast<uint4*>(a.dT + static_cast<int64_t>(vtl * kBP + m) * a.ldt + tok0 + 8 * c) = v;
+      }
+    }
+  }
+}
+
+// dst[c][r] = src[r][c] for r < rows, c < cols, and dst[c][r] = 0 for
+// rows <= r < rows_pad.  64 x 64 blocks staged through LDS; cols % 8 == 0,
+// rows_pad % 8 == 0, 16-byte aligned rows on both sides.
+constexpr int kTrTile = 64;
+constexpr int kTrStride = kTrTile + 8;  // bf16 per staged row (16-byte aligned)
+
+__global__ __launch_bounds__(256) void transpose_bf16(const uint16_t* __restrict__ src, int64_t lds,
+                                                      int rows, int cols, uint16_t* __restrict__ dst,
+                                                      int64_t ldd, int rows_pad) {
+  __shared__ uint16_t T[kTrTile * kTrStride];
+  const int r0 = blockIdx.x * kTrTile;
+  const int c0 = blockIdx.y * kTrTile;
+  const int tid = threadIdx.x;
+  // 64 rows x 8 pieces of 8 columns; thread -> (row, piece), two each
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int idx = it * 256 + tid;
+    const int r = idx >> 3;
+    const int p = idx & 7;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r0 + r < rows && c0 + 8 * p < cols)
+      v = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(r0 + r) * lds + c0 + 8 * p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      T[(8 * p + 2 * k) * kTrStride + r] = static_cast<uint16_t>(w[k]);
+      T[(8 * p + 2 * k + 1) * kTrStride + r] = static_cast<uint16_t>(w[k] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int idx = it * 256 + tid;
+    const int c = idx >> 3;
+    const int p = idx & 7;
+    if (c0 + c < cols && r0 + 8 * p < rows_pad) {
+      const uint4 v = *reinterpret_cast<const uint4*>(T + c * kTrStride + 8 * p);
+      *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(c0 + c) * ldd + r0 + 8 * p) = v;
+    }
+  }
+}
+
+// One product of a chunk: out[Q rows][P rows] (+)= Q . P^T over K.
+struct GemmOp {
+  const uint16_t* p;  // [P][ldp] bf16, K contiguous: output columns
+  int64_t ldp;
+  int P;
+  const uint16_t* q;  // [Q][ldq] bf16, K contiguous: output rows
+  int64_t ldq;
+  int Q;
+  int K;
+  float* out;         // [Q][ldo] fp32
+  int64_t ldo;
+  int accumulate;     // out = out + acc instead of out = acc
+  int n_ptiles;
+  int n_qtiles;
+  int first;          // first workgroup of this product (a multiple of 8)
+};
+
+struct GemmArgs {
+  GemmOp op[2];
+  int n_ops;
+};
+
+// Both products of a chunk in one launch.  Workgroups [op[0].first, ...)
+// compute op 0's tiles and [op[1].first, ...) op 1's; ids in between are
+// idle padding that keeps each product's first id a multiple of 8 (the XCD
+// regrouping works on ids relative to it).  The hardware dispatches
+// workgroups in id order as compute units free up, so the long tiles listed
+// first are spread over the chip before the short ones fill the gaps.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void grad_gemm_tiles(GemmArgs args) {
+  __shared__ uint4 smem[kGemmSmemVec];
+  const bool second = (args.n_ops > 1) && (static_cast<int>(blockIdx.x) >= args.op[1].first);
+  const GemmOp& g = second ? args.op[1] : args.op[0];
+  const int w = static_cast<int>(blockIdx.x) - g.first;
+  if (w < 0 || w >= g.n_ptiles * g.n_qtiles) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wp = wave / kWQ;
+  const int wq = wave % kWQ;
+  int qt, pt;
+  grouped_coords(w, g.n_qtiles, g.n_ptiles, kLinearVocabGroup, qt, pt);
+  const int p0 = pt * kBP;
+  const int q0 = qt * kBQ;
+  const int P_tail = min(g.P - p0, kBP);
+  const int Q_tail = min(g.Q - q0, kBQ);
+
+  const __amdgpu_buffer_rsrc_t pres = uniform_rsrc(g.p + static_cast<int64_t>(p0) * g.ldp, P_tail * g.ldp * 2);
+  const __amdgpu_buffer_rsrc_t qres = uniform_rsrc(g.q + static_cast<int64_t>(q0) * g.ldq, Q_tail * g.ldq * 2);
+  const Loader ld = make_loader(wave, lane, g.ldp, g.ldq);
+  f32x16_t acc[kI][kJ];
+  mainloop(smem, ld, wave, lane, wp, wq, pres, qres, g.K, acc);
+
+  // Staged through LDS one 32-row slice at a time so that each store
+  // instruction writes two 512-byte row segments.
+  const int half = lane >> 5;
+  float* stage = reinterpret_cast<float*>(smem) + wave * (32 * kOutStride);
+  float* srow = stage + (lane & 31) * kOutStride;
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+#pragma unroll
+    for (int i = 0; i < kI; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m0 = i * 32 + 8 * q + 4 * half;
+        *reinterpret_cast<float4*>(srow + m0) =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+      }
+    __syncthreads();
+#pragma unroll 4
+    for (int step = 0; step < 16; ++step) {
+      const int r = 2 * step + (lane >> 5);
+      const int c4 = lane & 31;
+      const int rr = wq * kQW + j * 32 + r;  // output row within the tile
+      if (rr < Q_tail) {
+        float4 v = *reinterpret_cast<const float4*>(stage + r * kOutStride + 4 * c4);
+        const int mrel = wp * kPW + 4 * c4;  // output column within the tile
+        float* dst = g.out + static_cast<int64_t>(q0 + rr) * g.ldo + p0 + mrel;
+        if (mrel + 4 <= P_tail) {
+          if (g.accumulate) {
+            const float4 o = *reinterpret_cast<const float4*>(dst);
+            v = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
+          }
+          *reinterpret_cast<float4*>(dst) = v;
+        } else {
+          const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (mrel + e < P_tail) dst[e] = g.accumulate ? dst[e] + vv[e] : vv[e];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// out[r][c] = 0 for r < rows, c < cols (cols % 4 == 0, 16-byte aligned rows)
+__global__ __launch_bounds__(256) void zero_rows_f32(float* __restrict__ out, int64_t ldo,
+                                                     int64_t rows, int cols) {
+  const int64_t quads = static_cast<int64_t>(cols / 4);
+  const int64_t total = rows * quads;
+  for (int64_t k = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; k < total;
+       k += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t r = k / quads;
+    const int64_t c = (k - r * quads) * 4;
+    *reinterpret_cast<float4*>(out + r * ldo + c) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+
+struct GradLayout {
+  int64_t Np;         // N rounded up to 8
+  int64_t chunk;      // vocabulary entries per pass (multiple of 256)
+  size_t off_hT, off_wT, off_d, off_dT, total;
+};
+
+GradLayout grad_layout(int64_t N, int64_t V, int64_t H) {
+  GradLayout L;
+  L.Np = round_up(N, 8);
+  L.chunk = min64(kGradChunk, round_up(V, kBP));
+  auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+  L.off_hT = 0;
+  L.off_wT = L.off_hT + al(static_cast<size_t>(H * L.Np * 2));
+  L.off_d = L.off_wT + al(static_cast<size_t>(H * L.chunk * 2));
+  L.off_dT = L.off_d + al(static_cast<size_t>(N * L.chunk * 2));
+  L.total = L.off_dT + al(static_cast<size_t>(L.chunk * L.Np * 2));
+  return L;
+}
+
+}  // namespace
+
+size_t linear_param_grads_workspace_bytes(int64_t N, int64_t V, int64_t H) {
+  return grad_layout(N, V, H).total;
+}
+
+hipError_t launch_linear_param_grads(const uint16_t* hidden, int64_t ldh, const uint16_t* weight,
+                                     int64_t ldw, const int64_t* targets, const uint8_t* mask,
+                                     const float* lse, const float* grad, int64_t N, int V, int H,
+                                     float* grad_hidden, int64_t ld_gh, float* grad_weight,
+                                     int64_t ld_gw, void* workspace, hipStream_t stream) {
+  if (N == 0) {
+    // no tokens: grad_weight is an empty sum; grad_hidden has no rows
+    if (grad_weight != nullptr) {
+      const int64_t quads = static_cast<int64_t>(V) * (H / 4);
+      const int64_t blocks = min64((quads + 255) / 256, 65536);
+      hipLaunchKernelGGL(zero_rows_f32, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
+                         grad_weight, ld_gw, static_cast<int64_t>(V), H);
+      return hipGetLastError();
+    }
+    return hipSuccess;
+  }
+  const GradLayout L = grad_layout(N, V, H);
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* hT = reinterpret_cast<uint16_t*>(ws + L.off_hT);
+  uint16_t* wT = reinterpret_cast<uint16_t*>(ws + L.off_wT);
+  uint16_t* d = reinterpret_cast<uint16_t*>(ws + L.off_d);
+  uint16_t* dT = reinterpret_cast<uint16_t*>(ws + L.off_dT);
+  const bool want_h = grad_hidden != nullptr;
+  const bool want_w = grad_weight != nullptr;
+  const int n_vtiles = (V + kBP - 1) / kBP;
+  const int n_tblocks = static_cast<int>((N + kBQ - 1) / kBQ);
+  const int tiles_per_chunk = static_cast<int>(L.chunk / kBP);
+  const int n_chunks = (n_vtiles + tiles_per_chunk - 1) / tiles_per_chunk;
+  const int n_htiles = (H + kBP - 1) / kBP;
+
+  if (want_w) {
+    hipLaunchKernelGGL(transpose_bf16,
+                       dim3(static_cast<uint32_t>(L.Np / kTrTile + (L.Np % kTrTile != 0)),
+                            static_cast<uint32_t>((H + kTrTile - 1) / kTrTile)),
+                       dim3(256), 0, stream, hidden, ldh, static_cast<int>(N), H, hT, L.Np,
+                       static_cast<int>(L.Np));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  for (int c = 0; c < n_chunks; ++c) {
+    const int vt0 = c * tiles_per_chunk;
+    const int n_vt = static_cast<int>(min64(tiles_per_chunk, n_vtiles - vt0));
+    const int vocab0 = vt0 * kBP;
+    const int v_rows = static_cast<int>(min64(V - vocab0, n_vt * kBP));  // real vocabulary rows
+    const int width = n_vt * kBP;                     // padded chunk width
+
+    DlArgs da{};
+    da.hidden = hidden;
+    da.ldh = ldh;
+    da.weight = weight;
+    da.ldw = ldw;
+    da.targets = targets;
+    da.mask = mask;
+    da.lse = lse;
+    da.grad = grad;
+    da.N = N;
+    da.V = V;
+    da.H = H;
+    da.vt0 = vt0;
+    da.n_vt = n_vt;
+    da.n_tblocks = n_tblocks;
+    da.d = want_h ? d : nullptr;
+    da.ldd = L.chunk;
+    da.dT = want_w ? dT : nullptr;
+    da.ldt = L.Np;
+    hipLaunchKernelGGL(grad_dl_tiles, dim3(static_cast<uint32_t>(n_vt * n_tblocks)), dim3(kThreads),
+                       0, stream, da);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    GemmArgs ga{};
+    int nblk = 0;
+    if (want_h) {
+      hipLaunchKernelGGL(transpose_bf16,
+                         dim3(static_cast<uint32_t>(width / kTrTile),
+                              static_cast<uint32_t>((H + kTrTile - 1) / kTrTile)),
+                         dim3(256), 0, stream, weight + static_cast<int64_t>(vocab0) * ldw, ldw,
+                         v_rows, H, wT, L.chunk, width);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      GemmOp& o = ga.op[ga.n_ops++];
+      o.p = wT;
+      o.ldp = L.chunk;
+      o.P = H;
+      o.q = d;
+      o.ldq = L.chunk;
+      o.Q = static_cast<int>(N);
+      o.K = width;
+      o.out = grad_hidden;
+      o.ldo = ld_gh;
+      o.accumulate = c > 0;
+      o.n_ptiles = n_htiles;
+      o.n_qtiles = n_tblocks;
+      o.first = nblk;
+      nblk += static_cast<int>(round_up(static_cast<int64_t>(o.n_ptiles) * o.n_qtiles, 8));
+    }
+    if (want_w) {
+      GemmOp& o = ga.op[ga.n_ops++];
+      o.p = hT;
+      o.ldp = L.Np;
+      o.P = H;
+      o.q = dT;
+      o.ldq = L.Np;
+      o.Q = v_rows;
+      o.K = static_cast<int>(N);
+      o.out = grad_weight + static_cast<int64_t>(vocab0) * ld_gw;
+      o.ldo = ld_gw;
+      o.accumulate = 0;
+      o.n_ptiles = n_htiles;
+      o.n_qtiles = (v_rows + kBQ - 1) / kBQ;
+      o.first = nblk;
+      nblk += o.n_ptiles * o.n_qtiles;
+    }
+    hipLaunchKernelGGL(grad_gemm_tiles, dim3(static_cast<uint32_t>(nblk)), dim3(kThreads), 0,
+                       stream, ga);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace rlk

@@ -35,61 +35,21 @@
 
 #include "rlk_device.hpp"
 #include "rlk_internal.hpp"
+#include "tile_core.hpp"
 
 namespace rlk {
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+using namespace tile;
 
-constexpr int kBV = kLinearVocabTile;   // vocabulary entries per tile (= chunk)
-constexpr int kBT = kLinearTokenTile;   // tokens per tile
-constexpr int kBK = kLinearKStage;      // K per pipeline stage
-constexpr int kWaves = 8;               // 2 (vocabulary) x 4 (tokens), two per SIMD
-constexpr int kThreads = 64 * kWaves;
-constexpr int kWT = kWaves / 2;         // waves along the token side
-constexpr int kTW = kBT / kWT;          // tokens per wave (64)
-constexpr int kJ = kTW / 32;            // 32-token MFMA blocks per wave (2)
-constexpr int kI = (kBV / 2) / 32;      // 32-entry vocabulary blocks per wave (4)
-constexpr int kRowChunks = kBK / 8;     // 16-byte chunks per tile row per stage
-constexpr int kAVec = kBV * kRowChunks; // uint4 per stage, W side
-constexpr int kBVec = kBT * kRowChunks; // uint4 per stage, hidden side
-constexpr int kStageVec = kAVec + kBVec;
-constexpr int kBlkPerWave = (kAVec / 64) / kWaves;  // 1 KB copies per wave per operand per stage
-constexpr int kSub = kBK / 16;          // 16-deep MFMA steps per stage
+constexpr int kBV = kLinearVocabTile;   // vocabulary entries per tile (= chunk): the P side
+constexpr int kBT = kLinearTokenTile;   // tokens per tile: the Q side
 constexpr int kStageStride = 132;       // floats per staged dlogits row (128 + 4 pad)
 constexpr int kStagingVec = kWaves * 32 * kStageStride / 4;
 constexpr int kSmemVec = (2 * kStageVec > kStagingVec) ? 2 * kStageVec : kStagingVec;
-static_assert(kAVec == kBVec, "loader assumes square tiles");
-static_assert(kRowChunks == 8, "swizzle assumes 8 chunks per row");
-static_assert(kBlkPerWave % 2 == 0, "a stage's copies are issued in two halves");
+static_assert(kBV == kBP && kBT == kBQ, "vocabulary rows are the P side, tokens the Q side");
 static_assert(kSmemVec * 16 <= 160 * 1024, "LDS budget of one CU");
-
-// Word 3 of a raw buffer resource on gfx9-family parts (data format field)
-constexpr int kBufferResourceWord3 = 0x00020000;
-
-// Raw buffer resource over [base, base + bytes), built from wave-uniform
-// values so that it lives in scalar registers.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const uint16_t* base, int64_t bytes) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
-  const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
-  void* q = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(q, 0, n, kBufferResourceWord3);
-}
-
-// A byte offset beyond any buffer range: such loads return zero.
-constexpr int kOutOfRange = 0x7ffffff0;
-
-// LDS chunk swizzle: chunk c of tile row r is stored at c ^ ((r >> 1) & 7) so
-// that the 16-byte fragment reads of consecutive rows spread over all banks.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
-
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-// generic pointer into __shared__ memory -> LDS address space pointer
-__device__ __forceinline__ lds_void_ptr to_lds(uint4* p) { return (lds_void_ptr)(p); }
 
 struct TileArgs {
   const uint16_t* hidden;
@@ -113,24 +73,10 @@ struct TileArgs {
   int64_t ldg;
 };
 
-// blockIdx -> (vocabulary tile, token block).  Workgroups are dispatched
-// round-robin over the 8 XCDs, so ids are first regrouped into contiguous
-// per-XCD ranges; within a range, tiles are ordered by groups of
-// kLinearVocabGroup vocabulary tiles x all token blocks, so the workgroups
-// sharing an XCD (and its L2) work on few W tiles and few hidden blocks at a
-// time.  A bijection on [0, n_tiles); it only decides *when* a tile runs,
-// never how it is computed.
+// blockIdx -> (vocabulary tile, token block): XCD-contiguous ranges, then
+// groups of kLinearVocabGroup vocabulary tiles x all token blocks.
 __device__ __forceinline__ void tile_coords(int w, int n_vtiles, int n_tblocks, int& vt, int& tb) {
-  const int total = n_vtiles * n_tblocks;
-  const int t8 = (total / 8) * 8;
-  int L = w;
-  if (w < t8) L = (w & 7) * (t8 / 8) + (w >> 3);
-  const int span = kLinearVocabGroup * n_tblocks;
-  const int g = L / span;
-  const int rem = L - g * span;
-  const int gsize = min(kLinearVocabGroup, n_vtiles - g * kLinearVocabGroup);
-  tb = rem / gsize;
-  vt = g * kLinearVocabGroup + (rem - tb * gsize);
+  grouped_coords(w, n_vtiles, n_tblocks, kLinearVocabGroup, vt, tb);
 }
 
 // Backward tile kernel: the forward's per-tile main loop (same copies, same
@@ -142,114 +88,23 @@ void linear_tiles_bwd(TileArgs args) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wv = wave / kWT;  // vocabulary half of the tile
-  const int wt = wave % kWT;  // token quarter of the tile
+  const int wv = wave / kWQ;  // vocabulary half of the tile
+  const int wt = wave % kWQ;  // token quarter of the tile
   int vt, tb;
   tile_coords(blockIdx.x, args.n_vtiles, args.n_tblocks, vt, tb);
   const int vocab0 = vt * kBV;
   const int64_t tok0 = static_cast<int64_t>(tb) * kBT;
   const int N_tail = static_cast<int>(min<int64_t>(args.N - tok0, kBT));  // rows of this block < N
   const int V_tail = min(args.V - vocab0, kBV);
-  const int H = args.H;
-  const int n_kt = (H + kBK - 1) / kBK;
 
-  // Loader: global -> LDS directly (buffer_load ... lds), no staging
-  // registers.  One wave instruction fills 1 KB of LDS = 8 tile rows of 128
-  // bytes; lane l writes physical chunk (l & 7) of its row, which holds
-  // logical chunk (l & 7) ^ swizzle(row).  Rows past V (or N) lie outside the
-  // buffer's range and read as zero.  Each lane's byte offset is fixed for
-  // the whole K loop; a stage's K position goes into the scalar offset.  In
-  // a ragged last stage, chunks past H are forced out of range (zero).
+  // W rows past V and hidden rows past N lie outside the resources' ranges
+  // and read as zero.
   const __amdgpu_buffer_rsrc_t wres =
       uniform_rsrc(args.weight + static_cast<int64_t>(vocab0) * args.ldw, V_tail * args.ldw * 2);
   const __amdgpu_buffer_rsrc_t hres = uniform_rsrc(args.hidden + tok0 * args.ldh, N_tail * args.ldh * 2);
-  int voff_w[kBlkPerWave], voff_h[kBlkPerWave], kcol[kBlkPerWave];
-#pragma unroll
-  for (int q = 0; q < kBlkPerWave; ++q) {
-    const int idx = (wave * kBlkPerWave + q) * 64 + lane;
-    const int r = idx / kRowChunks;
-    const int c = (idx % kRowChunks) ^ ((r >> 1) & 7);
-    kcol[q] = 8 * c;
-    voff_w[q] = (r * static_cast<int>(args.ldw) + 8 * c) * 2;
-    voff_h[q] = (r * static_cast<int>(args.ldh) + 8 * c) * 2;
-  }
-  // copies q in [q0, q1) of stage kt into LDS buffer st
-  auto issue = [&](int kt, int st, int q0, int q1) {
-    const int k0 = kt * kBK;
-    const bool full = (k0 + kBK) <= H;
-    uint4* a = smem + st * kStageVec;
-    uint4* b = a + kAVec;
-#pragma unroll
-    for (int q = q0; q < q1; ++q) {
-      const int blk = wave * kBlkPerWave + q;
-      int vw = voff_w[q], vh = voff_h[q];
-      if (!full && (k0 + kcol[q]) >= H) {
-        vw = kOutOfRange;
-        vh = kOutOfRange;
-      }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, to_lds(a + blk * 64), 16, vw, k0 * 2, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(hres, to_lds(b + blk * 64), 16, vh, k0 * 2, 0, 0);
-    }
-  };
-
+  const Loader ld = make_loader(wave, lane, args.ldw, args.ldh);
   f32x16_t acc[kI][kJ];
-#pragma unroll
-  for (int i = 0; i < kI; ++i)
-#pragma unroll
-    for (int j = 0; j < kJ; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  // MFMA operands of one 16-deep step: lane supplies row (lane & 31) and
-  // k-chunk (lane >> 5) of each 32-row block
-  auto frag = [&](const uint4* a, const uint4* b, int kk, bf16x8_t (&fa)[kI], bf16x8_t (&fb)[kJ]) {
-    const int c = 2 * kk + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < kI; ++i) {
-      const int r = wv * 128 + i * 32 + (lane & 31);
-      fa[i] = __builtin_bit_cast(bf16x8_t, a[r * kRowChunks + swz(r, c)]);
-    }
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) {
-      const int r = wt * kTW + j * 32 + (lane & 31);
-      fb[j] = __builtin_bit_cast(bf16x8_t, b[r * kRowChunks + swz(r, c)]);
-    }
-  };
-  auto mma = [&](const bf16x8_t (&fa)[kI], const bf16x8_t (&fb)[kJ]) {
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int i = 0; i < kI; ++i)
-#pragma unroll
-      for (int j = 0; j < kJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    __builtin_amdgcn_s_setprio(0);
-  };
-
-  // Main loop: K stages in ascending order through two LDS buffers.  At the
-  // top of stage kt each wave waits for its own copies of stage kt, and the
-  // barrier makes every wave's copies visible (and frees the other buffer);
-  // stage kt + 1's copies are then issued during the first two MFMA steps.
-  // The wait and the barrier form one asm statement so that no LDS read can
-  // be scheduled between them.
-  issue(0, 0, 0, kBlkPerWave);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    const bool pf = (kt + 1) < n_kt;
-    const uint4* a = smem + (kt & 1) * kStageVec;
-    const uint4* b = a + kAVec;
-    bf16x8_t fa0[kI], fb0[kJ], fa1[kI], fb1[kJ];
-    frag(a, b, 0, fa0, fb0);
-#pragma unroll
-    for (int kk = 0; kk < kSub; kk += 2) {
-      frag(a, b, kk + 1, fa1, fb1);
-      if (pf && kk == 0) issue(kt + 1, (kt + 1) & 1, 0, kBlkPerWave / 2);
-      mma(fa0, fb0);
-      if (kk + 2 < kSub) frag(a, b, kk + 2, fa0, fb0);
-      if (pf && kk == 0) issue(kt + 1, (kt + 1) & 1, kBlkPerWave / 2, kBlkPerWave);
-      mma(fa1, fb1);
-    }
-  }
-  __syncthreads();
+  mainloop(smem, ld, wave, lane, wv, wt, wres, hres, args.H, acc);
 
   // Result layout of a 32x32 MFMA block: lane holds token column
   // (lane & 31) and vocabulary rows 8 (e >> 2) + 4 (lane >> 5) + (e & 3).
@@ -263,7 +118,7 @@ void linear_tiles_bwd(TileArgs args) {
     const float nan = __builtin_nanf("");
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
-      const int tl = wt * kTW + j * 32 + (lane & 31);
+      const int tl = wt * kQW + j * 32 + (lane & 31);
       const bool have = tl < N_tail;
       const int64_t tok = tok0 + tl;
       const bool active = have && ((args.mask == nullptr) || (args.mask[tok] != 0));
@@ -294,7 +149,7 @@ void linear_tiles_bwd(TileArgs args) {
       for (int step = 0; step < 16; ++step) {
         const int r = 2 * step + (lane >> 5);
         const int c4 = lane & 31;
-        const int tr = wt * kTW + j * 32 + r;
+        const int tr = wt * kQW + j * 32 + r;
         if (tr < N_tail) {
           const float4 v = *reinterpret_cast<const float4*>(stage + r * kStageStride + 4 * c4);
           const int mrel = wv * 128 + 4 * c4;  // relative to vocab0
@@ -326,21 +181,12 @@ void linear_tiles_fwd_persistent(TileArgs args) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wv = wave / kWT;
-  const int wt = wave % kWT;
+  const int wv = wave / kWQ;
+  const int wt = wave % kWQ;
   const int n_tiles = args.n_vtiles * args.n_tblocks;
   const int H = args.H;
   const int n_kt = (H + kBK - 1) / kBK;
-  int voff_w[kBlkPerWave], voff_h[kBlkPerWave], kcol[kBlkPerWave];
-#pragma unroll
-  for (int q = 0; q < kBlkPerWave; ++q) {
-    const int idx = (wave * kBlkPerWave + q) * 64 + lane;
-    const int r = idx / kRowChunks;
-    const int c = (idx % kRowChunks) ^ ((r >> 1) & 7);
-    kcol[q] = 8 * c;
-    voff_w[q] = (r * static_cast<int>(args.ldw) + 8 * c) * 2;
-    voff_h[q] = (r * static_cast<int>(args.ldh) + 8 * c) * 2;
-  }
+  const Loader ld = make_loader(wave, lane, args.ldw, args.ldh);
   struct Geo {
     int vt;
     int vocab0;
@@ -363,42 +209,12 @@ void linear_tiles_fwd_persistent(TileArgs args) {
     g.hres = uniform_rsrc(args.hidden + g.tok0 * args.ldh, g.N_tail * args.ldh * 2);
     return g;
   };
-  auto issue = [&](const Geo& g, int kt, int st, int q0, int q1) {
-    const int k0 = kt * kBK;
-    const bool full = (k0 + kBK) <= H;
-    uint4* a = smem + st * kStageVec;
-    uint4* b = a + kAVec;
-#pragma unroll
-    for (int q = q0; q < q1; ++q) {
-      const int blk = wave * kBlkPerWave + q;
-      int vw = voff_w[q], vh = voff_h[q];
-      if (!full && (k0 + kcol[q]) >= H) {
-        vw = kOutOfRange;
-        vh = kOutOfRange;
-      }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(g.wres, to_lds(a + blk * 64), 16, vw, k0 * 2, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(g.hres, to_lds(b + blk * 64), 16, vh, k0 * 2, 0, 0);
-    }
-  };
-  auto frag = [&](const uint4* a, const uint4* b, int kk, bf16x8_t (&fa)[kI], bf16x8_t (&fb)[kJ]) {
-    const int c = 2 * kk + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < kI; ++i) {
-      const int r = wv * 128 + i * 32 + (lane & 31);
-      fa[i] = __builtin_bit_cast(bf16x8_t, a[r * kRowChunks + swz(r, c)]);
-    }
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) {
-      const int r = wt * kTW + j * 32 + (lane & 31);
-      fb[j] = __builtin_bit_cast(bf16x8_t, b[r * kRowChunks + swz(r, c)]);
-    }
-  };
 
   int tile = blockIdx.x;
   if (tile >= n_tiles) return;
   Geo cur = geo(tile);
   int g0 = 0;  // ring position of the current tile's stage 0
-  issue(cur, 0, 0, 0, kBlkPerWave);
+  issue<0, kBlkPerWave>(smem, ld, wave, cur.wres, cur.hres, 0, 0, H);
   for (;;) {
     const int next = tile + gridDim.x;
     const bool has_next = next < n_tiles;
@@ -408,50 +224,29 @@ void linear_tiles_fwd_persistent(TileArgs args) {
     int64_t tgt[kJ];
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
-      const int tl = wt * kTW + j * 32 + (lane & 31);
+      const int tl = wt * kQW + j * 32 + (lane & 31);
       tgt[j] = (tl < cur.N_tail) ? args.targets[cur.tok0 + tl] : -1;
     }
     f32x16_t acc[kI][kJ];
-#pragma unroll
-    for (int i = 0; i < kI; ++i)
-#pragma unroll
-      for (int j = 0; j < kJ; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    auto mma = [&](const bf16x8_t (&fa)[kI], const bf16x8_t (&fb)[kJ]) {
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int i = 0; i < kI; ++i)
-#pragma unroll
-        for (int j = 0; j < kJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-      __builtin_amdgcn_s_setprio(0);
-    };
+    zero(acc);
     for (int kt = 0; kt < n_kt; ++kt) {
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
       const int buf = (g0 + kt) & 1;
       const int nbuf = buf ^ 1;
       const bool pf_same = (kt + 1) < n_kt;
       const bool pf_next = !pf_same && has_next;
-      const uint4* a = smem + buf * kStageVec;
-      const uint4* b = a + kAVec;
-      bf16x8_t fa0[kI], fb0[kJ], fa1[kI], fb1[kJ];
-      frag(a, b, 0, fa0, fb0);
-#pragma unroll
-      for (int kk = 0; kk < kSub; kk += 2) {
-        frag(a, b, kk + 1, fa1, fb1);
-        if (kk == 0) {
-          if (pf_same) issue(cur, kt + 1, nbuf, 0, kBlkPerWave / 2);
-          else if (pf_next) issue(nxt, 0, nbuf, 0, kBlkPerWave / 2);
-        }
-        mma(fa0, fb0);
-        if (kk + 2 < kSub) frag(a, b, kk + 2, fa0, fb0);
-        if (kk == 0) {
-          if (pf_same) issue(cur, kt + 1, nbuf, kBlkPerWave / 2, kBlkPerWave);
-          else if (pf_next) issue(nxt, 0, nbuf, kBlkPerWave / 2, kBlkPerWave);
-        }
-        mma(fa1, fb1);
-      }
+      stage(
+          acc, smem + buf * kStageVec, wv, wt, lane,
+          [&] {
+            if (pf_same) issue<0, kBlkPerWave / 2>(smem, ld, wave, cur.wres, cur.hres, kt + 1, nbuf, H);
+            else if (pf_next) issue<0, kBlkPerWave / 2>(smem, ld, wave, nxt.wres, nxt.hres, 0, nbuf, H);
+          },
+          [&] {
+            if (pf_same)
+              issue<kBlkPerWave / 2, kBlkPerWave>(smem, ld, wave, cur.wres, cur.hres, kt + 1, nbuf, H);
+            else if (pf_next)
+              issue<kBlkPerWave / 2, kBlkPerWave>(smem, ld, wave, nxt.wres, nxt.hres, 0, nbuf, H);
+          });
     }
     // everyone is done reading the last stage's buffer; the next tile's
     // stage 0 may still be landing in the other one
@@ -464,7 +259,7 @@ void linear_tiles_fwd_persistent(TileArgs args) {
     float2* red = reinterpret_cast<float2*>(smem + free_buf * kStageVec);
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
-      const int tl = wt * kTW + j * 32 + (lane & 31);
+      const int tl = wt * kQW + j * 32 + (lane & 31);
       const int64_t tok = cur.tok0 + tl;
       float mx = neg_inf();
 #pragma unroll

@@ -155,6 +155,53 @@ int rlk_logp_backward(const void* logits, int64_t ld, const void* hidden, int64_
       ld_g, stream));
 }
 
+size_t rlk_linear_logp_param_grads_workspace_size(int64_t N, int64_t V, int64_t H) {
+  if (N < 0 || V < 1 || H < 1) return 0;
+  return rlk::linear_param_grads_workspace_bytes(N, V, H);
+}
+
+int rlk_linear_logp_param_grads(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
+                                const int64_t* targets, const uint8_t* mask, const float* lse,
+                                const float* grad_logp, int64_t N, int64_t V, int64_t H,
+                                float* grad_hidden, int64_t ld_gh, float* grad_weight,
+                                int64_t ld_gw, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  int st = check_sizes(N, V);
+  if (st != RLK_OK) return st;
+  if (grad_hidden == nullptr && grad_weight == nullptr) return RLK_ERR_INVALID_ARG;
+  if (weight == nullptr || H < 1 || ld_w < H) return RLK_ERR_INVALID_ARG;
+  if (grad_weight != nullptr) {
+    if (ld_gw < H) return RLK_ERR_INVALID_ARG;
+    if ((ld_gw % 4) != 0 || !aligned16(grad_weight)) return RLK_ERR_UNSUPPORTED;
+    if (ld_gw > (int64_t(1) << 62) / V) return RLK_ERR_UNSUPPORTED;
+  }
+  if (N == 0) {
+    if ((H % 8) != 0) return RLK_ERR_UNSUPPORTED;
+    return status_of(rlk::launch_linear_param_grads(
+        nullptr, 0, static_cast<const uint16_t*>(weight), ld_w, nullptr, nullptr, nullptr, nullptr,
+        0, static_cast<int>(V), static_cast<int>(H), nullptr, 0, grad_weight, ld_gw, nullptr,
+        stream));
+  }
+  if (targets == nullptr || lse == nullptr || grad_logp == nullptr || workspace == nullptr)
+    return RLK_ERR_INVALID_ARG;
+  st = check_linear(hidden, ld_h, weight, ld_w, N, V, H);
+  if (st != RLK_OK) return st;
+  // the transposed hidden's rows (N rounded up to 8) are addressed like a
+  // fused-tile operand
+  if (N > kMaxLinearLd - 16) return RLK_ERR_UNSUPPORTED;
+  if (grad_hidden != nullptr) {
+    if (ld_gh < H) return RLK_ERR_INVALID_ARG;
+    if ((ld_gh % 4) != 0 || !aligned16(grad_hidden)) return RLK_ERR_UNSUPPORTED;
+    if (ld_gh > (int64_t(1) << 62) / N) return RLK_ERR_UNSUPPORTED;
+  }
+  if (workspace_bytes < rlk::linear_param_grads_workspace_bytes(N, V, H)) return RLK_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return RLK_ERR_UNSUPPORTED;
+  return status_of(rlk::launch_linear_param_grads(
+      static_cast<const uint16_t*>(hidden), ld_h, static_cast<const uint16_t*>(weight), ld_w,
+      targets, mask, lse, grad_logp, N, static_cast<int>(V), static_cast<int>(H), grad_hidden,
+      ld_gh, grad_weight, ld_gw, workspace, stream));
+}
+
 int rlk_token_losses(const float* logp, const float* logp_old, const float* logp_ref,
                      const float* advantages, const uint8_t* mask, int64_t N, float eps_lo,
                      float eps_hi, float beta, float* ratio, float* loss, float* kl,
@@ -188,7 +235,7 @@ const char* rlk_status_string(int status) {
 const char* rlk_build_info(void) {
   return "rlk 0.1.0; arch=gfx950; rev=" RLK_GIT_REV
          "; schedule=rows:256thr,8x16B/lane-step; bwd:256thr,8x8B; tile:" RLK_STR(256) "x" RLK_STR(
-             256) "x" RLK_STR(64) ",8waves,mfma32x32x16bf16,2stage,group8,fwd-persistent; combine:wave-per-row";
+             256) "x" RLK_STR(64) ",8waves,mfma32x32x16bf16,2stage,group8,fwd-persistent; combine:wave-per-row; grads:chunk" RLK_STR(16384) ",dl-bf16,wT";
 }
 
 }  // extern "C"

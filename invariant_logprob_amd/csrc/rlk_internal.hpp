@@ -15,6 +15,9 @@ constexpr int kLinearTokenTile = 256;
 constexpr int kLinearKStage = 64;
 // Vocabulary tiles grouped together in the launch order (scheduling only).
 constexpr int kLinearVocabGroup = 8;
+// Vocabulary entries per pass of the parameter-gradient path (a multiple of
+// the vocabulary tile): the chunking of the contraction over the vocabulary.
+constexpr int kGradChunk = 16384;
 
 int logits_schedule_threads();
 int logits_schedule_unroll();
@@ -60,5 +63,13 @@ hipError_t launch_linear_dlogits(const uint16_t* hidden, int64_t ldh, const uint
                                  int64_t ldw, const int64_t* targets, const uint8_t* mask,
                                  const float* lse, const float* grad, int64_t N, int V, int H,
                                  float* dl, int64_t ldg, hipStream_t stream);
+
+size_t linear_param_grads_workspace_bytes(int64_t N, int64_t V, int64_t H);
+
+hipError_t launch_linear_param_grads(const uint16_t* hidden, int64_t ldh, const uint16_t* weight,
+                                     int64_t ldw, const int64_t* targets, const uint8_t* mask,
+                                     const float* lse, const float* grad, int64_t N, int V, int H,
+                                     float* grad_hidden, int64_t ld_gh, float* grad_weight,
+                                     int64_t ld_gw, void* workspace, hipStream_t stream);
 
 }  // namespace rlk

@@ -1,0 +1,228 @@
+// Shared core of the bf16 MFMA tile kernels (gfx950): the 256 x 256 tile
+// geometry, the direct global -> LDS loader, the swizzled fragment reads and
+// the K main loop.  Every tile kernel of the library forms its products
+// through these pieces, so a tile's fp32 result depends only on its operand
+// rows and on K -- never on the kernel, launch or batch that computes it.
+//
+// A tile multiplies kBP rows of operand P (the MFMA "M" side) by kBQ rows of
+// operand Q (the MFMA "N" side); both operands are bf16 rows with K
+// contiguous, and K is visited in ascending 64-wide stages, 16 per
+// v_mfma_f32_32x32x16_bf16 instruction, accumulating in fp32.  Eight waves
+// (two per SIMD) split the tile 2 (P) x 4 (Q); each wave owns 128 x 64 =
+// 4 x 2 MFMA blocks.  Result layout of a 32 x 32 block: lane l holds Q row
+// (l & 31) and P rows 8 (e >> 2) + 4 (l >> 5) + (e & 3), e = 0 .. 15.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rlk_device.hpp"
+#include "rlk_internal.hpp"
+
+namespace rlk {
+namespace tile {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kBP = 256;                // P rows per tile
+constexpr int kBQ = 256;                // Q rows per tile
+constexpr int kBK = kLinearKStage;      // K per pipeline stage
+constexpr int kWaves = 8;               // 2 (P) x 4 (Q), two per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWQ = kWaves / 2;         // waves along Q
+constexpr int kQW = kBQ / kWQ;          // Q rows per wave (64)
+constexpr int kPW = kBP / 2;            // P rows per wave (128)
+constexpr int kJ = kQW / 32;            // 32-row Q blocks per wave (2)
+constexpr int kI = kPW / 32;            // 32-row P blocks per wave (4)
+constexpr int kRowChunks = kBK / 8;     // 16-byte chunks per tile row per stage
+constexpr int kPVec = kBP * kRowChunks; // uint4 per stage, P side
+constexpr int kQVec = kBQ * kRowChunks; // uint4 per stage, Q side
+constexpr int kStageVec = kPVec + kQVec;
+constexpr int kBlkPerWave = (kPVec / 64) / kWaves;  // 1 KB copies per wave per operand per stage
+constexpr int kSub = kBK / 16;          // 16-deep MFMA steps per stage
+static_assert(kPVec == kQVec, "loader assumes square tiles");
+static_assert(kRowChunks == 8, "swizzle assumes 8 chunks per row");
+static_assert(kBlkPerWave % 2 == 0, "a stage's copies are issued in two halves");
+static_assert(2 * kStageVec * 16 <= 160 * 1024, "LDS budget of one CU");
+
+// Word 3 of a raw buffer resource on gfx9-family parts (data format field)
+constexpr int kBufferResourceWord3 = 0x00020000;
+// A byte offset beyond any buffer range: such loads return zero.
+constexpr int kOutOfRange = 0x7ffffff0;
+
+// Raw buffer resource over [base, base + bytes), built from wave-uniform
+// values so that it lives in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const uint16_t* base, int64_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+  const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  void* q = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(q, 0, n, kBufferResourceWord3);
+}
+
+// LDS chunk swizzle: chunk c of tile row r is stored at c ^ ((r >> 1) & 7) so
+// that the 16-byte fragment reads of consecutive rows spread over all banks.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+// generic pointer into __shared__ memory -> LDS address space pointer
+__device__ __forceinline__ lds_void_ptr to_lds(uint4* p) { return (lds_void_ptr)(p); }
+
+// Per-lane loader state.  One wave instruction fills 1 KB of LDS = 8 tile
+// rows of 128 bytes; lane l writes physical chunk (l & 7) of its row, which
+// holds logical chunk (l & 7) ^ swizzle(row).  Each lane's byte offset is
+// fixed for the whole K loop; a stage's K position goes into the scalar
+// offset.
+struct Loader {
+  int voff_p[kBlkPerWave];
+  int voff_q[kBlkPerWave];
+  int kcol[kBlkPerWave];
+};
+
+__device__ __forceinline__ Loader make_loader(int wave, int lane, int64_t ldp, int64_t ldq) {
+  Loader L;
+#pragma unroll
+  for (int q = 0; q < kBlkPerWave; ++q) {
+    const int idx = (wave * kBlkPerWave + q) * 64 + lane;
+    const int r = idx / kRowChunks;
+    const int c = (idx % kRowChunks) ^ ((r >> 1) & 7);
+    L.kcol[q] = 8 * c;
+    L.voff_p[q] = (r * static_cast<int>(ldp) + 8 * c) * 2;
+    L.voff_q[q] = (r * static_cast<int>(ldq) + 8 * c) * 2;
+  }
+  return L;
+}
+
+// Copies [Q0, Q1) of this wave for K stage kt into LDS stage buffer st.
+// Rows past the operand's range (the resource's byte count) read as zero; in
+// a ragged last stage, chunks at or past K are forced out of range (zero).
+template <int Q0, int Q1>
+__device__ __forceinline__ void issue(uint4* smem, const Loader& L, int wave,
+                                      __amdgpu_buffer_rsrc_t pres, __amdgpu_buffer_rsrc_t qres,
+                                      int kt, int st, int K) {
+  const int k0 = kt * kBK;
+  const bool full = (k0 + kBK) <= K;
+  uint4* a = smem + st * kStageVec;
+  uint4* b = a + kPVec;
+#pragma unroll
+  for (int q = Q0; q < Q1; ++q) {
+    const int blk = wave * kBlkPerWave + q;
+    int vp = L.voff_p[q], vq = L.voff_q[q];
+    if (!full && (k0 + L.kcol[q]) >= K) {
+      vp = kOutOfRange;
+      vq = kOutOfRange;
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(pres, to_lds(a + blk * 64), 16, vp, k0 * 2, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(qres, to_lds(b + blk * 64), 16, vq, k0 * 2, 0, 0);
+  }
+}
+
+// MFMA operands of one 16-deep step: lane supplies row (lane & 31) and
+// k-chunk (lane >> 5) of each 32-row block.
+__device__ __forceinline__ void frag(const uint4* a, int kk, int wp, int wq, int lane,
+                                     bf16x8_t (&fa)[kI], bf16x8_t (&fb)[kJ]) {
+  const uint4* b = a + kPVec;
+  const int c = 2 * kk + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < kI; ++i) {
+    const int r = wp * kPW + i * 32 + (lane & 31);
+    fa[i] = __builtin_bit_cast(bf16x8_t, a[r * kRowChunks + swz(r, c)]);
+  }
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int r = wq * kQW + j * 32 + (lane & 31);
+    fb[j] = __builtin_bit_cast(bf16x8_t, b[r * kRowChunks + swz(r, c)]);
+  }
+}
+
+__device__ __forceinline__ void mma(f32x16_t (&acc)[kI][kJ], const bf16x8_t (&fa)[kI],
+                                    const bf16x8_t (&fb)[kJ]) {
+  __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+  for (int i = 0; i < kI; ++i)
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  __builtin_amdgcn_s_setprio(0);
+}
+
+__device__ __forceinline__ void zero(f32x16_t (&acc)[kI][kJ]) {
+#pragma unroll
+  for (int i = 0; i < kI; ++i)
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+}
+
+// One stage's MFMA work with the copies of the stage after it issued in two
+// halves during the first two steps (the caller's callbacks pf0 / pf1).
+template <typename Pf0, typename Pf1>
+__device__ __forceinline__ void stage(f32x16_t (&acc)[kI][kJ], const uint4* a, int wp, int wq,
+                                      int lane, Pf0&& pf0, Pf1&& pf1) {
+  bf16x8_t fa0[kI], fb0[kJ], fa1[kI], fb1[kJ];
+  frag(a, 0, wp, wq, lane, fa0, fb0);
+#pragma unroll
+  for (int kk = 0; kk < kSub; kk += 2) {
+    frag(a, kk + 1, wp, wq, lane, fa1, fb1);
+    if (kk == 0) pf0();
+    mma(acc, fa0, fb0);
+    if (kk + 2 < kSub) frag(a, kk + 2, wp, wq, lane, fa0, fb0);
+    if (kk == 0) pf1();
+    mma(acc, fa1, fb1);
+  }
+}
+
+// Whole-K main loop of one tile through two LDS buffers.  At the top of
+// stage kt each wave waits for its own copies of stage kt, and the barrier
+// makes every wave's copies visible (and frees the other buffer); stage
+// kt + 1's copies are issued during the first two MFMA steps.  The wait and
+// the barrier form one asm statement so that no LDS read can be scheduled
+// between them.  Ends with a barrier: the LDS may be reused at once.
+__device__ __forceinline__ void mainloop(uint4* smem, const Loader& L, int wave, int lane, int wp,
+                                         int wq, __amdgpu_buffer_rsrc_t pres,
+                                         __amdgpu_buffer_rsrc_t qres, int K,
+                                         f32x16_t (&acc)[kI][kJ]) {
+  const int n_kt = (K + kBK - 1) / kBK;
+  zero(acc);
+  issue<0, kBlkPerWave>(smem, L, wave, pres, qres, 0, 0, K);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    const bool pf = (kt + 1) < n_kt;
+    const int nb = (kt + 1) & 1;
+    stage(
+        acc, smem + (kt & 1) * kStageVec, wp, wq, lane,
+        [&] {
+          if (pf) issue<0, kBlkPerWave / 2>(smem, L, wave, pres, qres, kt + 1, nb, K);
+        },
+        [&] {
+          if (pf) issue<kBlkPerWave / 2, kBlkPerWave>(smem, L, wave, pres, qres, kt + 1, nb, K);
+        });
+  }
+  __syncthreads();
+}
+
+// Launch-order regrouping: workgroups are dispatched round-robin over the 8
+// XCDs, so ids are first regrouped into contiguous per-XCD ranges; within a
+// range, tiles go by groups of `group` major tiles x all minor tiles, so the
+// workgroups sharing an XCD (and its L2) work on few operand slabs at a
+// time.  A bijection on [0, n_major * n_minor); it only decides *when* a
+// tile runs, never how it is computed.
+__device__ __forceinline__ void grouped_coords(int w, int n_major, int n_minor, int group,
+                                               int& major, int& minor) {
+  const int total = n_major * n_minor;
+  const int t8 = (total / 8) * 8;
+  int L = w;
+  if (w < t8) L = (w & 7) * (t8 / 8) + (w >> 3);
+  const int span = group * n_minor;
+  const int g = L / span;
+  const int rem = L - g * span;
+  const int gsize = min(group, n_major - g * group);
+  minor = rem / gsize;
+  major = g * group + (rem - minor * gsize);
+}
+
+}  // namespace tile
+}  // namespace rlk

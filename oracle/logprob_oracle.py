@@ -334,3 +334,58 @@ def linear_param_grads(hidden_bits, weight_bits, targets, mask, lse, grad_logp):
     """Parameter gradients from bf16 hidden [N, H] and weight [V, H] bits."""
     return linear_param_grads_from_f64(bf16_to_f64(hidden_bits), bf16_to_f64(weight_bits),
                                        targets, mask, lse, grad_logp)
+
+
+def linear_grad_hidden_rows(hidden_bits, weight_bits, targets, mask, lse, grad_logp, rows,
+                            block=16384):
+    """Rows ``rows`` of grad_hidden = D . W (float64 [len(rows), H]).
+
+    The same formula as linear_param_grads for a few token rows of a large
+    problem; the weight is visited in blocks of vocabulary rows only to bound
+    host memory."""
+    hb = np.asarray(hidden_bits, dtype=np.uint16)
+    wb = np.asarray(weight_bits, dtype=np.uint16)
+    n = hb.shape[0]
+    v, hh = wb.shape
+    t = np.asarray(targets, dtype=np.int64).reshape(n)
+    act = _active(mask, n)
+    g = np.asarray(grad_logp, dtype=np.float64).reshape(n)
+    ls = np.asarray(lse, dtype=np.float64).reshape(n)
+    rows = [int(r) for r in rows]
+    out = np.zeros((len(rows), hh))
+    h = bf16_to_f64(hb[rows])
+    for k0 in range(0, v, block):
+        k1 = min(v, k0 + block)
+        w = bf16_to_f64(wb[k0:k1])
+        z = h @ w.T
+        for a, i in enumerate(rows):
+            if not act[i]:
+                continue
+            if not (0 <= t[i] < v):
+                raise ValueError("active row with target outside [0, V)")
+            d = -g[i] * np.exp(z[a] - ls[i])
+            if k0 <= t[i] < k1:
+                d[t[i] - k0] += g[i]
+            out[a] += d @ w
+    return out
+
+
+def linear_grad_weight_rows(hidden_bits, weight_bits, targets, mask, lse, grad_logp, vocab_rows):
+    """Rows ``vocab_rows`` of grad_weight = D^T . h (float64 [len, H]): the
+    same formula as linear_param_grads for a few vocabulary rows."""
+    hb = np.asarray(hidden_bits, dtype=np.uint16)
+    n = hb.shape[0]
+    t = np.asarray(targets, dtype=np.int64).reshape(n)
+    act = _active(mask, n)
+    g = np.asarray(grad_logp, dtype=np.float64).reshape(n)
+    ls = np.asarray(lse, dtype=np.float64).reshape(n)
+    vocab_rows = np.asarray(vocab_rows, dtype=np.int64)
+    h = bf16_to_f64(hb)
+    w = bf16_to_f64(np.asarray(weight_bits, dtype=np.uint16)[vocab_rows])
+    z = h @ w.T                                   # [N, k]
+    d = np.zeros_like(z)
+    rows = np.nonzero(act)[0]
+    d[rows] = -g[rows, None] * np.exp(z[rows] - ls[rows, None])
+    for i in rows:
+        d[i, vocab_rows == t[i]] += g[i]
+    return d.T @ h

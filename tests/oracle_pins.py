@@ -593,3 +593,27 @@ def pin_param_grads_invariants(o):
 
 ALL_PINS += [pin_param_grads_finite_differences, pin_param_grads_closed_forms,
              pin_param_grads_invariants]
+
+
+def pin_param_grad_row_samplers(o):
+    """The per-row samplers used at full sizes agree with the full
+    (finite-difference pinned) parameter gradients."""
+    rng = np.random.default_rng(44)
+    n, v, hh = 9, 70, 16
+    hb = _rand_bf16(rng, (n, hh), 1.0)
+    wb = _rand_bf16(rng, (v, hh), 0.5)
+    t = rng.integers(0, v, size=n)
+    g = rng.standard_normal(n)
+    mask = np.ones(n, dtype=np.uint8)
+    mask[[2, 7]] = 0
+    _, lse = o.linear_logp(hb, wb, t, mask)
+    gh, gw = o.linear_param_grads(hb, wb, t, mask, lse, g)
+    rows = [0, 2, 8]
+    gh_s = o.linear_grad_hidden_rows(hb, wb, t, mask, lse, g, rows, block=16)
+    assert np.max(np.abs(gh_s - gh[rows])) <= 1e-13
+    vr = [int(t[0]), 5, v - 1]
+    gw_s = o.linear_grad_weight_rows(hb, wb, t, mask, lse, g, vr)
+    assert np.max(np.abs(gw_s - gw[vr])) <= 1e-13
+
+
+ALL_PINS += [pin_param_grad_row_samplers]

@@ -140,3 +140,36 @@ def test_token_losses_validation(lib):
     assert f(*args(r=NUL)) == INVALID          # no output at all
     assert f(*args(lo=1.0)) == INVALID
     assert f(*args(beta=-0.1)) == INVALID
+
+
+def test_linear_param_grads_validation(lib):
+    f = lib.rlk_linear_logp_param_grads
+    n, v, h = 300, 1000, 64
+    ws = lib.rlk_linear_logp_param_grads_workspace_size(n, v, h)
+    # transposed hidden [H, N8] + weight chunk [H, C] + D in two layouts
+    c = 1024
+    assert ws >= h * 304 * 2 + h * c * 2 + n * c * 2 + c * 304 * 2
+    assert lib.rlk_linear_logp_param_grads_workspace_size(n, 200000, h) < \
+        lib.rlk_linear_logp_param_grads_workspace_size(n, 20000, h) * 20   # chunked, not [N, V]
+
+    def args(**k):
+        return [k.get("h", A16), k.get("ldh", h), k.get("w", A16), k.get("ldw", h), k.get("t", A16),
+                NUL, k.get("lse", A16), k.get("g", A16), k.get("n", n), k.get("v", v), k.get("H", h),
+                k.get("gh", A16), k.get("ldgh", h), k.get("gw", A16), k.get("ldgw", h),
+                k.get("ws", A16), k.get("wsb", ws), NUL]
+
+    assert f(*args(gh=NUL, gw=NUL)) == INVALID            # nothing requested
+    assert f(*args(n=-1)) == INVALID
+    assert f(*args(v=0)) == INVALID
+    assert f(*args(lse=NUL)) == INVALID
+    assert f(*args(g=NUL)) == INVALID
+    assert f(*args(t=NUL)) == INVALID
+    assert f(*args(ws=NUL)) == INVALID
+    assert f(*args(wsb=ws - 1)) == INVALID                 # workspace too small
+    assert f(*args(ldgh=h - 4)) == INVALID
+    assert f(*args(ldgw=h - 4)) == INVALID
+    assert f(*args(ldgh=h + 2)) == UNSUPPORTED             # ld_gh % 4
+    assert f(*args(gw=A2)) == UNSUPPORTED                  # misaligned output
+    assert f(*args(H=60, ldh=64, ldw=64, ldgh=64, ldgw=64)) == UNSUPPORTED  # H % 8
+    assert f(*args(n=1 << 22)) == UNSUPPORTED              # N beyond the transposed-operand range
+    assert f(*args(ws=A2)) == UNSUPPORTED

@@ -1,0 +1,247 @@
+"""GPU parity and invariance of the fused path's parameter gradients,
+grad_hidden = D . W and grad_weight = D^T . h (D the logits gradient),
+through the C ABI, against the fp64 oracle.
+
+Tolerance.  The pages give none for these outputs, so it is derived from the
+arithmetic: the library rounds each entry of D once to bf16 (relative error
+at most 2^-9) and multiplies on bf16 MFMA with fp32 accumulation.  Per
+element the rounding alone can move grad_hidden[i, k] by at most
+2^-9 * sum_j |D_ij| |W_jk| (and grad_weight[j, k] by 2^-9 * sum_i |D_ij|
+|h_ik|).  The tests allow twice that bound plus 1e-6, which also covers the
+fp32 sums and the fp32 logits and lse feeding D.
+"""
+import json
+
+import numpy as np
+import pytest
+import torch
+
+import invariance as inv
+import invariant_logprob_amd as ilp
+import oracle
+from gpu_util import assert_close, bits16, f32bits, require_gpu
+from invariant_logprob_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+ROUNDING = 2.0 ** -9
+
+
+def tol_from(bound):
+    return 2 * ROUNDING * bound + 1e-6
+
+
+@pytest.fixture(scope="module")
+def dev():
+    d = require_gpu()
+    ilp.load_library()
+    return d
+
+
+def _bits_equal(a, b):
+    return torch.equal(f32bits(a), f32bits(b))
+
+
+def _grads(b, lse, **kw):
+    gh, gw = ilp.linear_logp_param_grads(b.hidden, b.weight, b.targets, lse, b.grad, b.mask, **kw)
+    torch.cuda.synchronize()
+    return gh, gw
+
+
+@pytest.mark.parametrize("n,v,h", [(1, 256, 64), (33, 1000, 256), (300, 17000, 136),
+                                   (257, 513, 8)])
+def test_small_parity(dev, n, v, h):
+    """Several tiles, a ragged token block, a ragged vocabulary chunk (17000
+    = one full 16384 chunk + a partial one) and a ragged K (H = 136)."""
+    b = wl.fused_batch(n, v, h, seed=n + v + h + 1, device=dev, w_sigma=0.05, n_masked=n // 10)
+    _, lse = ilp.linear_logp(b.hidden, b.weight, b.targets, b.mask)
+    gh, gw = _grads(b, lse)
+    hb, wb = bits16(b.hidden), bits16(b.weight)
+    t = b.targets.cpu().numpy()
+    m = b.mask.cpu().numpy()
+    ls = lse.cpu().numpy()
+    g = b.grad.cpu().numpy()
+    rgh, rgw = oracle.linear_param_grads(hb, wb, t, m, ls, g)
+    d_abs = np.abs(oracle.linear_logp_backward(hb, wb, t, m, ls, g))
+    h_abs = np.abs(oracle.bf16_to_f64(hb))
+    w_abs = np.abs(oracle.bf16_to_f64(wb))
+    assert_close(gh.cpu().numpy(), rgh, tol_from(d_abs @ w_abs), f"grad_hidden {n}x{v}x{h}")
+    assert_close(gw.cpu().numpy(), rgw, tol_from(d_abs.T @ h_abs), f"grad_weight {n}x{v}x{h}")
+    inactive = torch.from_numpy(m == 0)
+    assert bool((f32bits(gh)[inactive] == 0).all()), "inactive rows must be +0.0"
+    # one output at a time gives the same bits
+    gh1, none1 = _grads(b, lse, want_weight=False)
+    none2, gw2 = _grads(b, lse, want_hidden=False)
+    assert none1 is None and none2 is None
+    assert _bits_equal(gh1, gh) and _bits_equal(gw2, gw)
+
+
+def test_closed_forms(dev):
+    v, h = 600, 64
+    w = (torch.randn((v, h), device=dev) * 0.5).to(torch.bfloat16)
+    # zero hidden rows: logits 0, p = 1/V, grad_h_i = g_i (W[t_i] - mean_j W_j), grad_W = 0
+    hid = torch.zeros((4, h), dtype=torch.bfloat16, device=dev)
+    t = torch.tensor([0, 17, 300, 599], device=dev)
+    g = torch.tensor([1.0, -2.0, 0.5, 0.0], device=dev)
+    _, lse = ilp.linear_logp(hid, w, t)
+    gh, gw = ilp.linear_logp_param_grads(hid, w, t, lse, g)
+    torch.cuda.synchronize()
+    w64 = w.double().cpu()
+    ref = g.double().cpu()[:, None] * (w64[t.cpu()] - w64.mean(dim=0))
+    # D = g (onehot - 1/V) in bf16: 1/V rounds with relative error 2^-9
+    bound = (g.double().abs().cpu()[:, None] * (w64[t.cpu()].abs() + w64.abs().mean(dim=0)))
+    assert_close(gh.cpu().numpy(), ref.numpy(), tol_from(bound.numpy()), "zero-hidden grad_h")
+    assert float(gw.abs().max()) == 0.0
+    # a row with g = 0 has zero hidden gradient bits
+    assert bool((f32bits(gh[3]) == 0).all())
+
+
+def test_invalid_target_and_empty_batch(dev):
+    v, h = 300, 64
+    b = wl.fused_batch(5, v, h, seed=3, device=dev, w_sigma=0.05)
+    t = b.targets.clone()
+    t[2] = v        # active row with an invalid target
+    _, lse = ilp.linear_logp(b.hidden, b.weight, t)
+    gh, gw = ilp.linear_logp_param_grads(b.hidden, b.weight, t, lse, b.grad)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(gh[2]).all())
+    assert bool(torch.isfinite(gh[[0, 1, 3, 4]]).all())
+    assert bool(torch.isnan(gw).all()), "an invalid active target must poison grad_weight"
+    # N == 0: grad_weight is the empty sum, written as zeros
+    gw0 = torch.full((v, h), float("nan"), device=dev)
+    e = torch.empty((0, h), dtype=torch.bfloat16, device=dev)
+    z = torch.empty((0,), device=dev)
+    ilp.linear_logp_param_grads(e, b.weight, torch.empty((0,), dtype=torch.int64, device=dev), z, z,
+                                want_hidden=False, grad_weight=gw0)
+    torch.cuda.synchronize()
+    assert bool((f32bits(gw0) == 0).all())
+
+
+def test_grad_hidden_transforms(dev):
+    """grad_hidden rows are bitwise invariant under T1-T6 (the harness
+    compares raw bits of every active row)."""
+    n, v, h = 520, 17000, 128
+    b = wl.fused_batch(n, v, h, seed=9, device=dev, w_sigma=0.05, n_masked=30)
+    w = b.weight
+    base = {"x": b.hidden, "targets": b.targets, "mask": b.mask, "grad": b.grad}
+
+    def run(batch):
+        _, lse = ilp.linear_logp(batch["x"], w, batch["targets"], batch["mask"])
+        gh, _ = ilp.linear_logp_param_grads(batch["x"], w, batch["targets"], lse, batch["grad"],
+                                            batch["mask"], want_weight=False)
+        return {"lse": lse, "grad_hidden": gh}
+
+    def filler(k, seed):
+        gg = torch.Generator(device=dev).manual_seed(seed)
+        return {"x": (torch.randn((k, h), generator=gg, device=dev) * 3).to(torch.bfloat16),
+                "targets": torch.randint(0, v, (k,), generator=gg, device=dev),
+                "mask": torch.ones(k, dtype=torch.uint8, device=dev),
+                "grad": torch.randn((k,), generator=gg, device=dev)}
+
+    cases = [("T1", {"size": s, "start": st}, inv.t1_population(base, s, st))
+             for s, st in ((1, 0), (33, 5), (257, 100))]
+    cases += [("T2", {"seed": 1}, inv.t2_position(base, 1)),
+              ("T3", {"keep": "every 7th"}, inv.t3_neighbours(base, list(range(0, n, 7)), filler, 2)),
+              ("T4", {"left": 9, "every": 50}, inv.t4_padding(base, filler, 3, left=9, right=4, every=50)),
+              ("T5", {"chunk": 128}, inv.t5_schedule(base, 128)),
+              ("T6", {"compacted": True}, inv.t6_compacted(base))]
+    failures = []
+    base_out = None
+    for cls, params, (calls, row_map) in cases:
+        man = {"operator": "linear_logp.grad_hidden", "chain_index": 7, "seed": 9,
+               "transform": {"class": cls, "name": inv.TRANSFORM_NAMES[cls], **params}}
+        recs, base_out = inv.check(run, base, calls, row_map, man, base_out)
+        failures += recs
+    assert not failures, json.dumps(failures[:3], indent=1)
+
+
+def test_grad_weight_determinism_and_layouts(dev):
+    """grad_weight sums over the whole batch: bitwise run to run and under
+    masked rows appended after the batch; a permuted batch is another sum
+    order, equal within the derived tolerance."""
+    n, v, h = 400, 3000, 192
+    b = wl.fused_batch(n, v, h, seed=21, device=dev, w_sigma=0.05, n_masked=20)
+    _, lse = ilp.linear_logp(b.hidden, b.weight, b.targets, b.mask)
+    _, gw = _grads(b, lse, want_hidden=False)
+    _, gw_again = _grads(b, lse, want_hidden=False)
+    assert _bits_equal(gw, gw_again)
+    # 77 masked rows with random content and invalid targets after the batch
+    k = 77
+    gg = torch.Generator(device=dev).manual_seed(5)
+    hid2 = torch.cat([b.hidden, (torch.randn((k, h), generator=gg, device=dev) * 3).to(torch.bfloat16)])
+    t2 = torch.cat([b.targets, torch.full((k,), -100, dtype=torch.int64, device=dev)])
+    m2 = torch.cat([b.mask, torch.zeros(k, dtype=torch.uint8, device=dev)])
+    g2 = torch.cat([b.grad, torch.randn((k,), generator=gg, device=dev)])
+    lse2 = torch.cat([lse, torch.zeros(k, device=dev)])
+    _, gw_pad = ilp.linear_logp_param_grads(hid2, b.weight, t2, lse2, g2, m2, want_hidden=False)
+    torch.cuda.synchronize()
+    assert _bits_equal(gw_pad, gw)
+    # permutation: same set of samples, another order of the sum
+    perm = torch.randperm(n, generator=gg, device=dev)
+    _, gw_perm = ilp.linear_logp_param_grads(b.hidden[perm], b.weight, b.targets[perm], lse[perm],
+                                             b.grad[perm], b.mask[perm], want_hidden=False)
+    torch.cuda.synchronize()
+    hb, wb = bits16(b.hidden), bits16(b.weight)
+    d_abs = np.abs(oracle.linear_logp_backward(hb, wb, b.targets.cpu().numpy(), b.mask.cpu().numpy(),
+                                               lse.cpu().numpy(), b.grad.cpu().numpy()))
+    bound = d_abs.T @ np.abs(oracle.bf16_to_f64(hb))
+    assert_close(gw_perm.cpu().numpy(), gw.cpu().numpy().astype(np.float64), 2 * tol_from(bound),
+                 "grad_weight under a permutation")
+
+
+def test_full_size_sampled(dev):
+    """hidden [2048, 5120], W [151936, 5120]: sampled rows of both gradients
+    against the oracle; grad_hidden rows bitwise equal from a 512-row call and
+    from single-row calls."""
+    b = wl.fused_bwd(seed=0, device=dev)
+    n = b.hidden.shape[0]
+    _, lse = ilp.linear_logp(b.hidden, b.weight, b.targets, b.mask)
+    gh, gw = _grads(b, lse)
+    hb, wb = bits16(b.hidden), bits16(b.weight)
+    t = b.targets.cpu().numpy()
+    m = b.mask.cpu().numpy()
+    ls = lse.cpu().numpy()
+    g = b.grad.cpu().numpy()
+    rows = [0, 777, 2047]
+    rgh = oracle.linear_grad_hidden_rows(hb, wb, t, m, ls, g, rows)
+    w64 = oracle.bf16_to_f64(wb)
+    d_rows = oracle.logp_backward_from_f64(oracle.bf16_to_f64(hb[rows]) @ w64.T, t[rows], m[rows],
+                                           ls[rows], g[rows])
+    bound_h = np.abs(d_rows) @ np.abs(w64)
+    del w64
+    assert_close(gh[rows].cpu().numpy(), rgh, tol_from(bound_h), "C5 grad_hidden rows")
+    vrows = sorted({int(t[0]), int(t[1000]), 0, 75000, 151935})
+    rgw = oracle.linear_grad_weight_rows(hb, wb, t, m, ls, g, vrows)
+    h64 = oracle.bf16_to_f64(hb)
+    z = h64 @ oracle.bf16_to_f64(wb[vrows]).T
+    act = m.astype(bool)
+    p = np.exp(z - ls[:, None])
+    onehot = (t[:, None] == np.asarray(vrows)[None, :]).astype(np.float64)
+    d_cols = np.where(act[:, None], g[:, None] * (onehot - p), 0.0)
+    bound_w = np.abs(d_cols).T @ np.abs(h64)
+    assert_close(gw[vrows].cpu().numpy(), rgw, tol_from(bound_w), "C5 grad_weight rows")
+    sl = slice(512, 1024)
+    gh_c, _ = ilp.linear_logp_param_grads(b.hidden[sl], b.weight, b.targets[sl], lse[sl], b.grad[sl],
+                                          b.mask[sl], want_weight=False)
+    torch.cuda.synchronize()
+    assert _bits_equal(gh_c, gh[sl])
+    for r in (0, 777, n - 1):
+        gh_r, _ = ilp.linear_logp_param_grads(b.hidden[r:r + 1], b.weight, b.targets[r:r + 1],
+                                              lse[r:r + 1], b.grad[r:r + 1], b.mask[r:r + 1],
+                                              want_weight=False)
+        torch.cuda.synchronize()
+        assert _bits_equal(gh_r, gh[r:r + 1]), r
+
+
+def test_autograd_wrapper(dev):
+    n, v, h = 70, 900, 64
+    b = wl.fused_batch(n, v, h, seed=4, device=dev, w_sigma=0.05, n_masked=5)
+    hid = b.hidden.clone().requires_grad_(True)
+    w = b.weight.clone().requires_grad_(True)
+    logp = ilp.LinearLogprob.apply(hid, w, b.targets, b.mask)
+    (logp * b.grad).sum().backward()
+    _, lse = ilp.linear_logp(b.hidden, b.weight, b.targets, b.mask)
+    gh, gw = _grads(b, lse)
+    assert hid.grad.dtype == torch.bfloat16 and w.grad.dtype == torch.bfloat16
+    assert torch.equal(hid.grad, gh.to(torch.bfloat16))
+    assert torch.equal(w.grad, gw.to(torch.bfloat16))
