@@ -261,24 +261,39 @@ void linear_tiles_fwd_persistent(TileArgs args) {
     for (int j = 0; j < kJ; ++j) {
       const int tl = wt * kQW + j * 32 + (lane & 31);
       const int64_t tok = cur.tok0 + tl;
+      // Row maximum, then the sum of exponentials in (i, e) order.  A full
+      // vocabulary tile (the common case, a uniform branch) needs no column
+      // test; a ragged last tile skips its columns past V.
       float mx = neg_inf();
-#pragma unroll
-      for (int i = 0; i < kI; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = wv * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-          if (m < cur.V_tail) mx = fmaxf(mx, acc[i][j][e]);
-        }
       float M = neg_inf();
       float s = 0.0f;
-      const float Mu = lse_raise(M, s, mx);
+      if (cur.V_tail >= kBV) {
 #pragma unroll
-      for (int i = 0; i < kI; ++i)
+        for (int i = 0; i < kI; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = wv * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-          if (m < cur.V_tail) s = s + lse_term(acc[i][j][e], Mu);
-        }
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[i][j][e]);
+        const float Mu = lse_raise(M, s, mx);
+#pragma unroll
+        for (int i = 0; i < kI; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s = s + lse_term(acc[i][j][e], Mu);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kI; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int m = wv * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+            if (m < cur.V_tail) mx = fmaxf(mx, acc[i][j][e]);
+          }
+        const float Mu = lse_raise(M, s, mx);
+#pragma unroll
+        for (int i = 0; i < kI; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int m = wv * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+            if (m < cur.V_tail) s = s + lse_term(acc[i][j][e], Mu);
+          }
+      }
       if (tl < cur.N_tail) {
         const int64_t t = tgt[j];
         const int64_t d = t - vwave;
@@ -286,15 +301,10 @@ void linear_tiles_fwd_persistent(TileArgs args) {
           const int dd = static_cast<int>(d);
           const int rem = dd & 31;
           if (((rem >> 2) & 1) == half) {
-            const int it = dd >> 5;
-            const int et = ((rem >> 3) << 2) | (rem & 3);
-            float val = 0.0f;
-#pragma unroll
-            for (int i = 0; i < kI; ++i)
-#pragma unroll
-              for (int e = 0; e < 16; ++e)
-                if (i == it && e == et) val = acc[i][j][e];
-            args.zt[tok] = val;
+            // vocabulary row dd of this wave = block dd >> 5, element
+            // 4 ((dd & 31) >> 3) + (dd & 3)
+            const int idx = 16 * (dd >> 5) + (((rem >> 3) << 2) | (rem & 3));
+            args.zt[tok] = select_acc(acc, j, idx);
           }
         }
       }

@@ -9,7 +9,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/rlk.h"
+#include "rlk.h"
 #include "rlk_internal.hpp"
 
 #ifndef RLK_GIT_REV

@@ -204,6 +204,24 @@ __device__ __forceinline__ void mainloop(uint4* smem, const Loader& L, int wave,
   __syncthreads();
 }
 
+// Element idx = 16 i + e of column block j of the accumulators, for a
+// per-lane idx in [0, 64): a six-level select tree on the bits of idx, so
+// that each level shares one lane mask.
+__device__ __forceinline__ float select_acc(const f32x16_t (&acc)[kI][kJ], int j, int idx) {
+  static_assert(kI * 16 == 64, "select tree is sized for 64 elements per column block");
+  float v[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const int a = 2 * k, b = 2 * k + 1;
+    v[k] = (idx & 1) ? acc[b >> 4][j][b & 15] : acc[a >> 4][j][a & 15];
+  }
+#pragma unroll
+  for (int lvl = 1, n = 16; lvl < 6; ++lvl, n >>= 1)
+#pragma unroll
+    for (int k = 0; k < n; ++k) v[k] = ((idx >> lvl) & 1) ? v[2 * k + 1] : v[2 * k];
+  return v[0];
+}
+
 // Launch-order regrouping: workgroups are dispatched round-robin over the 8
 // XCDs, so ids are first regrouped into contiguous per-XCD ranges; within a
 // range, tiles go by groups of `group` major tiles x all minor tiles, so the
