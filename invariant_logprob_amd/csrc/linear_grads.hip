@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "rlk_device.hpp"
 #include "rlk_internal.hpp"
 #include "tile_core.hpp"
@@ -114,38 +116,43 @@ void grad_dl_tiles(DlArgs a) {
   const int half = lane >> 5;
   // rel[j]: the target's offset from this lane's first vocabulary row
   // (128 wv + 4 (lane >> 5) of the tile), or -1 when outside this wave's rows
-  bool active[kJ], tvalid[kJ];
   int rel[kJ];
-  float ng[kJ], gg[kJ], off[kJ];
+  float ng[kJ], gg[kJ], off[kJ], pz[kJ];
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
     const int tl = wt * kQW + j * 32 + (lane & 31);
     const int64_t tok = tok0 + tl;
-    active[j] = (tl < N_tail) && ((a.mask == nullptr) || (a.mask[tok] != 0));
-    const int64_t t = active[j] ? a.targets[tok] : -1;
-    tvalid[j] = (t >= 0 && t < a.V);
+    const bool active = (tl < N_tail) && ((a.mask == nullptr) || (a.mask[tok] != 0));
+    const int64_t t = active ? a.targets[tok] : -1;
+    const bool tvalid = (t >= 0 && t < a.V);
     const int64_t r = t - (vocab0 + wv * 128 + 4 * half);
     rel[j] = (r >= 0 && r < 128) ? static_cast<int>(r) : -1;
-    gg[j] = active[j] ? a.grad[tok] : 0.0f;
+    gg[j] = active ? a.grad[tok] : 0.0f;
     ng[j] = -gg[j];
-    off[j] = active[j] ? a.lse[tok] * kLog2e : 0.0f;
+    off[j] = active ? a.lse[tok] * kLog2e : 0.0f;
+    pz[j] = (active && !tvalid) ? __builtin_nanf("") : 0.0f;
   }
   // bf16 D of vocabulary rows m0 .. m0 + 3 (m0 = 128 wv + 32 i + 8 q +
   // 4 (lane >> 5)) of token column j, two entries per word.  Evaluated once
   // per staging layout rather than held: the accumulators stay the only
-  // large live state.
-  const float nan = __builtin_nanf("");
+  // large live state.  No branches: p is always evaluated and clamped to be
+  // finite, so a masked row (g = 0) or a column past V (multiplier 0) gives
+  // +0, and an active row with an invalid target carries NaN in the
+  // additive term.
+  // kFull: the tile's 256 vocabulary rows are all < V (every tile but a
+  // ragged last one), so no row test is needed -- a uniform branch picks it.
+  auto epilogue = [&](auto full) {
+  constexpr bool kFull = decltype(full)::value;
   auto dpair = [&](int j, int i, int q) {
     const int m0 = wv * 128 + i * 32 + 8 * q + 4 * half;
     uint32_t b[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float p = fast_exp2(__builtin_fmaf(acc[i][j][4 * q + e], kLog2e, -off[j]));
+      const float p =
+          fminf(fast_exp2(__builtin_fmaf(acc[i][j][4 * q + e], kLog2e, -off[j])), __FLT_MAX__);
       const float add = (i * 32 + 8 * q + e == rel[j]) ? gg[j] : 0.0f;
-      float d = __builtin_fmaf(ng[j], p, add);
-      if (!active[j] || m0 + e >= V_tail) d = 0.0f;
-      else if (!tvalid[j]) d = nan;
-      b[e] = bf16_bits(d);
+      const bool col = kFull || m0 + e < V_tail;
+      b[e] = bf16_bits(__builtin_fmaf(col ? ng[j] : 0.0f, p, col ? add + pz[j] : 0.0f));
     }
     return make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
   };
@@ -210,6 +217,9 @@ void grad_dl_tiles(DlArgs a) {
       }
     }
   }
+  };
+  if (V_tail >= kBP) epilogue(std::true_type{});
+  else epilogue(std::false_type{});
 }
 
 // dst[c][r] = src[r][c] for r < rows, c < cols, and dst[c][r] = 0 for

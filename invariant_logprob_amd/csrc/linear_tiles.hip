@@ -127,6 +127,14 @@ void linear_tiles_bwd(TileArgs args) {
       const float g = active ? args.grad[tok] : 0.0f;
       const float ng = -g;
       const float off = active ? args.lse[tok] * kLog2e : 0.0f;
+      // The target's offset from this lane's first vocabulary row, or -1.
+      const int64_t rt = t - (vwave + 4 * half);
+      const int rel = (rt >= 0 && rt < 128) ? static_cast<int>(rt) : -1;
+      // d = g ([j == t] - p) without branches: p is always evaluated and
+      // clamped to be finite, so a masked row (g = 0, whatever its logits)
+      // gives -0 p + 0 = +0, and an active row with an invalid target
+      // carries NaN in the additive term.
+      const float poison = (active && !tvalid) ? nan : 0.0f;
       float* srow = stage + (lane & 31) * kStageStride;
 #pragma unroll
       for (int i = 0; i < kI; ++i)
@@ -136,11 +144,10 @@ void linear_tiles_bwd(TileArgs args) {
           float d[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float p = fast_exp2(__builtin_fmaf(acc[i][j][4 * q + e], kLog2e, -off));
-            const float add = (static_cast<int64_t>(vwave + m0 + e) == t) ? g : 0.0f;
-            d[e] = __builtin_fmaf(ng, p, add);
-            if (!active) d[e] = 0.0f;
-            else if (!tvalid) d[e] = nan;
+            const float p =
+                fminf(fast_exp2(__builtin_fmaf(acc[i][j][4 * q + e], kLog2e, -off)), __FLT_MAX__);
+            const float add = (i * 32 + 8 * q + e == rel) ? g : 0.0f;
+            d[e] = __builtin_fmaf(ng, p, add + poison);
           }
           *reinterpret_cast<float4*>(srow + m0) = make_float4(d[0], d[1], d[2], d[3]);
         }
