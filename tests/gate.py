@@ -38,11 +38,13 @@ for p in (ROOT, HERE):
 GENERATOR_VERSION = "workloads-1"
 THRESHOLDS = {
     "forward_accuracy": {"logp": "2e-5 + 1e-5|r|", "linear_logp": "2e-3"},
-    "gradient_accuracy": {"logp": "1e-3", "linear_logp": "1e-3"},
+    "gradient_accuracy": {"logp": "1e-3", "linear_logp": "1e-3",
+                          "linear_logp_params": "2^-8 sum|D||W| + 1e-6 (grad_hidden), "
+                                                "2^-8 sum|D||h| + 1e-6 (grad_weight)"},
     "forward_invariance": {"atol": 0.0, "rtol": 0.0},
     "gradient_invariance": {"atol": 0.0, "rtol": 0.0},
 }
-CHAIN_INDEX = {"logp": 8, "linear_logp": 7}
+CHAIN_INDEX = {"logp": 8, "linear_logp": 7, "linear_logp_params": 7}
 
 
 def fixture_id(man):
@@ -83,6 +85,18 @@ def case_list(quick):
                 cases.append({"operator": "linear_logp", "judgment": j, "workload": wl_name,
                               "workload_args": wl_args, "seed": 0,
                               "transform": {"class": t[0], **t[1]}})
+    # parameter gradients of the fused path: accuracy of both outputs; bitwise
+    # invariance of grad_hidden rows; grad_weight over the same complete sample
+    # set (masked rows appended after the batch) bitwise
+    for wl_name, wl_args in fused:
+        cases.append({"operator": "linear_logp_params", "judgment": "gradient_accuracy",
+                      "workload": wl_name, "workload_args": wl_args, "seed": 0})
+        for t in (("T1", {"size": 1, "start": 5}), ("T2", {"seed": 1}),
+                  ("T4", {"left": 3, "right": 1, "every": 40, "seed": 4}), ("T5", {"chunk": 32}),
+                  ("T4", {"left": 0, "right": 9, "every": 0, "seed": 5, "output": "grad_weight"})):
+            cases.append({"operator": "linear_logp_params", "judgment": "gradient_invariance",
+                          "workload": wl_name, "workload_args": wl_args, "seed": 0,
+                          "transform": {"class": t[0], **t[1]}})
     for c in cases:
         c["generator"] = GENERATOR_VERSION
         c["fixture_id"] = fixture_id({k: v for k, v in c.items() if k != "fixture_id"})
@@ -161,8 +175,15 @@ class Runner:
         return f
 
     # -- the operator under test ------------------------------------------
-    def run_op(self, man, shared, batch, backward):
+    def run_op(self, man, shared, batch, backward, want_weight=False):
         ilp = self.ilp
+        if man["operator"] == "linear_logp_params":
+            w = shared["weight"]
+            _, lse = ilp.linear_logp(batch["x"], w, batch["targets"], batch["mask"])
+            gh, gw = ilp.linear_logp_param_grads(batch["x"], w, batch["targets"], lse,
+                                                 batch["grad"], batch["mask"],
+                                                 want_weight=want_weight)
+            return {"grad_weight": gw} if want_weight else {"grad_hidden": gh}
         if man["operator"] == "logp":
             logp, lse = ilp.logp_selected(batch["x"], batch["targets"], batch["mask"])
             out = {"logp": logp, "lse": lse}
@@ -191,6 +212,8 @@ class Runner:
                "chain_index": CHAIN_INDEX[man["operator"]], "judgment": man["judgment"],
                "workload": man["workload"], "workload_args": man["workload_args"],
                "seed": man["seed"], "transform": man.get("transform")}
+        if man["operator"] == "linear_logp_params":
+            return self.run_params_case(man, shared, base, rec)
         if man["judgment"].endswith("accuracy"):
             out = self.run_op(man, shared, base, backward)
             torch.cuda.synchronize()
@@ -273,6 +296,98 @@ class Runner:
         return rec, recs
 
 
+def _params_case(self, man, shared, base, rec):
+    """Parameter gradients: accuracy of grad_hidden and grad_weight against
+    the oracle within the bound derived from the single bf16 rounding of D;
+    invariance of grad_hidden rows (harness) or of grad_weight over the same
+    complete sample set (masked rows appended), bitwise."""
+    import numpy as np
+
+    import invariance as inv
+    import oracle
+    torch = self.torch
+    ilp = self.ilp
+    w = shared["weight"]
+    if man["judgment"] == "gradient_accuracy":
+        _, lse = ilp.linear_logp(base["x"], w, base["targets"], base["mask"])
+        gh, gw = ilp.linear_logp_param_grads(base["x"], w, base["targets"], lse, base["grad"],
+                                             base["mask"])
+        torch.cuda.synchronize()
+        bits = lambda t: t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+        hb, wb = bits(base["x"]), bits(w)
+        t = base["targets"].cpu().numpy()
+        m = base["mask"].cpu().numpy()
+        ls = lse.cpu().numpy()
+        g = base["grad"].cpu().numpy()
+        rgh, rgw = oracle.linear_param_grads(hb, wb, t, m, ls, g)
+        d_abs = np.abs(oracle.linear_logp_backward(hb, wb, t, m, ls, g))
+        bounds = {"grad_hidden": d_abs @ np.abs(oracle.bf16_to_f64(wb)),
+                  "grad_weight": d_abs.T @ np.abs(oracle.bf16_to_f64(hb))}
+        worst = {"max_abs_error": 0.0, "max_rel_error": 0.0, "n_mismatched": 0, "n_compared": 0}
+        first = None
+        for k, got, ref in (("grad_hidden", gh, rgh), ("grad_weight", gw, rgw)):
+            got = got.cpu().numpy().astype(np.float64)
+            err = np.abs(got - ref)
+            bad = ~(err <= 2.0 ** -8 * bounds[k] + 1e-6)
+            worst["max_abs_error"] = max(worst["max_abs_error"], float(np.nanmax(err)))
+            rel = err / np.maximum(np.abs(ref), 1e-30)
+            worst["max_rel_error"] = max(worst["max_rel_error"], float(np.nanmax(rel)))
+            worst["n_mismatched"] += int(bad.sum())
+            worst["n_compared"] += int(bad.size)
+            if bad.any() and first is None:
+                first = {"output": k, "index": [int(i) for i in np.argwhere(bad)[0]]}
+        rec.update(worst)
+        rec.update({"units": "output elements", "first_mismatch": first,
+                    "status": "pass" if worst["n_mismatched"] == 0 else "fail",
+                    "threshold": THRESHOLDS["gradient_accuracy"]["linear_logp_params"]})
+        return rec, []
+    tr = man["transform"]
+    filler = self.filler(man, shared)
+    cls = tr["class"]
+    if cls == "T1":
+        calls, row_map = inv.t1_population(base, tr["size"], tr["start"])
+    elif cls == "T2":
+        calls, row_map = inv.t2_position(base, tr["seed"])
+    elif cls == "T4":
+        calls, row_map = inv.t4_padding(base, filler, tr["seed"], tr["left"], tr["right"],
+                                        tr["every"])
+    elif cls == "T5":
+        calls, row_map = inv.t5_schedule(base, tr["chunk"])
+    else:
+        raise ValueError(cls)
+    manifest = {"operator": man["operator"], "chain_index": CHAIN_INDEX[man["operator"]],
+                "transform": {**tr, "name": inv.TRANSFORM_NAMES[cls]}, "seed": man["seed"],
+                "device": str(self.dev), "direction": "backward",
+                "launch": {"calls": len(calls), "rows": [inv.nrows(c) for c in calls][:4]}}
+    if tr.get("output") == "grad_weight":
+        # the same complete sample set, the padding rows masked: one call each
+        assert len(calls) == 1
+        a = self.run_op(man, shared, base, True, want_weight=True)["grad_weight"]
+        b = self.run_op(man, shared, calls[0], True, want_weight=True)["grad_weight"]
+        torch.cuda.synchronize()
+        ia = a.contiguous().view(torch.int32)
+        ib = b.contiguous().view(torch.int32)
+        diff = (ia != ib)
+        recs = []
+        if bool(diff.any()):
+            first = [int(i) for i in torch.nonzero(diff)[0].cpu()]
+            recs.append({"relation": "I", "status": "fail", "fixture_id": man["fixture_id"],
+                         "operator": man["operator"], "transform": manifest["transform"],
+                         "output": "grad_weight", "n_mismatched": int(diff.sum()),
+                         "units": "output elements", "first_mismatch": first})
+    else:
+        run = lambda bt: self.run_op(man, shared, bt, True)
+        recs, _ = inv.check(run, base, calls, row_map, manifest)
+        for r in recs:
+            r["fixture_id"] = man["fixture_id"]
+    rec.update({"status": "pass" if not recs else "fail",
+                "threshold": THRESHOLDS[man["judgment"]], "n_drift_records": len(recs)})
+    return rec, recs
+
+
+Runner.run_params_case = _params_case
+
+
 def run_gate(quick=False, only=None):
     import torch
     runner = Runner()
@@ -288,7 +403,7 @@ def run_gate(quick=False, only=None):
         results.append(rec)
         drift += recs
     table = {}
-    for op in ("logp", "linear_logp"):
+    for op in ("logp", "linear_logp", "linear_logp_params"):
         for j in ("forward_accuracy", "forward_invariance", "gradient_accuracy", "gradient_invariance"):
             sel = [r for r in results if r["operator"] == op and r["judgment"] == j]
             if sel:

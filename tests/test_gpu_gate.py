@@ -13,6 +13,8 @@ def test_gate_quick_passes():
     for op in ("logp", "linear_logp"):
         assert set(report["judgments"][op]) == {"forward_accuracy", "forward_invariance",
                                                 "gradient_accuracy", "gradient_invariance"}
+    assert set(report["judgments"]["linear_logp_params"]) == {"gradient_accuracy",
+                                                              "gradient_invariance"}
     assert "gfx950" in report["actual_backend"] and report["fallback"] is None
     assert report["drift_records"] == []
     one = report["cases"][5]
