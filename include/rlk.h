@@ -166,10 +166,8 @@ int rlk_logp_backward(const void* logits, int64_t ld, const void* hidden,
 
 /*
  * Bytes of device workspace rlk_linear_logp_param_grads needs for (N, V, H):
- * the transposed hidden [H, N8] (N8 = N rounded up to 8), one chunk of the
- * transposed weight [H, C], and one chunk of the logits gradient in bf16 in
- * both layouts [N, C] and [C, N8], with C = min(16384, V rounded up to 256),
- * each rounded up to 256 bytes.
+ * one vocabulary chunk of the logits gradient in bf16, [N, C] with
+ * C = min(16384, V rounded up to 256), rounded up to 256 bytes.
  */
 size_t rlk_linear_logp_param_grads_workspace_size(int64_t N, int64_t V,
                                                   int64_t H);
@@ -186,7 +184,9 @@ size_t rlk_linear_logp_param_grads_workspace_size(int64_t N, int64_t V,
  * fixed chunks of 16384 entries; per chunk the logits are recomputed with
  * exactly the forward's tiles and K order, D is formed in fp32 as in
  * rlk_logp_backward and rounded once to bf16 -- the MFMA operand type --
- * and both products run on bf16 MFMA with fp32 accumulation.
+ * and both products run on bf16 MFMA with fp32 accumulation; W, hidden and D
+ * are contracted over their rows by reading them through transposing LDS
+ * loads, so nothing is transposed in memory.
  *   grad_hidden: chunk partial products are added in ascending chunk order,
  *     so each row depends on its own token only and is bit-identical for any
  *     batch composition.  Inactive rows are +0.0.

@@ -16,15 +16,14 @@
 //   1. grad_dl_tiles recomputes the chunk's logits with the forward's tile
 //      main loop (bit-identical z), forms D in fp32 exactly as the logits
 //      backward does, rounds it once to bf16 (the MFMA operand type) and
-//      writes it in two layouts: D_c [N, chunk] and D_c^T [chunk, N'].
-//   2. transpose_bf16 writes W_c^T [H, chunk] (the contraction over the
-//      vocabulary needs W with the vocabulary contiguous).
-//   3. grad_gemm_tiles runs both products of the chunk in one launch:
+//      writes D_c [N, chunk].
+//   2. grad_gemm_tiles runs both products of the chunk in one launch:
 //      grad_hidden (+)= D_c . W_c   (K = the chunk's vocabulary, ascending;
 //                                    chunk 0 writes, later chunks add)
 //      grad_weight[c] = D_c^T . h   (K = tokens, ascending)
-// h^T [H, N'] is written once per call.  N' = N rounded up to 8; padding
-// columns hold zeros.
+//      W_c, h and (for the second product) D_c are contracted over their
+//      rows, so those operands are read in their natural K-major layout
+//      through transposing LDS reads: nothing is transposed in memory.
 //
 // Invariance.  A row of grad_hidden depends on its own row of D and on W
 // only, through a K order fixed by V: bit-identical for any batch.  A row of
@@ -79,10 +78,8 @@ struct DlArgs {
   int vt0;        // first vocabulary tile of the chunk
   int n_vt;       // vocabulary tiles in the chunk
   int n_tblocks;  // 256-token blocks
-  uint16_t* d;    // [N][ldd] bf16, chunk-local columns, or null
+  uint16_t* d;    // [N][ldd] bf16, chunk-local columns
   int64_t ldd;
-  uint16_t* dT;   // [n_vt * 256][ldt] bf16, chunk-local rows, or null
-  int64_t ldt;    // N rounded up to 8
 };
 
 // D for one 256-vocabulary x 256-token tile of the chunk.  The main loop is
@@ -161,7 +158,7 @@ void grad_dl_tiles(DlArgs a) {
   // 16-byte pieces of a staged 256 x 256 tile: 32 per row, 16 per thread
   constexpr int kPieces = kBQ * (kBP / 8) / kThreads;
 
-  if (a.d != nullptr) {
+  {
     // S[token][vocab], then whole 512-byte token rows of D_c
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
@@ -185,94 +182,26 @@ void grad_dl_tiles(DlArgs a) {
         *reinterpret_cast<uint4*>(a.d + (tok0 + r) * a.ldd + vtl * kBP + 8 * c) = v;
       }
     }
-    __syncthreads();
-  }
-  if (a.dT != nullptr) {
-    // S[vocab][token], then 512-byte vocabulary rows of D_c^T (tokens past N
-    // up to the padded width are zeros)
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) {
-      const int tl = wt * kQW + j * 32 + (lane & 31);
-#pragma unroll
-      for (int i = 0; i < kI; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int m0 = wv * 128 + i * 32 + 8 * q + 4 * half;
-          const uint2 v = dpair(j, i, q);
-          S[(m0 + 0) * kDlStride + tl] = static_cast<uint16_t>(v.x);
-          S[(m0 + 1) * kDlStride + tl] = static_cast<uint16_t>(v.x >> 16);
-          S[(m0 + 2) * kDlStride + tl] = static_cast<uint16_t>(v.y);
-          S[(m0 + 3) * kDlStride + tl] = static_cast<uint16_t>(v.y >> 16);
-        }
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int it = 0; it < kPieces; ++it) {
-      const int idx = it * kThreads + tid;
-      const int m = idx >> 5;
-      const int c = idx & 31;
-      if (tok0 + 8 * c < a.ldt) {
-        const uint4 v = *reinterpret_cast<const uint4*>(S + m * kDlStride + 8 * c);
-        *reinterpret_cast<uint4*>(a.dT + static_cast<int64_t>(vtl * kBP + m) * a.ldt + tok0 + 8 * c) = v;
-      }
-    }
   }
   };
   if (V_tail >= kBP) epilogue(std::true_type{});
   else epilogue(std::false_type{});
 }
 
-// dst[c][r] = src[r][c] for r < rows, c < cols, and dst[c][r] = 0 for
-// rows <= r < rows_pad.  64 x 64 blocks staged through LDS; cols % 8 == 0,
-// rows_pad % 8 == 0, 16-byte aligned rows on both sides.
-constexpr int kTrTile = 64;
-constexpr int kTrStride = kTrTile + 8;  // bf16 per staged row (16-byte aligned)
-
-__global__ __launch_bounds__(256) void transpose_bf16(const uint16_t* __restrict__ src, int64_t lds,
-                                                      int rows, int cols, uint16_t* __restrict__ dst,
-                                                      int64_t ldd, int rows_pad) {
-  __shared__ uint16_t T[kTrTile * kTrStride];
-  const int r0 = blockIdx.x * kTrTile;
-  const int c0 = blockIdx.y * kTrTile;
-  const int tid = threadIdx.x;
-  // 64 rows x 8 pieces of 8 columns; thread -> (row, piece), two each
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int idx = it * 256 + tid;
-    const int r = idx >> 3;
-    const int p = idx & 7;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r0 + r < rows && c0 + 8 * p < cols)
-      v = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(r0 + r) * lds + c0 + 8 * p);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      T[(8 * p + 2 * k) * kTrStride + r] = static_cast<uint16_t>(w[k]);
-      T[(8 * p + 2 * k + 1) * kTrStride + r] = static_cast<uint16_t>(w[k] >> 16);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int idx = it * 256 + tid;
-    const int c = idx >> 3;
-    const int p = idx & 7;
-    if (c0 + c < cols && r0 + 8 * p < rows_pad) {
-      const uint4 v = *reinterpret_cast<const uint4*>(T + c * kTrStride + 8 * p);
-      *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(c0 + c) * ldd + r0 + 8 * p) = v;
-    }
-  }
-}
-
-// One product of a chunk: out[Q rows][P rows] (+)= Q . P^T over K.
+// One product of a chunk: out[Q rows][P rows] (+)= Q . P^T over K.  Each
+// side is either an operand with one row per tile row and K contiguous, or a
+// K-major operand whose columns are the tile rows (see tile_core.hpp).
 struct GemmOp {
-  const uint16_t* p;  // [P][ldp] bf16, K contiguous: output columns
+  const uint16_t* p;  // P side (output columns)
   int64_t ldp;
-  int P;
-  const uint16_t* q;  // [Q][ldq] bf16, K contiguous: output rows
+  int P;              // tile rows of the P side present
+  int kext_p;         // K-major P: K rows present
+  const uint16_t* q;  // Q side (output rows)
   int64_t ldq;
   int Q;
+  int kext_q;
   int K;
+  int q_kmajor;       // 0: Q one row per output row (grad_hidden); 1: Q K-major (grad_weight)
   float* out;         // [Q][ldo] fp32
   int64_t ldo;
   int accumulate;     // out = out + acc instead of out = acc
@@ -311,11 +240,18 @@ void grad_gemm_tiles(GemmArgs args) {
   const int P_tail = min(g.P - p0, kBP);
   const int Q_tail = min(g.Q - q0, kBQ);
 
-  const __amdgpu_buffer_rsrc_t pres = uniform_rsrc(g.p + static_cast<int64_t>(p0) * g.ldp, P_tail * g.ldp * 2);
-  const __amdgpu_buffer_rsrc_t qres = uniform_rsrc(g.q + static_cast<int64_t>(q0) * g.ldq, Q_tail * g.ldq * 2);
-  const Loader ld = make_loader(wave, lane, g.ldp, g.ldq);
   f32x16_t acc[kI][kJ];
-  mainloop(smem, ld, wave, lane, wp, wq, pres, qres, g.K, acc);
+  // P is K-major in both products (W_c over the vocabulary, h over tokens)
+  const Side Ps{g.p + p0, g.ldp, g.kext_p, p0};
+  if (g.q_kmajor) {
+    const Side Qs{g.q + q0, g.ldq, g.kext_q, q0};
+    const LoaderG<Lay::kCols, Lay::kCols> ld = make_loader_g<Lay::kCols, Lay::kCols>(wave, lane, g.ldp, g.ldq);
+    mainloop_g(smem, ld, wave, lane, wp, wq, Ps, Qs, g.K, acc);
+  } else {
+    const Side Qs{g.q + static_cast<int64_t>(q0) * g.ldq, g.ldq, Q_tail, 0};
+    const LoaderG<Lay::kCols, Lay::kRows> ld = make_loader_g<Lay::kCols, Lay::kRows>(wave, lane, g.ldp, g.ldq);
+    mainloop_g(smem, ld, wave, lane, wp, wq, Ps, Qs, g.K, acc);
+  }
 
   // Staged through LDS one 32-row slice at a time so that each store
   // instruction writes two 512-byte row segments.
@@ -376,29 +312,17 @@ __global__ __launch_bounds__(256) void zero_rows_f32(float* __restrict__ out, in
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 
-struct GradLayout {
-  int64_t Np;         // N rounded up to 8
-  int64_t chunk;      // vocabulary entries per pass (multiple of 256)
-  size_t off_hT, off_wT, off_d, off_dT, total;
-};
-
-GradLayout grad_layout(int64_t N, int64_t V, int64_t H) {
-  GradLayout L;
-  L.Np = round_up(N, 8);
-  L.chunk = min64(kGradChunk, round_up(V, kBP));
-  auto al = [](size_t b) { return (b + 255) / 256 * 256; };
-  L.off_hT = 0;
-  L.off_wT = L.off_hT + al(static_cast<size_t>(H * L.Np * 2));
-  L.off_d = L.off_wT + al(static_cast<size_t>(H * L.chunk * 2));
-  L.off_dT = L.off_d + al(static_cast<size_t>(N * L.chunk * 2));
-  L.total = L.off_dT + al(static_cast<size_t>(L.chunk * L.Np * 2));
-  return L;
+// Workspace: one chunk of D in bf16, [N, chunk].
+size_t grad_workspace(int64_t N, int64_t V) {
+  const int64_t chunk = min64(kGradChunk, round_up(V, kBP));
+  return static_cast<size_t>(round_up(N * chunk * 2, 256));
 }
 
 }  // namespace
 
 size_t linear_param_grads_workspace_bytes(int64_t N, int64_t V, int64_t H) {
-  return grad_layout(N, V, H).total;
+  (void)H;
+  return grad_workspace(N, V);
 }
 
 hipError_t launch_linear_param_grads(const uint16_t* hidden, int64_t ldh, const uint16_t* weight,
@@ -417,35 +341,22 @@ hipError_t launch_linear_param_grads(const uint16_t* hidden, int64_t ldh, const 
     }
     return hipSuccess;
   }
-  const GradLayout L = grad_layout(N, V, H);
-  char* ws = static_cast<char*>(workspace);
-  uint16_t* hT = reinterpret_cast<uint16_t*>(ws + L.off_hT);
-  uint16_t* wT = reinterpret_cast<uint16_t*>(ws + L.off_wT);
-  uint16_t* d = reinterpret_cast<uint16_t*>(ws + L.off_d);
-  uint16_t* dT = reinterpret_cast<uint16_t*>(ws + L.off_dT);
+  uint16_t* d = static_cast<uint16_t*>(workspace);
+  const int64_t chunk = min64(kGradChunk, round_up(V, kBP));
   const bool want_h = grad_hidden != nullptr;
   const bool want_w = grad_weight != nullptr;
   const int n_vtiles = (V + kBP - 1) / kBP;
   const int n_tblocks = static_cast<int>((N + kBQ - 1) / kBQ);
-  const int tiles_per_chunk = static_cast<int>(L.chunk / kBP);
+  const int tiles_per_chunk = static_cast<int>(chunk / kBP);
   const int n_chunks = (n_vtiles + tiles_per_chunk - 1) / tiles_per_chunk;
   const int n_htiles = (H + kBP - 1) / kBP;
 
-  if (want_w) {
-    hipLaunchKernelGGL(transpose_bf16,
-                       dim3(static_cast<uint32_t>(L.Np / kTrTile + (L.Np % kTrTile != 0)),
-                            static_cast<uint32_t>((H + kTrTile - 1) / kTrTile)),
-                       dim3(256), 0, stream, hidden, ldh, static_cast<int>(N), H, hT, L.Np,
-                       static_cast<int>(L.Np));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   for (int c = 0; c < n_chunks; ++c) {
     const int vt0 = c * tiles_per_chunk;
     const int n_vt = static_cast<int>(min64(tiles_per_chunk, n_vtiles - vt0));
     const int vocab0 = vt0 * kBP;
     const int v_rows = static_cast<int>(min64(V - vocab0, n_vt * kBP));  // real vocabulary rows
-    const int width = n_vt * kBP;                     // padded chunk width
+    const int width = n_vt * kBP;                                        // padded chunk width
 
     DlArgs da{};
     da.hidden = hidden;
@@ -462,10 +373,8 @@ hipError_t launch_linear_param_grads(const uint16_t* hidden, int64_t ldh, const 
     da.vt0 = vt0;
     da.n_vt = n_vt;
     da.n_tblocks = n_tblocks;
-    da.d = want_h ? d : nullptr;
-    da.ldd = L.chunk;
-    da.dT = want_w ? dT : nullptr;
-    da.ldt = L.Np;
+    da.d = d;
+    da.ldd = chunk;
     hipLaunchKernelGGL(grad_dl_tiles, dim3(static_cast<uint32_t>(n_vt * n_tblocks)), dim3(kThreads),
                        0, stream, da);
     hipError_t e = hipGetLastError();
@@ -474,21 +383,19 @@ hipError_t launch_linear_param_grads(const uint16_t* hidden, int64_t ldh, const 
     GemmArgs ga{};
     int nblk = 0;
     if (want_h) {
-      hipLaunchKernelGGL(transpose_bf16,
-                         dim3(static_cast<uint32_t>(width / kTrTile),
-                              static_cast<uint32_t>((H + kTrTile - 1) / kTrTile)),
-                         dim3(256), 0, stream, weight + static_cast<int64_t>(vocab0) * ldw, ldw,
-                         v_rows, H, wT, L.chunk, width);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
+      // grad_hidden[N, H] (+)= D_c[N, width] . W_c[width, H]: P = W_c read
+      // K-major (vocabulary rows), Q = D_c rows
       GemmOp& o = ga.op[ga.n_ops++];
-      o.p = wT;
-      o.ldp = L.chunk;
+      o.p = weight + static_cast<int64_t>(vocab0) * ldw;
+      o.ldp = ldw;
       o.P = H;
+      o.kext_p = v_rows;
       o.q = d;
-      o.ldq = L.chunk;
+      o.ldq = chunk;
       o.Q = static_cast<int>(N);
+      o.kext_q = 0;
       o.K = width;
+      o.q_kmajor = 0;
       o.out = grad_hidden;
       o.ldo = ld_gh;
       o.accumulate = c > 0;
@@ -498,14 +405,19 @@ hipError_t launch_linear_param_grads(const uint16_t* hidden, int64_t ldh, const 
       nblk += static_cast<int>(round_up(static_cast<int64_t>(o.n_ptiles) * o.n_qtiles, 8));
     }
     if (want_w) {
+      // grad_weight[vocab rows, H] = D_c^T . h: P = hidden and Q = D_c, both
+      // read K-major (token rows)
       GemmOp& o = ga.op[ga.n_ops++];
-      o.p = hT;
-      o.ldp = L.Np;
+      o.p = hidden;
+      o.ldp = ldh;
       o.P = H;
-      o.q = dT;
-      o.ldq = L.Np;
+      o.kext_p = static_cast<int>(N);
+      o.q = d;
+      o.ldq = chunk;
       o.Q = v_rows;
+      o.kext_q = static_cast<int>(N);
       o.K = static_cast<int>(N);
+      o.q_kmajor = 1;
       o.out = grad_weight + static_cast<int64_t>(vocab0) * ld_gw;
       o.ldo = ld_gw;
       o.accumulate = 0;

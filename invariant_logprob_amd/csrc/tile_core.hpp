@@ -204,6 +204,182 @@ __device__ __forceinline__ void mainloop(uint4* smem, const Loader& L, int wave,
   __syncthreads();
 }
 
+// ---------------------------------------------------------------------------
+// Operands in either layout.  A tile side (P or Q) reads its operand as
+//   Lay::kRows  the side's tile rows are operand rows with K contiguous (the
+//               layout above), or
+//   Lay::kCols  the operand is stored K-major: operand row k holds the side's
+//               tile rows as contiguous columns (W [V, H] contracted over V,
+//               hidden [N, H] or D [N, C] contracted over N).
+// A kCols stage sits in LDS as 64 K rows of 256 entries (512 B), 16-byte
+// chunk c of row k stored at c ^ 4 (k & 3).  Its MFMA fragments come from
+// transposing LDS reads (ds_read_b64_tr_b16): within each 16-lane group, a
+// lane that addresses row kb + s / 4, columns mb + 4 (s % 4) .. + 3 (s = the
+// lane's index in its group) makes lane i of the group receive rows kb .. kb +
+// 3 of column mb + i -- four consecutive K of one tile row, so two such reads
+// give the eight K of a fragment.  The swizzle puts the four rows of a read
+// in four different 64-byte bank ranges.
+
+enum class Lay { kRows, kCols };
+
+// One operand of a tile.  kRows: ptr = the tile's first row, extent = tile
+// rows present (rows past it read as zero).  kCols: ptr = element (k = 0,
+// column col0), the tile's first column; extent = K rows present.  A stage's
+// resource ends where row min(extent, k0 + 64) starts, so nothing past the
+// operand is read: bytes past it read as zero, and columns past the
+// operand's width feed only output entries that are never stored.
+struct Side {
+  const uint16_t* ptr;
+  int64_t ld;
+  int extent;
+  int col0;
+};
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+
+__device__ __forceinline__ int swz_cols(int k, int c) { return c ^ (4 * (k & 3)); }
+
+template <Lay LP, Lay LQ>
+struct LoaderG {
+  int voff_p[kBlkPerWave];
+  int voff_q[kBlkPerWave];
+  int kcol_p[kBlkPerWave];
+  int kcol_q[kBlkPerWave];
+};
+
+template <Lay L>
+__device__ __forceinline__ void lane_offset(int idx, int64_t ld, int& voff, int& kcol) {
+  if constexpr (L == Lay::kRows) {
+    const int r = idx / kRowChunks;
+    const int c = (idx % kRowChunks) ^ ((r >> 1) & 7);
+    kcol = 8 * c;
+    voff = (r * static_cast<int>(ld) + 8 * c) * 2;
+  } else {
+    const int k = idx / 32;  // 32 chunks of 16 bytes per 256-entry row
+    const int c = swz_cols(k, idx % 32);
+    kcol = 0;
+    voff = (k * static_cast<int>(ld) + 8 * c) * 2;
+  }
+}
+
+template <Lay LP, Lay LQ>
+__device__ __forceinline__ LoaderG<LP, LQ> make_loader_g(int wave, int lane, int64_t ldp,
+                                                         int64_t ldq) {
+  LoaderG<LP, LQ> L;
+#pragma unroll
+  for (int q = 0; q < kBlkPerWave; ++q) {
+    const int idx = (wave * kBlkPerWave + q) * 64 + lane;
+    lane_offset<LP>(idx, ldp, L.voff_p[q], L.kcol_p[q]);
+    lane_offset<LQ>(idx, ldq, L.voff_q[q], L.kcol_q[q]);
+  }
+  return L;
+}
+
+// Buffer resource and scalar offset of one side for the stage starting at k0.
+template <Lay L>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t side_rsrc(const Side& s, int k0, int& soff) {
+  if constexpr (L == Lay::kRows) {
+    soff = k0 * 2;
+    return uniform_rsrc(s.ptr, static_cast<int64_t>(s.extent) * s.ld * 2);
+  } else {
+    soff = 0;
+    const int rows = min(max(s.extent - k0, 0), kBK);
+    const int64_t elems = rows > 0 ? static_cast<int64_t>(rows) * s.ld - s.col0 : 0;
+    return uniform_rsrc(s.ptr + static_cast<int64_t>(k0) * s.ld, elems * 2);
+  }
+}
+
+template <int Q0, int Q1, Lay LP, Lay LQ>
+__device__ __forceinline__ void issue_g(uint4* smem, const LoaderG<LP, LQ>& L, int wave,
+                                        const Side& P, const Side& Q, int kt, int st, int K) {
+  const int k0 = kt * kBK;
+  const bool full = (k0 + kBK) <= K;
+  uint4* a = smem + st * kStageVec;
+  uint4* b = a + kPVec;
+  int sp, sq;
+  const __amdgpu_buffer_rsrc_t pres = side_rsrc<LP>(P, k0, sp);
+  const __amdgpu_buffer_rsrc_t qres = side_rsrc<LQ>(Q, k0, sq);
+#pragma unroll
+  for (int q = Q0; q < Q1; ++q) {
+    const int blk = wave * kBlkPerWave + q;
+    int vp = L.voff_p[q], vq = L.voff_q[q];
+    if constexpr (LP == Lay::kRows) {
+      if (!full && (k0 + L.kcol_p[q]) >= K) vp = kOutOfRange;
+    }
+    if constexpr (LQ == Lay::kRows) {
+      if (!full && (k0 + L.kcol_q[q]) >= K) vq = kOutOfRange;
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(pres, to_lds(a + blk * 64), 16, vp, sp, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(qres, to_lds(b + blk * 64), 16, vq, sq, 0, 0);
+  }
+}
+
+// Fragment of 32-row block starting at tile row r0 for 16-deep step kk.
+template <Lay L>
+__device__ __forceinline__ bf16x8_t frag_side(const uint4* base, int kk, int r0, int lane) {
+  if constexpr (L == Lay::kRows) {
+    const int c = 2 * kk + (lane >> 5);
+    const int r = r0 + (lane & 31);
+    return __builtin_bit_cast(bf16x8_t, base[r * kRowChunks + swz(r, c)]);
+  } else {
+    const int g = lane >> 4;
+    const int s = lane & 15;
+    const int m = r0 + 16 * (g & 1) + 4 * (s & 3);
+    const char* bytes = reinterpret_cast<const char*>(base);
+    s16x4_t h[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int k = 16 * kk + 8 * (g >> 1) + 4 * t + (s >> 2);
+      const char* p = bytes + k * 512 + 16 * swz_cols(k, m >> 3) + 2 * (m & 7);
+      h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+    }
+    const uint4 u = make_uint4(__builtin_bit_cast(uint2, h[0]).x, __builtin_bit_cast(uint2, h[0]).y,
+                               __builtin_bit_cast(uint2, h[1]).x, __builtin_bit_cast(uint2, h[1]).y);
+    return __builtin_bit_cast(bf16x8_t, u);
+  }
+}
+
+template <Lay LP, Lay LQ>
+__device__ __forceinline__ void frag_g(const uint4* a, int kk, int wp, int wq, int lane,
+                                       bf16x8_t (&fa)[kI], bf16x8_t (&fb)[kJ]) {
+  const uint4* b = a + kPVec;
+#pragma unroll
+  for (int i = 0; i < kI; ++i) fa[i] = frag_side<LP>(a, kk, wp * kPW + i * 32, lane);
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) fb[j] = frag_side<LQ>(b, kk, wq * kQW + j * 32, lane);
+}
+
+// The main loop of `mainloop` for operands in any layout: same stage order,
+// same double buffering, same MFMA sequence.
+template <Lay LP, Lay LQ>
+__device__ __forceinline__ void mainloop_g(uint4* smem, const LoaderG<LP, LQ>& L, int wave,
+                                           int lane, int wp, int wq, const Side& P, const Side& Q,
+                                           int K, f32x16_t (&acc)[kI][kJ]) {
+  const int n_kt = (K + kBK - 1) / kBK;
+  zero(acc);
+  if (n_kt <= 0) return;
+  issue_g<0, kBlkPerWave>(smem, L, wave, P, Q, 0, 0, K);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    const bool pf = (kt + 1) < n_kt;
+    const int nb = (kt + 1) & 1;
+    const uint4* a = smem + (kt & 1) * kStageVec;
+    bf16x8_t fa0[kI], fb0[kJ], fa1[kI], fb1[kJ];
+    frag_g<LP, LQ>(a, 0, wp, wq, lane, fa0, fb0);
+#pragma unroll
+    for (int kk = 0; kk < kSub; kk += 2) {
+      frag_g<LP, LQ>(a, kk + 1, wp, wq, lane, fa1, fb1);
+      if (kk == 0 && pf) issue_g<0, kBlkPerWave / 2>(smem, L, wave, P, Q, kt + 1, nb, K);
+      mma(acc, fa0, fb0);
+      if (kk + 2 < kSub) frag_g<LP, LQ>(a, kk + 2, wp, wq, lane, fa0, fb0);
+      if (kk == 0 && pf) issue_g<kBlkPerWave / 2, kBlkPerWave>(smem, L, wave, P, Q, kt + 1, nb, K);
+      mma(acc, fa1, fb1);
+    }
+  }
+  __syncthreads();
+}
+
 // Element idx = 16 i + e of column block j of the accumulators, for a
 // per-lane idx in [0, 64): a six-level select tree on the bits of idx, so
 // that each level shares one lane mask.
