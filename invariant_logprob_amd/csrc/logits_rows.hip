@@ -196,6 +196,20 @@ __global__ __launch_bounds__(THREADS) void logp_fwd_rows(
   }
 }
 
+// Column blocks of the elementwise kernels (backward, dense log-softmax).
+// Block L of the N x nb blocks covers row L / nb, 4-column groups
+// [(L mod nb) * THREADS * UNROLL, + THREADS * UNROLL): consecutive blocks
+// walk a row contiguously.  Workgroup ids are regrouped so that the blocks
+// each XCD runs form one contiguous range (workgroups are dispatched
+// round-robin over the 8 XCDs), and a grid-stride loop keeps the grid
+// within launch limits for any N; the grid is a multiple of 8, so every
+// iteration of a workgroup stays on its XCD.  Pure scheduling: each output
+// element depends on its own row only.
+__device__ __forceinline__ int64_t xcd_block(int64_t w, int64_t total) {
+  const int64_t t8 = (total / 8) * 8;
+  return (w < t8) ? (w & 7) * (t8 / 8) + (w >> 3) : w;
+}
+
 // Backward: thread handles groups of 4 columns (an 8-byte bf16 load, a
 // 16-byte fp32 store), so every load and store instruction of a wave covers
 // one contiguous span (512 B read, 1 KB written).
@@ -203,101 +217,111 @@ template <int THREADS, int UNROLL>
 __global__ __launch_bounds__(THREADS) void logp_bwd_rows(
     const uint16_t* __restrict__ logits, int64_t ld, const int64_t* __restrict__ targets,
     const uint8_t* __restrict__ mask, const float* __restrict__ lse,
-    const float* __restrict__ grad, int V, float* __restrict__ dl, int64_t ldg) {
-  const int64_t row = blockIdx.x;
+    const float* __restrict__ grad, int64_t N, int V, int nb, float* __restrict__ dl,
+    int64_t ldg) {
   const int tid = threadIdx.x;
   const int nq = (V + 3) >> 2;                  // 4-column groups
-  const int qbase = blockIdx.y * (THREADS * UNROLL);
-  float* outp = dl + row * ldg;
-  const bool active = (mask == nullptr) || (mask[row] != 0);
-  if (!active) {
+  const int64_t total = N * nb;
+  const float nan = __builtin_nanf("");
+  for (int64_t wid = blockIdx.x; wid < total; wid += gridDim.x) {
+    const int64_t L = xcd_block(wid, total);
+    const int64_t row = L / nb;
+    const int qbase = static_cast<int>(L - row * nb) * (THREADS * UNROLL);
+    float* outp = dl + row * ldg;
+    const bool active = (mask == nullptr) || (mask[row] != 0);
+    if (!active) {
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int q = qbase + u * THREADS + tid;
+        if (q >= nq) break;
+        const int j = 4 * q;
+        if (j + 4 <= V) {
+          store16_stream(outp + j, 0.f, 0.f, 0.f, 0.f);
+        } else {
+          for (int e = 0; j + e < V; ++e) outp[j + e] = 0.0f;
+        }
+      }
+      continue;
+    }
+    const int64_t t = targets[row];
+    const bool tvalid = (t >= 0 && t < V);
+    const float g = grad[row];
+    const float off = lse[row] * kLog2e;
+    const float ng = -g;
+    const uint2* vp = reinterpret_cast<const uint2*>(logits + row * ld);
+    uint2 w[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int q = qbase + u * THREADS + tid;
+      w[u] = make_uint2(kNegInfPair, kNegInfPair);
+      if (q < nq) w[u] = load8_stream(vp + q);
+    }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int q = qbase + u * THREADS + tid;
       if (q >= nq) break;
       const int j = 4 * q;
-      if (j + 4 <= V) {
-        store16_stream(outp + j, 0.f, 0.f, 0.f, 0.f);
-      } else {
-        for (int e = 0; j + e < V; ++e) outp[j + e] = 0.0f;
+      const float x[4] = {bf16_lo(w[u].x), bf16_hi(w[u].x), bf16_lo(w[u].y), bf16_hi(w[u].y)};
+      float d[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d[e] = ng * fast_exp2(__builtin_fmaf(x[e], kLog2e, -off));
+      if (t >= j && t < j + 4) {
+        const int et = static_cast<int>(t - j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e == et) d[e] = __builtin_fmaf(ng, fast_exp2(__builtin_fmaf(x[e], kLog2e, -off)), g);
       }
-    }
-    return;
-  }
-  const int64_t t = targets[row];
-  const bool tvalid = (t >= 0 && t < V);
-  const float g = grad[row];
-  const float off = lse[row] * kLog2e;
-  const float ng = -g;
-  const float nan = __builtin_nanf("");
-  const uint2* vp = reinterpret_cast<const uint2*>(logits + row * ld);
-  uint2 w[UNROLL];
+      if (!tvalid) {
 #pragma unroll
-  for (int u = 0; u < UNROLL; ++u) {
-    const int q = qbase + u * THREADS + tid;
-    w[u] = make_uint2(kNegInfPair, kNegInfPair);
-    if (q < nq) w[u] = load8_stream(vp + q);
-  }
-#pragma unroll
-  for (int u = 0; u < UNROLL; ++u) {
-    const int q = qbase + u * THREADS + tid;
-    if (q >= nq) break;
-    const int j = 4 * q;
-    const float x[4] = {bf16_lo(w[u].x), bf16_hi(w[u].x), bf16_lo(w[u].y), bf16_hi(w[u].y)};
-    float d[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) d[e] = ng * fast_exp2(__builtin_fmaf(x[e], kLog2e, -off));
-    if (t >= j && t < j + 4) {
-      const int et = static_cast<int>(t - j);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (e == et) d[e] = __builtin_fmaf(ng, fast_exp2(__builtin_fmaf(x[e], kLog2e, -off)), g);
-    }
-    if (!tvalid) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) d[e] = nan;
-    }
-    if (j + 4 <= V) {
-      store16_stream(outp + j, d[0], d[1], d[2], d[3]);
-    } else {
-      for (int e = 0; j + e < V; ++e) outp[j + e] = d[e];
+        for (int e = 0; e < 4; ++e) d[e] = nan;
+      }
+      if (j + 4 <= V) {
+        store16_stream(outp + j, d[0], d[1], d[2], d[3]);
+      } else {
+        for (int e = 0; j + e < V; ++e) outp[j + e] = d[e];
+      }
     }
   }
 }
 
 // Dense log-softmax rows out[i, j] = x_ij - lse_i, with the backward's
-// access pattern (8-byte loads, 16-byte stores, 8192 columns per block).
+// access pattern and block order.
 template <int THREADS, int UNROLL>
 __global__ __launch_bounds__(THREADS) void log_softmax_rows(
     const uint16_t* __restrict__ logits, int64_t ld, const uint8_t* __restrict__ mask,
-    const float* __restrict__ lse, int V, float* __restrict__ out, int64_t ldo) {
-  const int64_t row = blockIdx.x;
+    const float* __restrict__ lse, int64_t N, int V, int nb, float* __restrict__ out,
+    int64_t ldo) {
   const int tid = threadIdx.x;
   const int nq = (V + 3) >> 2;
-  const int qbase = blockIdx.y * (THREADS * UNROLL);
-  float* outp = out + row * ldo;
-  const bool active = (mask == nullptr) || (mask[row] != 0);
-  const float l = active ? lse[row] : 0.0f;
-  const uint2* vp = reinterpret_cast<const uint2*>(logits + row * ld);
-  uint2 w[UNROLL];
+  const int64_t total = N * nb;
+  for (int64_t wid = blockIdx.x; wid < total; wid += gridDim.x) {
+    const int64_t L = xcd_block(wid, total);
+    const int64_t row = L / nb;
+    const int qbase = static_cast<int>(L - row * nb) * (THREADS * UNROLL);
+    float* outp = out + row * ldo;
+    const bool active = (mask == nullptr) || (mask[row] != 0);
+    const float l = active ? lse[row] : 0.0f;
+    const uint2* vp = reinterpret_cast<const uint2*>(logits + row * ld);
+    uint2 w[UNROLL];
 #pragma unroll
-  for (int u = 0; u < UNROLL; ++u) {
-    const int q = qbase + u * THREADS + tid;
-    w[u] = make_uint2(0u, 0u);
-    if (active && q < nq) w[u] = load8_stream(vp + q);
-  }
+    for (int u = 0; u < UNROLL; ++u) {
+      const int q = qbase + u * THREADS + tid;
+      w[u] = make_uint2(0u, 0u);
+      if (active && q < nq) w[u] = load8_stream(vp + q);
+    }
 #pragma unroll
-  for (int u = 0; u < UNROLL; ++u) {
-    const int q = qbase + u * THREADS + tid;
-    if (q >= nq) break;
-    const int j = 4 * q;
-    float d[4] = {bf16_lo(w[u].x) - l, bf16_hi(w[u].x) - l, bf16_lo(w[u].y) - l,
-                  bf16_hi(w[u].y) - l};
-    if (!active) d[0] = d[1] = d[2] = d[3] = 0.0f;
-    if (j + 4 <= V) {
-      store16_stream(outp + j, d[0], d[1], d[2], d[3]);
-    } else {
-      for (int e = 0; j + e < V; ++e) outp[j + e] = d[e];
+    for (int u = 0; u < UNROLL; ++u) {
+      const int q = qbase + u * THREADS + tid;
+      if (q >= nq) break;
+      const int j = 4 * q;
+      float d[4] = {bf16_lo(w[u].x) - l, bf16_hi(w[u].x) - l, bf16_lo(w[u].y) - l,
+                    bf16_hi(w[u].y) - l};
+      if (!active) d[0] = d[1] = d[2] = d[3] = 0.0f;
+      if (j + 4 <= V) {
+        store16_stream(outp + j, d[0], d[1], d[2], d[3]);
+      } else {
+        for (int e = 0; j + e < V; ++e) outp[j + e] = d[e];
+      }
     }
   }
 }
@@ -308,8 +332,11 @@ __global__ __launch_bounds__(THREADS) void log_softmax_rows(
 // reduction order; they are part of the build identity.
 constexpr int kRowThreads = 256;
 constexpr int kRowUnroll = 8;
-constexpr int kBwdThreads = 256;
-constexpr int kBwdUnroll = 8;
+constexpr int kBwdThreads = 128;
+constexpr int kBwdUnroll = 4;
+// Upper bound on the elementwise kernels' grid (a multiple of 8); larger
+// problems loop.
+constexpr int64_t kBwdMaxGrid = int64_t(1) << 22;
 
 int logits_schedule_threads() { return kRowThreads; }
 int logits_schedule_unroll() { return kRowUnroll; }
@@ -329,15 +356,19 @@ hipError_t launch_logp_fwd_rows(const uint16_t* logits, int64_t ld, const int64_
   return hipGetLastError();
 }
 
+static uint32_t elementwise_grid(int64_t total) {
+  return static_cast<uint32_t>(total < kBwdMaxGrid ? total : kBwdMaxGrid);
+}
+
 hipError_t launch_logp_bwd_rows(const uint16_t* logits, int64_t ld, const int64_t* targets,
                                 const uint8_t* mask, const float* lse, const float* grad, int64_t N,
                                 int V, float* dl, int64_t ldg, hipStream_t stream) {
   const int nq = (V + 3) / 4;
   const int per_block = kBwdThreads * kBwdUnroll;
-  const int nblk = (nq + per_block - 1) / per_block;
-  hipLaunchKernelGGL((logp_bwd_rows<kBwdThreads, kBwdUnroll>),
-                     dim3(static_cast<uint32_t>(N), static_cast<uint32_t>(nblk)), dim3(kBwdThreads),
-                     0, stream, logits, ld, targets, mask, lse, grad, V, dl, ldg);
+  const int nb = (nq + per_block - 1) / per_block;
+  hipLaunchKernelGGL((logp_bwd_rows<kBwdThreads, kBwdUnroll>), dim3(elementwise_grid(N * nb)),
+                     dim3(kBwdThreads), 0, stream, logits, ld, targets, mask, lse, grad, N, V, nb,
+                     dl, ldg);
   return hipGetLastError();
 }
 
@@ -346,10 +377,9 @@ hipError_t launch_log_softmax_rows(const uint16_t* logits, int64_t ld, const uin
                                    hipStream_t stream) {
   const int nq = (V + 3) / 4;
   const int per_block = kBwdThreads * kBwdUnroll;
-  const int nblk = (nq + per_block - 1) / per_block;
-  hipLaunchKernelGGL((log_softmax_rows<kBwdThreads, kBwdUnroll>),
-                     dim3(static_cast<uint32_t>(N), static_cast<uint32_t>(nblk)), dim3(kBwdThreads),
-                     0, stream, logits, ld, mask, lse, V, out, ldo);
+  const int nb = (nq + per_block - 1) / per_block;
+  hipLaunchKernelGGL((log_softmax_rows<kBwdThreads, kBwdUnroll>), dim3(elementwise_grid(N * nb)),
+                     dim3(kBwdThreads), 0, stream, logits, ld, mask, lse, N, V, nb, out, ldo);
   return hipGetLastError();
 }
 
