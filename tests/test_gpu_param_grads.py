@@ -245,3 +245,32 @@ def test_autograd_wrapper(dev):
     assert hid.grad.dtype == torch.bfloat16 and w.grad.dtype == torch.bfloat16
     assert torch.equal(hid.grad, gh.to(torch.bfloat16))
     assert torch.equal(w.grad, gw.to(torch.bfloat16))
+
+
+def test_padded_leading_dimensions(dev):
+    """hidden and weight as views of wider buffers (ld = H + 24, + 8), and
+    outputs with ld = H + 12: the K-major operand reads follow the leading
+    dimensions, and the results equal those of contiguous copies bit for bit."""
+    n, v, h = 150, 1700, 200
+    b = wl.fused_batch(n, v, h, seed=17, device=dev, w_sigma=0.05, n_masked=11)
+    hb = torch.full((n, h + 24), float("nan"), device=dev).to(torch.bfloat16)
+    hb[:, :h] = b.hidden
+    wb = torch.full((v, h + 8), float("nan"), device=dev).to(torch.bfloat16)
+    wb[:, :h] = b.weight
+    hid, wei = hb[:, :h], wb[:, :h]
+    logp, lse = ilp.linear_logp(b.hidden, b.weight, b.targets, b.mask)
+    gh, gw = _grads(b, lse)
+    # the forward and the logits backward on the padded views give the same bits
+    logp2, lse2 = ilp.linear_logp(hid, wei, b.targets, b.mask)
+    d = ilp.linear_logp_backward(b.hidden, b.weight, b.targets, lse, b.grad, b.mask)
+    d2 = ilp.linear_logp_backward(hid, wei, b.targets, lse, b.grad, b.mask)
+    torch.cuda.synchronize()
+    assert _bits_equal(logp2, logp) and _bits_equal(lse2, lse) and _bits_equal(d2, d)
+    gh_buf = torch.full((n, h + 12), float("nan"), device=dev)
+    gw_buf = torch.full((v, h + 12), float("nan"), device=dev)
+    gh2, gw2 = ilp.linear_logp_param_grads(hid, wei, b.targets, lse, b.grad, b.mask,
+                                           grad_hidden=gh_buf[:, :h], grad_weight=gw_buf[:, :h])
+    torch.cuda.synchronize()
+    assert _bits_equal(gh2, gh) and _bits_equal(gw2, gw)
+    # columns past H of the output buffers are never written
+    assert bool(torch.isnan(gh_buf[:, h:]).all()) and bool(torch.isnan(gw_buf[:, h:]).all())
