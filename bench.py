@@ -42,7 +42,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--legs", default="logits_fwd,logits_bwd,fused_fwd,fused_fb")
     p.add_argument("--extra-legs",
-                   default="logits_entropy,log_softmax,token_losses,fused_param_grads",
+                   default="logits_entropy,log_softmax,token_losses,fused_param_grads,fused_fb_kept_logits",
                    help="rows beyond the hot path, timed after the steps (not part of a step)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="instead of the hot path, run a plain 1 GiB device copy 5 times "
@@ -245,6 +245,15 @@ def main():
                                                 workspace=wsg5),
             n5 * h5 * 2 + v5 * h5 * 2 + n5 * h5 * 4 + v5 * h5 * 4)
         xflops["fused_param_grads"] = 3 * 2.0 * n5 * v5 * h5
+    if c5 is not None and "fused_fb_kept_logits" in args.extra_legs.split(","):
+        # the fwd+bwd workload with the forward keeping its fp32 logits and the
+        # backward computed from them in place (one projection, 2 N V H flops)
+        def kept():
+            ilp.linear_logp_with_logits(c5.hidden, c5.weight, c5.targets, c5.mask, workspace=ws5,
+                                        logp=logp5, lse=lse5, logits=d5)
+            ilp.logp_backward(d5, c5.targets, lse5, c5.grad, c5.mask, out=d5)
+        xfns["fused_fb_kept_logits"] = (kept, n5 * h5 * 2 + v5 * h5 * 2 + 2 * n5 * v5 * 4 * 2)
+        xflops["fused_fb_kept_logits"] = 2.0 * n5 * v5 * h5
     for name in [x for x in args.extra_legs.split(",") if x in xfns]:
         fn, nbytes = xfns[name]
         for _ in range(max(1, args.warmup)):

@@ -165,6 +165,48 @@ int rlk_logp_backward(const void* logits, int64_t ld, const void* hidden,
                       hipStream_t stream);
 
 /*
+ * The fused forward of rlk_linear_logp that also keeps its fp32 logits, for
+ * callers that trade N x V x 4 bytes of device memory for a backward without
+ * the second projection (the pages' "linear_logp" with its backward, as in
+ * rlk_logp_backward's fused mode; page "[WS1 Test] ...", section
+ * "Workstream 3 - #153").  logp, lse and the workspace are exactly as in
+ * rlk_linear_logp, and logp and lse are bit-identical to its outputs.
+ *   logits : fp32 [N, ld_z] (ld_z >= V, ld_z % 4 == 0, 16-B aligned), caller
+ *            owned: z_ij = W_j . h_i for every row i < N, masked or not (the
+ *            projection does not read the mask), columns j < V; columns
+ *            >= V are not written.  Each value is bit-identical to the
+ *            logit the fused backward recomputes for that element.
+ */
+int rlk_linear_logp_with_logits(const void* hidden, int64_t ld_h,
+                                const void* weight, int64_t ld_w,
+                                const int64_t* targets, const uint8_t* mask,
+                                int64_t N, int64_t V, int64_t H, float* logp,
+                                float* lse, float* logits, int64_t ld_z,
+                                void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
+ * Backward of the selected logprob from fp32 logits (normally those
+ * rlk_linear_logp_with_logits kept):
+ *   grad_logits[i, j] = grad_logp[i] * ([j == t_i] - exp(x_ij - lse_i)),
+ * with the per-element arithmetic of rlk_logp_backward's fused mode, so
+ * that for the same logits and lse the two outputs are bit-identical.
+ *   logits      : fp32 [N, ld] (ld >= V, ld % 4 == 0, 16-B aligned); rows
+ *                 hold ld elements; inactive rows are not read.
+ *   grad_logits : fp32 [N, ld_g], same constraints; columns >= V are not
+ *                 written; inactive rows are written as +0.0.  It may be
+ *                 `logits` itself with ld_g == ld (in place); any other
+ *                 overlap of the two is RLK_ERR_INVALID_ARG.
+ *   lse, grad_logp, targets, mask: as in rlk_logp_backward.  An active row
+ *                 with a target outside [0, V) gets NaN in every entry.
+ */
+int rlk_logp_backward_f32(const float* logits, int64_t ld,
+                          const int64_t* targets, const uint8_t* mask,
+                          const float* lse, const float* grad_logp, int64_t N,
+                          int64_t V, float* grad_logits, int64_t ld_g,
+                          hipStream_t stream);
+
+/*
  * Bytes of device workspace rlk_linear_logp_param_grads needs for (N, V, H):
  * one vocabulary chunk of the logits gradient in bf16, [N, C] with
  * C = min(16384, V rounded up to 256), rounded up to 256 bytes.

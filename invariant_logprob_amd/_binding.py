@@ -55,6 +55,11 @@ def load_library():
     lib.rlk_logp_backward.argtypes = [vp, i64, vp, i64, vp, i64, i64, vp, vp, vp, vp, i64, i64, vp,
                                       i64, vp]
     lib.rlk_logp_backward.restype = ctypes.c_int
+    lib.rlk_linear_logp_with_logits.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, vp, vp,
+                                                vp, i64, vp, sz, vp]
+    lib.rlk_linear_logp_with_logits.restype = ctypes.c_int
+    lib.rlk_logp_backward_f32.argtypes = [vp, i64, vp, vp, vp, vp, i64, i64, vp, i64, vp]
+    lib.rlk_logp_backward_f32.restype = ctypes.c_int
     lib.rlk_linear_logp_param_grads_workspace_size.argtypes = [i64, i64, i64]
     lib.rlk_linear_logp_param_grads_workspace_size.restype = sz
     lib.rlk_linear_logp_param_grads.argtypes = [vp, i64, vp, i64, vp, vp, vp, vp, i64, i64, i64, vp,
@@ -93,7 +98,7 @@ def _device_of(t, name):
     return t.device
 
 
-def _matrix(t, name, dtype):
+def _matrix(t, name, dtype, read=True):
     _device_of(t, name)
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
@@ -102,9 +107,20 @@ def _matrix(t, name, dtype):
     if t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must have unit stride along its last dimension")
     if t.shape[0] > 1:
-        return t.stride(0)
-    # a single row is never addressed through its leading dimension
-    return (t.shape[1] + 7) // 8 * 8
+        ld = t.stride(0)
+    else:
+        # a single row: any leading dimension the library accepts will do
+        # (a multiple of 8 bf16 or 4 fp32 elements, 16 bytes)
+        mult = 16 // t.element_size()
+        ld = (t.shape[1] + mult - 1) // mult * mult
+    # The library reads input rows in whole aligned groups up to ld, the last
+    # row included, so the storage must hold all of it.
+    if read and t.numel() > 0:
+        end = (t.storage_offset() + (t.shape[0] - 1) * ld + ld) * t.element_size()
+        if end > t.untyped_storage().nbytes():
+            raise ValueError(f"{name}: the storage must hold {ld} elements in every row, the last "
+                             f"one included (pad the rows to a multiple of 8 elements)")
+    return ld
 
 
 def _rows(t, name, n, dtype):
@@ -261,20 +277,62 @@ def linear_logp(hidden, weight, targets, mask=None, *, workspace=None, logp=None
     return logp, lse
 
 
-def _grad_out(out, n, v, dev):
+def linear_logp_with_logits(hidden, weight, targets, mask=None, *, workspace=None, logp=None,
+                            lse=None, logits=None):
+    """The fused forward that also keeps its fp32 logits z = hidden . weight^T
+    (every row, masked or not), for a backward without the second
+    projection: logp_backward(logits, ...).  Returns (logp, lse, logits);
+    logp and lse are bit-identical to linear_logp's."""
+    lib = load_library()
+    ldh = _matrix(hidden, "hidden", torch.bfloat16)
+    ldw = _matrix(weight, "weight", torch.bfloat16)
+    n, h = hidden.shape
+    v, h2 = weight.shape
+    if h != h2:
+        raise ValueError(f"hidden has H={h} but weight has H={h2}")
+    _rows(targets, "targets", n, torch.int64)
+    mask = _mask(mask, n)
+    dev = _same_device(hidden, weight, targets, mask)
+    if logp is None:
+        logp = torch.empty(n, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(n, dtype=torch.float32, device=dev)
+    logits, ldz = _grad_out(logits, n, v, dev, "logits")
+    if n == 0:
+        return logp, lse, logits
+    need = linear_logp_workspace_size(n, v, h)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace too small: need {need} bytes")
+    with torch.cuda.device(dev):
+        st = lib.rlk_linear_logp_with_logits(
+            _ptr(hidden), ldh, _ptr(weight), ldw, _ptr(targets), _ptr(mask), n, v, h, _ptr(logp),
+            _ptr(lse), _ptr(logits), ldz, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(dev))
+    _raise(st, "rlk_linear_logp_with_logits")
+    return logp, lse, logits
+
+
+def _grad_out(out, n, v, dev, name="out"):
     if out is None:
         ldg = (v + 3) // 4 * 4
         buf = torch.empty((n, ldg), dtype=torch.float32, device=dev)
         return buf[:, :v], ldg
-    ldg = _matrix(out, "out", torch.float32)
+    ldg = _matrix(out, name, torch.float32, read=False)
     if tuple(out.shape) != (n, v):
-        raise ValueError(f"out must have shape ({n}, {v})")
+        raise ValueError(f"{name} must have shape ({n}, {v})")
     return out, ldg
 
 
 def logp_backward(logits, targets, lse, grad_logp, mask=None, *, out=None):
-    """d(sum_i g_i logp_i)/d logits from bf16 logits [N, V]: float32 [N, V]."""
+    """d(sum_i g_i logp_i)/d logits: float32 [N, V].  From bf16 logits [N, V],
+    or from the fp32 logits linear_logp_with_logits keeps (then the result is
+    bit-identical to linear_logp_backward's, and `out` may be `logits` itself
+    to compute in place)."""
     lib = load_library()
+    if isinstance(logits, torch.Tensor) and logits.dtype == torch.float32:
+        return _logp_backward_f32(lib, logits, targets, lse, grad_logp, mask, out)
     ld = _matrix(logits, "logits", torch.bfloat16)
     n, v = logits.shape
     _rows(targets, "targets", n, torch.int64)
@@ -289,6 +347,24 @@ def logp_backward(logits, targets, lse, grad_logp, mask=None, *, out=None):
         st = lib.rlk_logp_backward(_ptr(logits), ld, None, 0, None, 0, 0, _ptr(targets), _ptr(mask),
                                    _ptr(lse), _ptr(grad_logp), n, v, _ptr(out), ldg, _stream(dev))
     _raise(st, "rlk_logp_backward")
+    return out
+
+
+def _logp_backward_f32(lib, logits, targets, lse, grad_logp, mask, out):
+    ld = _matrix(logits, "logits", torch.float32)
+    n, v = logits.shape
+    _rows(targets, "targets", n, torch.int64)
+    _rows(lse, "lse", n, torch.float32)
+    _rows(grad_logp, "grad_logp", n, torch.float32)
+    mask = _mask(mask, n)
+    dev = _same_device(logits, targets, lse, grad_logp, mask)
+    out, ldg = _grad_out(out, n, v, dev)
+    if n == 0:
+        return out
+    with torch.cuda.device(dev):
+        st = lib.rlk_logp_backward_f32(_ptr(logits), ld, _ptr(targets), _ptr(mask), _ptr(lse),
+                                       _ptr(grad_logp), n, v, _ptr(out), ldg, _stream(dev))
+    _raise(st, "rlk_logp_backward_f32")
     return out
 
 
@@ -325,7 +401,7 @@ def linear_logp_param_grads_workspace_size(n, v, h):
 def _param_out(out, rows, cols, dev, name):
     if out is None:
         return torch.empty((rows, cols), dtype=torch.float32, device=dev), cols
-    ld = _matrix(out, name, torch.float32)
+    ld = _matrix(out, name, torch.float32, read=False)
     if tuple(out.shape) != (rows, cols):
         raise ValueError(f"{name} must have shape ({rows}, {cols})")
     return out, ld

@@ -66,6 +66,8 @@ struct TileArgs {
   // forward outputs
   float2* part;   // [N][n_vtiles] (M, s)
   float* zt;      // [N] target logit
+  float* logits;  // [N][ldz] fp32 logits, written by the storing forward only
+  int64_t ldz;
   // backward inputs / output
   const float* lse;
   const float* grad;
@@ -181,7 +183,9 @@ void linear_tiles_bwd(TileArgs args) {
 // next tile's first K stage is in flight during this tile's last stage and
 // its epilogue.  The per-tile arithmetic (copies, MFMA sequence and K order)
 // is the same as linear_tiles_bwd's, so the backward recomputes the very same
-// logits.
+// logits.  With kStoreLogits the epilogue also writes the tile's fp32 logits
+// (every row below N, every column below V), straight from the accumulators.
+template <bool kStoreLogits>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void linear_tiles_fwd_persistent(TileArgs args) {
   __shared__ uint4 smem[2 * kStageVec];
@@ -264,6 +268,39 @@ void linear_tiles_fwd_persistent(TileArgs args) {
     const int half = lane >> 5;
     const int vwave = cur.vocab0 + wv * 128;
     float2* red = reinterpret_cast<float2*>(smem + free_buf * kStageVec);
+    if constexpr (kStoreLogits) {
+      // Lane (l, l + 32) pairs write 32 contiguous bytes of a token's row; the
+      // four q steps of a block complete 128-byte lines.  The lane index and
+      // the row stride are opaque to the compiler here, or it hoists these
+      // per-lane offsets out of the tile loop, past the register budget.
+      int zl = lane;
+      asm volatile("" : "+v"(zl));
+      int64_t ldz = args.ldz;
+      asm volatile("" : "+s"(ldz));
+      const int zhalf = zl >> 5;
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        const int tl = wt * kQW + j * 32 + (zl & 31);
+        if (tl < cur.N_tail) {
+          float* zrow = args.logits + (cur.tok0 + tl) * ldz + vwave + 4 * zhalf;
+#pragma unroll
+          for (int i = 0; i < kI; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int m = wv * 128 + i * 32 + 8 * q + 4 * zhalf;  // column - vocab0
+              float* dst = zrow + i * 32 + 8 * q;
+              if (m + 4 <= cur.V_tail) {
+                *reinterpret_cast<float4*>(dst) = make_float4(
+                    acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if (m + e < cur.V_tail) dst[e] = acc[i][j][4 * q + e];
+              }
+            }
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
       const int tl = wt * kQW + j * 32 + (lane & 31);
@@ -411,8 +448,8 @@ size_t linear_workspace_bytes(int64_t N, int64_t V) {
 
 hipError_t launch_linear_logp(const uint16_t* hidden, int64_t ldh, const uint16_t* weight,
                               int64_t ldw, const int64_t* targets, const uint8_t* mask, int64_t N,
-                              int V, int H, float* logp, float* lse, void* workspace,
-                              hipStream_t stream) {
+                              int V, int H, float* logp, float* lse, float* logits, int64_t ldz,
+                              void* workspace, hipStream_t stream) {
   TileArgs a = make_args(hidden, ldh, weight, ldw, targets, mask, N, V, H);
   const int64_t n_vtiles = a.n_vtiles;
   const size_t part_bytes = ((static_cast<size_t>(n_vtiles) * N * sizeof(float2) + 255) / 256) * 256;
@@ -430,8 +467,14 @@ hipError_t launch_linear_logp(const uint16_t* hidden, int64_t ldh, const uint16_
       cus = n;
   }
   const int64_t grid = tiles < cus ? tiles : cus;
-  hipLaunchKernelGGL(linear_tiles_fwd_persistent, dim3(static_cast<uint32_t>(grid)), dim3(kThreads),
-                     0, stream, a);
+  a.logits = logits;
+  a.ldz = ldz;
+  if (logits != nullptr)
+    hipLaunchKernelGGL(linear_tiles_fwd_persistent<true>, dim3(static_cast<uint32_t>(grid)),
+                       dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(linear_tiles_fwd_persistent<false>, dim3(static_cast<uint32_t>(grid)),
+                       dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(lse_chunk_combine,

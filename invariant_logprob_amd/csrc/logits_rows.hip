@@ -284,6 +284,76 @@ __global__ __launch_bounds__(THREADS) void logp_bwd_rows(
   }
 }
 
+// The backward from fp32 logits (the storing fused forward's output), with
+// the access pattern and block order of logp_bwd_rows and the per-element
+// arithmetic of the fused backward's epilogue:
+//   d = fma(-g, min(2^(fma(x, log2 e, -lse log2 e)), FLT_MAX), [j == t] g + poison)
+// so that for the same logits and lse its output is bit-identical to the
+// fused backward's.  A lane reads all of its elements before it writes any,
+// and lanes own disjoint elements, so logits and dl may be one buffer.
+template <int THREADS, int UNROLL>
+__global__ __launch_bounds__(THREADS) void logp_bwd_rows_f32(
+    const float* logits, int64_t ld, const int64_t* __restrict__ targets,
+    const uint8_t* __restrict__ mask, const float* __restrict__ lse,
+    const float* __restrict__ grad, int64_t N, int V, int nb, float* dl, int64_t ldg) {
+  const int tid = threadIdx.x;
+  const int nq = (V + 3) >> 2;                  // 4-column groups
+  const int64_t total = N * nb;
+  const float nan = __builtin_nanf("");
+  for (int64_t wid = blockIdx.x; wid < total; wid += gridDim.x) {
+    const int64_t L = xcd_block(wid, total);
+    const int64_t row = L / nb;
+    const int qbase = static_cast<int>(L - row * nb) * (THREADS * UNROLL);
+    float* outp = dl + row * ldg;
+    const bool active = (mask == nullptr) || (mask[row] != 0);
+    if (!active) {
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int q = qbase + u * THREADS + tid;
+        if (q >= nq) break;
+        const int j = 4 * q;
+        if (j + 4 <= V) {
+          store16_stream(outp + j, 0.f, 0.f, 0.f, 0.f);
+        } else {
+          for (int e = 0; j + e < V; ++e) outp[j + e] = 0.0f;
+        }
+      }
+      continue;
+    }
+    const int64_t t = targets[row];
+    const float g = grad[row];
+    const float off = lse[row] * kLog2e;
+    const float poison = (t >= 0 && t < V) ? 0.0f : nan;
+    const float4* vp = reinterpret_cast<const float4*>(logits + row * ld);
+    float4 w[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int q = qbase + u * THREADS + tid;
+      w[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (q < nq) w[u] = vp[q];
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int q = qbase + u * THREADS + tid;
+      if (q >= nq) break;
+      const int j = 4 * q;
+      const float x[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+      float d[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = fminf(fast_exp2(__builtin_fmaf(x[e], kLog2e, -off)), __FLT_MAX__);
+        const float add = (j + e == t) ? g : 0.0f;
+        d[e] = __builtin_fmaf(-g, p, add + poison);
+      }
+      if (j + 4 <= V) {
+        store16_stream(outp + j, d[0], d[1], d[2], d[3]);
+      } else {
+        for (int e = 0; j + e < V; ++e) outp[j + e] = d[e];
+      }
+    }
+  }
+}
+
 // Dense log-softmax rows out[i, j] = x_ij - lse_i, with the backward's
 // access pattern and block order.
 template <int THREADS, int UNROLL>
@@ -367,6 +437,18 @@ hipError_t launch_logp_bwd_rows(const uint16_t* logits, int64_t ld, const int64_
   const int per_block = kBwdThreads * kBwdUnroll;
   const int nb = (nq + per_block - 1) / per_block;
   hipLaunchKernelGGL((logp_bwd_rows<kBwdThreads, kBwdUnroll>), dim3(elementwise_grid(N * nb)),
+                     dim3(kBwdThreads), 0, stream, logits, ld, targets, mask, lse, grad, N, V, nb,
+                     dl, ldg);
+  return hipGetLastError();
+}
+
+hipError_t launch_logp_bwd_rows_f32(const float* logits, int64_t ld, const int64_t* targets,
+                                    const uint8_t* mask, const float* lse, const float* grad,
+                                    int64_t N, int V, float* dl, int64_t ldg, hipStream_t stream) {
+  const int nq = (V + 3) / 4;
+  const int per_block = kBwdThreads * kBwdUnroll;
+  const int nb = (nq + per_block - 1) / per_block;
+  hipLaunchKernelGGL((logp_bwd_rows_f32<kBwdThreads, kBwdUnroll>), dim3(elementwise_grid(N * nb)),
                      dim3(kBwdThreads), 0, stream, logits, ld, targets, mask, lse, grad, N, V, nb,
                      dl, ldg);
   return hipGetLastError();

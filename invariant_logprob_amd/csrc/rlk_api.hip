@@ -53,6 +53,15 @@ int check_linear(const void* hidden, int64_t ld_h, const void* weight, int64_t l
   return RLK_OK;
 }
 
+// An fp32 [N, ld] matrix (rows of ld elements, V of them used).
+int check_f32_rows(const void* p, int64_t ld, int64_t N, int64_t V) {
+  if (p == nullptr) return RLK_ERR_INVALID_ARG;
+  if (ld < V) return RLK_ERR_INVALID_ARG;
+  if ((ld % 4) != 0 || !aligned16(p)) return RLK_ERR_UNSUPPORTED;
+  if (N > 0 && ld > (int64_t(1) << 62) / N) return RLK_ERR_UNSUPPORTED;
+  return RLK_OK;
+}
+
 int check_sizes(int64_t N, int64_t V) {
   if (N < 0 || V < 1) return RLK_ERR_INVALID_ARG;
   if (N > kMaxN || V > kMaxV) return RLK_ERR_UNSUPPORTED;
@@ -125,7 +134,53 @@ int rlk_linear_logp(const void* hidden, int64_t ld_h, const void* weight, int64_
   if (!aligned16(workspace)) return RLK_ERR_UNSUPPORTED;
   return status_of(rlk::launch_linear_logp(
       static_cast<const uint16_t*>(hidden), ld_h, static_cast<const uint16_t*>(weight), ld_w,
-      targets, mask, N, static_cast<int>(V), static_cast<int>(H), logp, lse, workspace, stream));
+      targets, mask, N, static_cast<int>(V), static_cast<int>(H), logp, lse, nullptr, 0,
+      workspace, stream));
+}
+
+int rlk_linear_logp_with_logits(const void* hidden, int64_t ld_h, const void* weight,
+                                int64_t ld_w, const int64_t* targets, const uint8_t* mask,
+                                int64_t N, int64_t V, int64_t H, float* logp, float* lse,
+                                float* logits, int64_t ld_z, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  int st = check_sizes(N, V);
+  if (st != RLK_OK) return st;
+  if (N == 0) return RLK_OK;
+  if (targets == nullptr || logp == nullptr || workspace == nullptr) return RLK_ERR_INVALID_ARG;
+  st = check_linear(hidden, ld_h, weight, ld_w, N, V, H);
+  if (st != RLK_OK) return st;
+  st = check_f32_rows(logits, ld_z, N, V);
+  if (st != RLK_OK) return st;
+  if (workspace_bytes < rlk::linear_workspace_bytes(N, V)) return RLK_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return RLK_ERR_UNSUPPORTED;
+  return status_of(rlk::launch_linear_logp(
+      static_cast<const uint16_t*>(hidden), ld_h, static_cast<const uint16_t*>(weight), ld_w,
+      targets, mask, N, static_cast<int>(V), static_cast<int>(H), logp, lse, logits, ld_z,
+      workspace, stream));
+}
+
+int rlk_logp_backward_f32(const float* logits, int64_t ld, const int64_t* targets,
+                          const uint8_t* mask, const float* lse, const float* grad_logp, int64_t N,
+                          int64_t V, float* grad_logits, int64_t ld_g, hipStream_t stream) {
+  int st = check_sizes(N, V);
+  if (st != RLK_OK) return st;
+  if (N == 0) return RLK_OK;
+  if (targets == nullptr || lse == nullptr || grad_logp == nullptr) return RLK_ERR_INVALID_ARG;
+  st = check_f32_rows(logits, ld, N, V);
+  if (st != RLK_OK) return st;
+  st = check_f32_rows(grad_logits, ld_g, N, V);
+  if (st != RLK_OK) return st;
+  // In place (the same buffer and stride) or disjoint; any other overlap of
+  // the two [N, ld] spans would let a lane overwrite another lane's input.
+  if (grad_logits != logits || ld_g != ld) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(logits);
+    const uintptr_t a1 = a0 + static_cast<uintptr_t>((N - 1) * ld + V) * sizeof(float);
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(grad_logits);
+    const uintptr_t b1 = b0 + static_cast<uintptr_t>((N - 1) * ld_g + V) * sizeof(float);
+    if (a0 < b1 && b0 < a1) return RLK_ERR_INVALID_ARG;
+  }
+  return status_of(rlk::launch_logp_bwd_rows_f32(logits, ld, targets, mask, lse, grad_logp, N,
+                                                 static_cast<int>(V), grad_logits, ld_g, stream));
 }
 
 int rlk_logp_backward(const void* logits, int64_t ld, const void* hidden, int64_t ld_h,

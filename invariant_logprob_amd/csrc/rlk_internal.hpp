@@ -33,6 +33,13 @@ hipError_t launch_log_softmax_rows(const uint16_t* logits, int64_t ld, const uin
 hipError_t launch_logp_bwd_rows(const uint16_t* logits, int64_t ld, const int64_t* targets,
                                 const uint8_t* mask, const float* lse, const float* grad, int64_t N,
                                 int V, float* dl, int64_t ldg, hipStream_t stream);
+// The same backward from fp32 logits (as the storing fused forward writes
+// them), with the fused backward's arithmetic, so its output is bit-identical
+// to launch_linear_dlogits' for the same logits.  logits and dl may be the
+// same buffer (ld == ldg).
+hipError_t launch_logp_bwd_rows_f32(const float* logits, int64_t ld, const int64_t* targets,
+                                    const uint8_t* mask, const float* lse, const float* grad,
+                                    int64_t N, int V, float* dl, int64_t ldg, hipStream_t stream);
 
 size_t linear_workspace_bytes(int64_t N, int64_t V);
 
@@ -54,10 +61,12 @@ struct TokenLossArgs {
 
 hipError_t launch_token_losses(const TokenLossArgs& a, hipStream_t stream);
 
+// logits may be null; otherwise the forward also writes the fp32 logits
+// [N, ldz] (every row below N, columns below V).
 hipError_t launch_linear_logp(const uint16_t* hidden, int64_t ldh, const uint16_t* weight,
                               int64_t ldw, const int64_t* targets, const uint8_t* mask, int64_t N,
-                              int V, int H, float* logp, float* lse, void* workspace,
-                              hipStream_t stream);
+                              int V, int H, float* logp, float* lse, float* logits, int64_t ldz,
+                              void* workspace, hipStream_t stream);
 
 hipError_t launch_linear_dlogits(const uint16_t* hidden, int64_t ldh, const uint16_t* weight,
                                  int64_t ldw, const int64_t* targets, const uint8_t* mask,

@@ -105,6 +105,40 @@ def test_backward_validation(lib):
     assert call(lg=NUL, h=A16, ldh=64, w=A2, ldw=64, H=64) == UNSUPPORTED
 
 
+def test_linear_logp_with_logits_validation(lib):
+    f = lib.rlk_linear_logp_with_logits
+    ws = lib.rlk_linear_logp_workspace_size(300, 1000, 64)
+    args = lambda **k: [A16, 64, A16, 64, A16, NUL, k.get("n", 300), k.get("v", 1000), 64, A16,
+                        NUL, k.get("z", A16), k.get("ldz", 1000), A16, k.get("wsb", ws), NUL]
+    assert f(*args(n=0)) == OK
+    assert f(*args(z=NUL)) == INVALID                     # the logits output is required
+    assert f(*args(ldz=996)) == INVALID                   # ld_z < V
+    assert f(*args(ldz=1002)) == UNSUPPORTED              # ld_z % 4
+    assert f(*args(z=ctypes.c_void_p(0x10008))) == UNSUPPORTED   # misaligned
+    assert f(*args(wsb=ws - 1)) == INVALID
+
+
+def test_backward_f32_validation(lib):
+    f = lib.rlk_logp_backward_f32
+    base = dict(z=A16, ld=1024, t=A16, m=NUL, lse=A16, g=A16, n=4, v=1000, out=A16, ldg=1024)
+    call = lambda **k: f(*[{**base, **k}[x] for x in ("z", "ld", "t", "m", "lse", "g", "n", "v",
+                                                      "out", "ldg")], NUL)
+    assert call(n=0) == OK
+    assert call(z=NUL) == INVALID
+    assert call(out=NUL) == INVALID
+    assert call(lse=NUL) == INVALID
+    assert call(g=NUL) == INVALID
+    assert call(t=NUL) == INVALID
+    assert call(ld=996) == INVALID                        # ld < V
+    assert call(ld=1026, ldg=1026) == UNSUPPORTED         # ld % 4
+    assert call(z=ctypes.c_void_p(0x10008)) == UNSUPPORTED
+    # in place is the same buffer with the same stride; any other overlap is refused
+    assert call(out=A16, ldg=1028) == INVALID
+    assert call(out=ctypes.c_void_p(0x10000 + 16 * 4)) == INVALID
+    assert call(out=ctypes.c_void_p(0x10000 + 3 * 1024 * 4)) == INVALID   # the last input row
+    assert call(out=ctypes.c_void_p(0x10000 - 3 * 1024 * 4)) == INVALID   # ends in the first one
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
     x = torch.zeros(2, 8, dtype=torch.bfloat16)
