@@ -42,7 +42,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--legs", default="logits_fwd,logits_bwd,fused_fwd,fused_fb")
     p.add_argument("--extra-legs",
-                   default="logits_entropy,log_softmax,token_losses,fused_param_grads,fused_fb_kept_logits",
+                   default="logits_entropy,log_softmax,token_losses,fused_param_grads,"
+                           "fused_fb_kept_logits,fused_param_grads_kept_logits",
                    help="rows beyond the hot path, timed after the steps (not part of a step)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="instead of the hot path, run a plain 1 GiB device copy 5 times "
@@ -245,6 +246,18 @@ def main():
                                                 workspace=wsg5),
             n5 * h5 * 2 + v5 * h5 * 2 + n5 * h5 * 4 + v5 * h5 * 4)
         xflops["fused_param_grads"] = 3 * 2.0 * n5 * v5 * h5
+        if "fused_param_grads_kept_logits" in args.extra_legs.split(","):
+            # the same gradients from logits the forward kept (computed once,
+            # outside the timing): the two products only, 2 x 2 N V H flops
+            zk5 = torch.empty((n5, v5), dtype=torch.float32, device=dev)
+            ilp.linear_logp_with_logits(c5.hidden, c5.weight, c5.targets, c5.mask, workspace=ws5,
+                                        logp=logp5, lse=lse5, logits=zk5)
+            xfns["fused_param_grads_kept_logits"] = (
+                lambda: ilp.linear_logp_param_grads(c5.hidden, c5.weight, c5.targets, lse5,
+                                                    c5.grad, c5.mask, grad_hidden=gh5,
+                                                    grad_weight=gw5, workspace=wsg5, logits=zk5),
+                n5 * h5 * 2 + v5 * h5 * 2 + n5 * v5 * 4 + n5 * h5 * 4 + v5 * h5 * 4)
+            xflops["fused_param_grads_kept_logits"] = 2 * 2.0 * n5 * v5 * h5
     if c5 is not None and "fused_fb_kept_logits" in args.extra_legs.split(","):
         # the fwd+bwd workload with the forward keeping its fp32 logits and the
         # backward computed from them in place (one projection, 2 N V H flops)

@@ -253,6 +253,30 @@ int rlk_linear_logp_param_grads(const void* hidden, int64_t ld_h,
                                 hipStream_t stream);
 
 /*
+ * rlk_linear_logp_param_grads from the fp32 logits the forward kept
+ * (rlk_linear_logp_with_logits): each vocabulary chunk's logits gradient is
+ * formed from `logits` [N, ld_z] (ld_z >= V, ld_z % 4 == 0, 16-B aligned;
+ * inactive rows are not read) instead of being recomputed, with the same
+ * arithmetic, so grad_hidden and grad_weight are bit-identical to
+ * rlk_linear_logp_param_grads' for logits that function would recompute.
+ * hidden is still read (grad_weight = D^T . hidden).  Every other argument,
+ * the workspace and the error codes are as there; logits NULL with N > 0 is
+ * RLK_ERR_INVALID_ARG.
+ */
+int rlk_linear_logp_param_grads_from_logits(const float* logits, int64_t ld_z,
+                                            const void* hidden, int64_t ld_h,
+                                            const void* weight, int64_t ld_w,
+                                            const int64_t* targets,
+                                            const uint8_t* mask, const float* lse,
+                                            const float* grad_logp, int64_t N,
+                                            int64_t V, int64_t H,
+                                            float* grad_hidden, int64_t ld_gh,
+                                            float* grad_weight, int64_t ld_gw,
+                                            void* workspace,
+                                            size_t workspace_bytes,
+                                            hipStream_t stream);
+
+/*
  * Per-token loss terms consuming the selected logprob (the chain's last
  * entry, grpo_loss / ratio_kl, as per-token outputs so that each token's
  * values cannot depend on the batch: page "docs(ws1): ...", section

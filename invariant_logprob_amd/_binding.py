@@ -65,6 +65,10 @@ def load_library():
     lib.rlk_linear_logp_param_grads.argtypes = [vp, i64, vp, i64, vp, vp, vp, vp, i64, i64, i64, vp,
                                                 i64, vp, i64, vp, sz, vp]
     lib.rlk_linear_logp_param_grads.restype = ctypes.c_int
+    lib.rlk_linear_logp_param_grads_from_logits.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, vp,
+                                                            vp, i64, i64, i64, vp, i64, vp, i64,
+                                                            vp, sz, vp]
+    lib.rlk_linear_logp_param_grads_from_logits.restype = ctypes.c_int
     lib.rlk_status_string.argtypes = [ctypes.c_int]
     lib.rlk_status_string.restype = ctypes.c_char_p
     lib.rlk_build_info.argtypes = []
@@ -409,10 +413,12 @@ def _param_out(out, rows, cols, dev, name):
 
 def linear_logp_param_grads(hidden, weight, targets, lse, grad_logp, mask=None, *,
                             want_hidden=True, want_weight=True, grad_hidden=None,
-                            grad_weight=None, workspace=None):
+                            grad_weight=None, workspace=None, logits=None):
     """Gradients of sum_i g_i logp_i with respect to hidden [N, H] and weight
     [V, H] of the fused path: returns (grad_hidden, grad_weight), float32,
-    each None when not requested."""
+    each None when not requested.  `logits`: the fp32 [N, V] logits
+    linear_logp_with_logits kept, used instead of recomputing them (the
+    gradients are bit-identical)."""
     lib = load_library()
     if not (want_hidden or want_weight):
         raise ValueError("request at least one of grad_hidden / grad_weight")
@@ -426,7 +432,12 @@ def linear_logp_param_grads(hidden, weight, targets, lse, grad_logp, mask=None, 
     _rows(lse, "lse", n, torch.float32)
     _rows(grad_logp, "grad_logp", n, torch.float32)
     mask = _mask(mask, n)
-    dev = _same_device(hidden, weight, targets, lse, grad_logp, mask)
+    dev = _same_device(hidden, weight, targets, lse, grad_logp, mask, logits)
+    ldz = 0
+    if logits is not None:
+        ldz = _matrix(logits, "logits", torch.float32)
+        if tuple(logits.shape) != (n, v):
+            raise ValueError(f"logits must have shape ({n}, {v})")
     gh = gw = None
     ld_gh = ld_gw = 0
     if want_hidden:
@@ -439,11 +450,18 @@ def linear_logp_param_grads(hidden, weight, targets, lse, grad_logp, mask=None, 
     if workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace too small: need {need} bytes")
     with torch.cuda.device(dev):
-        st = lib.rlk_linear_logp_param_grads(
-            _ptr(hidden), ldh, _ptr(weight), ldw, _ptr(targets), _ptr(mask), _ptr(lse),
-            _ptr(grad_logp), n, v, h, _ptr(gh), ld_gh, _ptr(gw), ld_gw, _ptr(workspace),
-            workspace.numel() * workspace.element_size(), _stream(dev))
-    _raise(st, "rlk_linear_logp_param_grads")
+        if logits is None:
+            st = lib.rlk_linear_logp_param_grads(
+                _ptr(hidden), ldh, _ptr(weight), ldw, _ptr(targets), _ptr(mask), _ptr(lse),
+                _ptr(grad_logp), n, v, h, _ptr(gh), ld_gh, _ptr(gw), ld_gw, _ptr(workspace),
+                workspace.numel() * workspace.element_size(), _stream(dev))
+            _raise(st, "rlk_linear_logp_param_grads")
+        else:
+            st = lib.rlk_linear_logp_param_grads_from_logits(
+                _ptr(logits), ldz, _ptr(hidden), ldh, _ptr(weight), ldw, _ptr(targets),
+                _ptr(mask), _ptr(lse), _ptr(grad_logp), n, v, h, _ptr(gh), ld_gh, _ptr(gw), ld_gw,
+                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+            _raise(st, "rlk_linear_logp_param_grads_from_logits")
     return gh, gw
 
 

@@ -16,7 +16,10 @@
 //   1. grad_dl_tiles recomputes the chunk's logits with the forward's tile
 //      main loop (bit-identical z), forms D in fp32 exactly as the logits
 //      backward does, rounds it once to bf16 (the MFMA operand type) and
-//      writes D_c [N, chunk].
+//      writes D_c [N, chunk].  Given the fp32 logits the forward kept,
+//      grad_dl_from_logits forms the same D_c from them instead, element by
+//      element with the same arithmetic, so the gradients come out
+//      bit-identical at a fraction of the cost.
 //   2. grad_gemm_tiles runs both products of the chunk in one launch:
 //      grad_hidden (+)= D_c . W_c   (K = the chunk's vocabulary, ascending;
 //                                    chunk 0 writes, later chunks add)
@@ -188,6 +191,67 @@ void grad_dl_tiles(DlArgs a) {
   else epilogue(std::false_type{});
 }
 
+// D_c from kept fp32 logits [N, ldz]: entry (row, k) of the chunk is vocabulary
+// column vocab0 + k.  The per-element arithmetic is grad_dl_tiles' (so is
+// the bf16 rounding); columns at or past V within the padded chunk width
+// and inactive rows get +0, and an active row with an invalid target NaN.
+// Blocks of 2048 columns of one row: 128 threads x 4 groups of 4 columns,
+// 16-byte loads, 8-byte stores (512 contiguous bytes per wave instruction).
+constexpr int kDlzThreads = 128;
+constexpr int kDlzUnroll = 4;
+constexpr int kDlzBlockCols = kDlzThreads * kDlzUnroll * 4;
+
+__global__ __launch_bounds__(kDlzThreads) void grad_dl_from_logits(
+    const float* __restrict__ logits, int64_t ldz, const int64_t* __restrict__ targets,
+    const uint8_t* __restrict__ mask, const float* __restrict__ lse,
+    const float* __restrict__ grad, int64_t N, int V, int vocab0, int width, int nb,
+    uint16_t* __restrict__ d, int64_t ldd) {
+  const int tid = threadIdx.x;
+  const int64_t total = N * nb;
+  for (int64_t wid = blockIdx.x; wid < total; wid += gridDim.x) {
+    const int64_t row = wid / nb;
+    const int k0 = static_cast<int>(wid - row * nb) * kDlzBlockCols;
+    const bool active = (mask == nullptr) || (mask[row] != 0);
+    const int64_t t = active ? targets[row] : -1;
+    const float g = active ? grad[row] : 0.0f;
+    const float ng = -g;
+    const float off = active ? lse[row] * kLog2e : 0.0f;
+    const float pz = (active && !(t >= 0 && t < V)) ? __builtin_nanf("") : 0.0f;
+    const float* zr = logits + row * ldz + vocab0;
+    uint16_t* dr = d + row * ldd;
+    float4 w[kDlzUnroll];
+#pragma unroll
+    for (int u = 0; u < kDlzUnroll; ++u) {
+      const int k = k0 + 4 * (u * kDlzThreads + tid);
+      w[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (active && k < width && vocab0 + k < V) {
+        if (vocab0 + k + 4 <= V) {
+          w[u] = *reinterpret_cast<const float4*>(zr + k);
+        } else {
+          float x[4] = {0.f, 0.f, 0.f, 0.f};
+          for (int e = 0; vocab0 + k + e < V; ++e) x[e] = zr[k + e];
+          w[u] = make_float4(x[0], x[1], x[2], x[3]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kDlzUnroll; ++u) {
+      const int k = k0 + 4 * (u * kDlzThreads + tid);
+      if (k >= width) break;
+      const float x[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+      uint32_t b[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = fminf(fast_exp2(__builtin_fmaf(x[e], kLog2e, -off)), __FLT_MAX__);
+        const bool col = vocab0 + k + e < V;
+        const float add = (vocab0 + k + e == t) ? g : 0.0f;
+        b[e] = bf16_bits(__builtin_fmaf(col ? ng : 0.0f, p, col ? add + pz : 0.0f));
+      }
+      *reinterpret_cast<uint2*>(dr + k) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+    }
+  }
+}
+
 // One product of a chunk: out[Q rows][P rows] (+)= Q . P^T over K.  Each
 // side is either an operand with one row per tile row and K contiguous, or a
 // K-major operand whose columns are the tile rows (see tile_core.hpp).
@@ -329,7 +393,8 @@ hipError_t launch_linear_param_grads(const uint16_t* hidden, int64_t ldh, const 
                                      int64_t ldw, const int64_t* targets, const uint8_t* mask,
                                      const float* lse, const float* grad, int64_t N, int V, int H,
                                      float* grad_hidden, int64_t ld_gh, float* grad_weight,
-                                     int64_t ld_gw, void* workspace, hipStream_t stream) {
+                                     int64_t ld_gw, const float* logits, int64_t ldz,
+                                     void* workspace, hipStream_t stream) {
   if (N == 0) {
     // no tokens: grad_weight is an empty sum; grad_hidden has no rows
     if (grad_weight != nullptr) {
@@ -358,25 +423,33 @@ hipError_t launch_linear_param_grads(const uint16_t* hidden, int64_t ldh, const 
     const int v_rows = static_cast<int>(min64(V - vocab0, n_vt * kBP));  // real vocabulary rows
     const int width = n_vt * kBP;                                        // padded chunk width
 
-    DlArgs da{};
-    da.hidden = hidden;
-    da.ldh = ldh;
-    da.weight = weight;
-    da.ldw = ldw;
-    da.targets = targets;
-    da.mask = mask;
-    da.lse = lse;
-    da.grad = grad;
-    da.N = N;
-    da.V = V;
-    da.H = H;
-    da.vt0 = vt0;
-    da.n_vt = n_vt;
-    da.n_tblocks = n_tblocks;
-    da.d = d;
-    da.ldd = chunk;
-    hipLaunchKernelGGL(grad_dl_tiles, dim3(static_cast<uint32_t>(n_vt * n_tblocks)), dim3(kThreads),
-                       0, stream, da);
+    if (logits != nullptr) {
+      const int nb = (width + kDlzBlockCols - 1) / kDlzBlockCols;
+      const int64_t blocks = min64(N * nb, int64_t(1) << 22);
+      hipLaunchKernelGGL(grad_dl_from_logits, dim3(static_cast<uint32_t>(blocks)),
+                         dim3(kDlzThreads), 0, stream, logits, ldz, targets, mask, lse, grad, N, V,
+                         vocab0, width, nb, d, static_cast<int64_t>(chunk));
+    } else {
+      DlArgs da{};
+      da.hidden = hidden;
+      da.ldh = ldh;
+      da.weight = weight;
+      da.ldw = ldw;
+      da.targets = targets;
+      da.mask = mask;
+      da.lse = lse;
+      da.grad = grad;
+      da.N = N;
+      da.V = V;
+      da.H = H;
+      da.vt0 = vt0;
+      da.n_vt = n_vt;
+      da.n_tblocks = n_tblocks;
+      da.d = d;
+      da.ldd = chunk;
+      hipLaunchKernelGGL(grad_dl_tiles, dim3(static_cast<uint32_t>(n_vt * n_tblocks)),
+                         dim3(kThreads), 0, stream, da);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 

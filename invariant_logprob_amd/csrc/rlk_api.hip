@@ -68,6 +68,53 @@ int check_sizes(int64_t N, int64_t V) {
   return RLK_OK;
 }
 
+// Both parameter-gradient entry points: logits null (recomputed per chunk)
+// or the fp32 logits the forward kept.
+int param_grads(const float* logits, int64_t ld_z, const void* hidden, int64_t ld_h,
+                const void* weight, int64_t ld_w, const int64_t* targets, const uint8_t* mask,
+                const float* lse, const float* grad_logp, int64_t N, int64_t V, int64_t H,
+                float* grad_hidden, int64_t ld_gh, float* grad_weight, int64_t ld_gw,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_sizes(N, V);
+  if (st != RLK_OK) return st;
+  if (grad_hidden == nullptr && grad_weight == nullptr) return RLK_ERR_INVALID_ARG;
+  if (weight == nullptr || H < 1 || ld_w < H) return RLK_ERR_INVALID_ARG;
+  if (grad_weight != nullptr) {
+    if (ld_gw < H) return RLK_ERR_INVALID_ARG;
+    if ((ld_gw % 4) != 0 || !aligned16(grad_weight)) return RLK_ERR_UNSUPPORTED;
+    if (ld_gw > (int64_t(1) << 62) / V) return RLK_ERR_UNSUPPORTED;
+  }
+  if (N == 0) {
+    if ((H % 8) != 0) return RLK_ERR_UNSUPPORTED;
+    return status_of(rlk::launch_linear_param_grads(
+        nullptr, 0, static_cast<const uint16_t*>(weight), ld_w, nullptr, nullptr, nullptr, nullptr,
+        0, static_cast<int>(V), static_cast<int>(H), nullptr, 0, grad_weight, ld_gw, nullptr, 0,
+        nullptr, stream));
+  }
+  if (targets == nullptr || lse == nullptr || grad_logp == nullptr || workspace == nullptr)
+    return RLK_ERR_INVALID_ARG;
+  st = check_linear(hidden, ld_h, weight, ld_w, N, V, H);
+  if (st != RLK_OK) return st;
+  // the transposed hidden's rows (N rounded up to 8) are addressed like a
+  // fused-tile operand
+  if (N > kMaxLinearLd - 16) return RLK_ERR_UNSUPPORTED;
+  if (grad_hidden != nullptr) {
+    if (ld_gh < H) return RLK_ERR_INVALID_ARG;
+    if ((ld_gh % 4) != 0 || !aligned16(grad_hidden)) return RLK_ERR_UNSUPPORTED;
+    if (ld_gh > (int64_t(1) << 62) / N) return RLK_ERR_UNSUPPORTED;
+  }
+  if (logits != nullptr) {
+    st = check_f32_rows(logits, ld_z, N, V);
+    if (st != RLK_OK) return st;
+  }
+  if (workspace_bytes < rlk::linear_param_grads_workspace_bytes(N, V, H)) return RLK_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return RLK_ERR_UNSUPPORTED;
+  return status_of(rlk::launch_linear_param_grads(
+      static_cast<const uint16_t*>(hidden), ld_h, static_cast<const uint16_t*>(weight), ld_w,
+      targets, mask, lse, grad_logp, N, static_cast<int>(V), static_cast<int>(H), grad_hidden,
+      ld_gh, grad_weight, ld_gw, logits, ld_z, workspace, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -221,40 +268,21 @@ int rlk_linear_logp_param_grads(const void* hidden, int64_t ld_h, const void* we
                                 float* grad_hidden, int64_t ld_gh, float* grad_weight,
                                 int64_t ld_gw, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
-  int st = check_sizes(N, V);
-  if (st != RLK_OK) return st;
-  if (grad_hidden == nullptr && grad_weight == nullptr) return RLK_ERR_INVALID_ARG;
-  if (weight == nullptr || H < 1 || ld_w < H) return RLK_ERR_INVALID_ARG;
-  if (grad_weight != nullptr) {
-    if (ld_gw < H) return RLK_ERR_INVALID_ARG;
-    if ((ld_gw % 4) != 0 || !aligned16(grad_weight)) return RLK_ERR_UNSUPPORTED;
-    if (ld_gw > (int64_t(1) << 62) / V) return RLK_ERR_UNSUPPORTED;
-  }
-  if (N == 0) {
-    if ((H % 8) != 0) return RLK_ERR_UNSUPPORTED;
-    return status_of(rlk::launch_linear_param_grads(
-        nullptr, 0, static_cast<const uint16_t*>(weight), ld_w, nullptr, nullptr, nullptr, nullptr,
-        0, static_cast<int>(V), static_cast<int>(H), nullptr, 0, grad_weight, ld_gw, nullptr,
-        stream));
-  }
-  if (targets == nullptr || lse == nullptr || grad_logp == nullptr || workspace == nullptr)
-    return RLK_ERR_INVALID_ARG;
-  st = check_linear(hidden, ld_h, weight, ld_w, N, V, H);
-  if (st != RLK_OK) return st;
-  // the transposed hidden's rows (N rounded up to 8) are addressed like a
-  // fused-tile operand
-  if (N > kMaxLinearLd - 16) return RLK_ERR_UNSUPPORTED;
-  if (grad_hidden != nullptr) {
-    if (ld_gh < H) return RLK_ERR_INVALID_ARG;
-    if ((ld_gh % 4) != 0 || !aligned16(grad_hidden)) return RLK_ERR_UNSUPPORTED;
-    if (ld_gh > (int64_t(1) << 62) / N) return RLK_ERR_UNSUPPORTED;
-  }
-  if (workspace_bytes < rlk::linear_param_grads_workspace_bytes(N, V, H)) return RLK_ERR_INVALID_ARG;
-  if (!aligned16(workspace)) return RLK_ERR_UNSUPPORTED;
-  return status_of(rlk::launch_linear_param_grads(
-      static_cast<const uint16_t*>(hidden), ld_h, static_cast<const uint16_t*>(weight), ld_w,
-      targets, mask, lse, grad_logp, N, static_cast<int>(V), static_cast<int>(H), grad_hidden,
-      ld_gh, grad_weight, ld_gw, workspace, stream));
+  return param_grads(nullptr, 0, hidden, ld_h, weight, ld_w, targets, mask, lse, grad_logp, N, V,
+                     H, grad_hidden, ld_gh, grad_weight, ld_gw, workspace, workspace_bytes, stream);
+}
+
+int rlk_linear_logp_param_grads_from_logits(const float* logits, int64_t ld_z, const void* hidden,
+                                            int64_t ld_h, const void* weight, int64_t ld_w,
+                                            const int64_t* targets, const uint8_t* mask,
+                                            const float* lse, const float* grad_logp, int64_t N,
+                                            int64_t V, int64_t H, float* grad_hidden,
+                                            int64_t ld_gh, float* grad_weight, int64_t ld_gw,
+                                            void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream) {
+  if (logits == nullptr && N > 0) return RLK_ERR_INVALID_ARG;
+  return param_grads(logits, ld_z, hidden, ld_h, weight, ld_w, targets, mask, lse, grad_logp, N, V,
+                     H, grad_hidden, ld_gh, grad_weight, ld_gw, workspace, workspace_bytes, stream);
 }
 
 int rlk_token_losses(const float* logp, const float* logp_old, const float* logp_ref,

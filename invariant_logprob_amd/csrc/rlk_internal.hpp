@@ -75,10 +75,14 @@ hipError_t launch_linear_dlogits(const uint16_t* hidden, int64_t ldh, const uint
 
 size_t linear_param_grads_workspace_bytes(int64_t N, int64_t V, int64_t H);
 
+// logits may be null (the logits are recomputed per chunk); otherwise they
+// are the fp32 [N, ldz] logits the forward kept, and each chunk's D is
+// formed from them.  The gradients are bit-identical either way.
 hipError_t launch_linear_param_grads(const uint16_t* hidden, int64_t ldh, const uint16_t* weight,
                                      int64_t ldw, const int64_t* targets, const uint8_t* mask,
                                      const float* lse, const float* grad, int64_t N, int V, int H,
                                      float* grad_hidden, int64_t ld_gh, float* grad_weight,
-                                     int64_t ld_gw, void* workspace, hipStream_t stream);
+                                     int64_t ld_gw, const float* logits, int64_t ldz,
+                                     void* workspace, hipStream_t stream);
 
 }  // namespace rlk

@@ -207,3 +207,22 @@ def test_linear_param_grads_validation(lib):
     assert f(*args(H=60, ldh=64, ldw=64, ldgh=64, ldgw=64)) == UNSUPPORTED  # H % 8
     assert f(*args(n=1 << 22)) == UNSUPPORTED              # N beyond the transposed-operand range
     assert f(*args(ws=A2)) == UNSUPPORTED
+
+
+def test_linear_param_grads_from_logits_validation(lib):
+    f = lib.rlk_linear_logp_param_grads_from_logits
+    n, v, h = 300, 1000, 64
+    ws = lib.rlk_linear_logp_param_grads_workspace_size(n, v, h)
+
+    def args(**k):
+        return [k.get("z", A16), k.get("ldz", v), A16, h, A16, h, A16, NUL, A16, A16,
+                k.get("n", n), v, h, k.get("gh", A16), h, k.get("gw", A16), h, A16,
+                k.get("wsb", ws), NUL]
+
+    assert f(*args(n=0, gw=NUL)) == OK                     # nothing to do, nothing launched
+    assert f(*args(z=NUL)) == INVALID                      # the kept logits are required
+    assert f(*args(ldz=v - 4)) == INVALID                  # ld_z < V
+    assert f(*args(ldz=v + 2)) == UNSUPPORTED              # ld_z % 4
+    assert f(*args(z=ctypes.c_void_p(0x10008))) == UNSUPPORTED   # misaligned
+    assert f(*args(gh=NUL, gw=NUL)) == INVALID
+    assert f(*args(wsb=ws - 1)) == INVALID

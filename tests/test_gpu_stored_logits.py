@@ -169,3 +169,42 @@ def test_binding_refuses_rows_its_storage_does_not_hold(dev):
     # the same row inside padded storage is fine
     xp = torch.randn((1, 1008), device=dev).to(torch.bfloat16)[:, :1001]
     ilp.logp_selected(xp, t)
+
+
+@pytest.mark.parametrize("n,v,h", [(33, 1000, 256), (300, 17000, 136), (257, 513, 8)])
+def test_param_grads_from_kept_logits(dev, n, v, h):
+    """Parameter gradients from the kept logits equal the recomputing path's
+    bit for bit: several vocabulary chunks with a ragged last one, masked rows
+    and one active row with an invalid target (NaN in the same places)."""
+    b = wl.fused_batch(n, v, h, seed=5 * n + v, device=dev, w_sigma=0.05, n_masked=n // 10)
+    t = b.targets.clone()
+    t[1] = v
+    b.mask[1] = 1
+    logp, lse, z = ilp.linear_logp_with_logits(b.hidden, b.weight, t, b.mask)
+    gh0, gw0 = ilp.linear_logp_param_grads(b.hidden, b.weight, t, lse, b.grad, b.mask)
+    gh1, gw1 = ilp.linear_logp_param_grads(b.hidden, b.weight, t, lse, b.grad, b.mask, logits=z)
+    torch.cuda.synchronize()
+    assert _bits_equal(gh1, gh0) and _bits_equal(gw1, gw0)
+    assert bool(torch.isnan(gh1[1]).all())
+    # without the invalid row: finite, and still equal
+    t[1] = 0
+    logp, lse, z = ilp.linear_logp_with_logits(b.hidden, b.weight, t, b.mask)
+    gh0, gw0 = ilp.linear_logp_param_grads(b.hidden, b.weight, t, lse, b.grad, b.mask)
+    gh1, gw1 = ilp.linear_logp_param_grads(b.hidden, b.weight, t, lse, b.grad, b.mask, logits=z,
+                                           want_hidden=False)
+    torch.cuda.synchronize()
+    assert gh1 is None and _bits_equal(gw1, gw0) and bool(torch.isfinite(gw1).all())
+
+
+def test_param_grads_from_kept_logits_full_size(dev):
+    """hidden [2048, 5120], W [151936, 5120]: both gradients from the kept
+    logits equal the recomputing path's over the whole outputs."""
+    b = wl.fused_bwd(seed=0, device=dev)
+    logp, lse, z = ilp.linear_logp_with_logits(b.hidden, b.weight, b.targets, b.mask)
+    gh0, gw0 = ilp.linear_logp_param_grads(b.hidden, b.weight, b.targets, lse, b.grad, b.mask)
+    torch.cuda.synchronize()
+    gh1, gw1 = ilp.linear_logp_param_grads(b.hidden, b.weight, b.targets, lse, b.grad, b.mask,
+                                           logits=z)
+    torch.cuda.synchronize()
+    assert _bits_equal(gh1, gh0)
+    assert _bits_equal(gw1, gw0)
