@@ -43,7 +43,8 @@ def parse():
     p.add_argument("--legs", default="logits_fwd,logits_bwd,fused_fwd,fused_fb")
     p.add_argument("--extra-legs",
                    default="logits_entropy,log_softmax,token_losses,fused_param_grads,"
-                           "fused_fb_kept_logits,fused_param_grads_kept_logits",
+                           "fused_fb_kept_logits,fused_param_grads_kept_logits,logits_small,"
+                           "logits_varlen",
                    help="rows beyond the hot path, timed after the steps (not part of a step)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="instead of the hot path, run a plain 1 GiB device copy 5 times "
@@ -288,6 +289,43 @@ def main():
         else:
             extra[name] = {"ms": xms, "algorithmic_bytes": nbytes, "GB_per_s": xgbs,
                            "hbm_frac": xgbs / HBM_PEAK_GBS}
+
+    # the two small logits configurations, per launch: N=8, V=1024 (latency)
+    # and 8 varlen sequences packed to N~4096, V=32000; median of 20 launches
+    # back to back (warm) and after a 512 MB write that flushes the MALL (cold)
+    small = [x for x in ("logits_small", "logits_varlen") if x in args.extra_legs.split(",")]
+    if small:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        for name in small:
+            cb = (wl.logits_small if name == "logits_small" else wl.logits_varlen)(seed=0, device=dev)
+            nb_, vb_ = cb.logits.shape
+            actb = int(cb.mask.sum())
+            lpb = torch.empty(nb_, dtype=torch.float32, device=dev)
+            lsb = torch.empty(nb_, dtype=torch.float32, device=dev)
+            fn = (lambda cb=cb, lpb=lpb, lsb=lsb:
+                  ilp.logp_selected(cb.logits, cb.targets, cb.mask, logp=lpb, lse=lsb))
+            times = {}
+            for mode in ("warm", "cold"):
+                fn()
+                torch.cuda.synchronize()
+                ts = []
+                for _ in range(20):
+                    if mode == "cold":
+                        flush.fill_(1)
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    fn()
+                    e1.record()
+                    e1.synchronize()
+                    ts.append(e0.elapsed_time(e1))
+                times[mode] = sorted(ts)[len(ts) // 2]
+            nbytes = actb * vb_ * 2 + nb_ * (8 + 1 + 8)
+            gbs = nbytes / (times["cold"] * 1e-3) / 1e9
+            extra[name] = {"ms": times["warm"], "cold_ms": times["cold"], "rows": nb_,
+                           "active_rows": actb, "V": vb_, "algorithmic_bytes": nbytes,
+                           "GB_per_s_cold": gbs, "hbm_frac_cold": gbs / HBM_PEAK_GBS}
+        del flush
 
     cpu = None
     if not args.no_cpu_baseline and "logits_fwd" in legs:

@@ -486,23 +486,32 @@ class SelectedLogprob(torch.autograd.Function):
 
 class LinearLogprob(torch.autograd.Function):
     """Autograd wrapper of the fused path: forward through rlk_linear_logp,
-    backward through rlk_linear_logp_param_grads with the saved lse.  The
+    backward through rlk_linear_logp_param_grads with the saved lse.  With
+    keep_logits=True the forward keeps its fp32 logits (N x V x 4 bytes,
+    held until backward) and the backward forms the gradients from them
+    instead of recomputing them; the gradients are bit-identical.  The
     gradients are float32; autograd casts them to the inputs' dtype."""
 
     @staticmethod
-    def forward(ctx, hidden, weight, targets, mask=None):
-        logp, lse = linear_logp(hidden, weight, targets, mask)
+    def forward(ctx, hidden, weight, targets, mask=None, keep_logits=False):
+        if keep_logits:
+            logp, lse, logits = linear_logp_with_logits(hidden, weight, targets, mask)
+        else:
+            logp, lse = linear_logp(hidden, weight, targets, mask)
+            logits = torch.empty(0)
         ctx.save_for_backward(hidden, weight, targets, lse,
-                              mask if mask is not None else torch.empty(0))
+                              mask if mask is not None else torch.empty(0), logits)
         ctx.has_mask = mask is not None
+        ctx.keep_logits = bool(keep_logits)
         return logp
 
     @staticmethod
     def backward(ctx, grad):
-        hidden, weight, targets, lse, mask = ctx.saved_tensors
+        hidden, weight, targets, lse, mask, logits = ctx.saved_tensors
         g = grad.contiguous().to(torch.float32)
         gh, gw = linear_logp_param_grads(hidden, weight, targets, lse, g,
                                          mask if ctx.has_mask else None,
                                          want_hidden=ctx.needs_input_grad[0],
-                                         want_weight=ctx.needs_input_grad[1])
-        return gh, gw, None, None
+                                         want_weight=ctx.needs_input_grad[1],
+                                         logits=logits if ctx.keep_logits else None)
+        return gh, gw, None, None, None

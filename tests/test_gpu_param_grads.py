@@ -245,6 +245,13 @@ def test_autograd_wrapper(dev):
     assert hid.grad.dtype == torch.bfloat16 and w.grad.dtype == torch.bfloat16
     assert torch.equal(hid.grad, gh.to(torch.bfloat16))
     assert torch.equal(w.grad, gw.to(torch.bfloat16))
+    # keeping the logits for the backward gives the same gradients
+    hid2 = b.hidden.clone().requires_grad_(True)
+    w2 = b.weight.clone().requires_grad_(True)
+    logp2 = ilp.LinearLogprob.apply(hid2, w2, b.targets, b.mask, True)
+    (logp2 * b.grad).sum().backward()
+    assert torch.equal(logp2.detach().view(torch.int32), logp.detach().view(torch.int32))
+    assert torch.equal(hid2.grad, hid.grad) and torch.equal(w2.grad, w.grad)
 
 
 def test_padded_leading_dimensions(dev):
