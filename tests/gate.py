@@ -37,14 +37,18 @@ for p in (ROOT, HERE):
 
 GENERATOR_VERSION = "workloads-1"
 THRESHOLDS = {
-    "forward_accuracy": {"logp": "2e-5 + 1e-5|r|", "linear_logp": "2e-3"},
-    "gradient_accuracy": {"logp": "1e-3", "linear_logp": "1e-3",
+    "forward_accuracy": {"logp": "2e-5 + 1e-5|r|", "linear_logp": "2e-3",
+                         "linear_logp_kept": "2e-3"},
+    "gradient_accuracy": {"logp": "1e-3", "linear_logp": "1e-3", "linear_logp_kept": "1e-3",
                           "linear_logp_params": "2^-8 sum|D||W| + 1e-6 (grad_hidden), "
                                                 "2^-8 sum|D||h| + 1e-6 (grad_weight)"},
     "forward_invariance": {"atol": 0.0, "rtol": 0.0},
     "gradient_invariance": {"atol": 0.0, "rtol": 0.0},
 }
-CHAIN_INDEX = {"logp": 8, "linear_logp": 7, "linear_logp_params": 7}
+# linear_logp_kept: the fused operator with its fp32 logits kept by the
+# forward and its backward computed from them (the same chain entry)
+CHAIN_INDEX = {"logp": 8, "linear_logp": 7, "linear_logp_kept": 7, "linear_logp_params": 7}
+OPERATORS = ("logp", "linear_logp", "linear_logp_kept", "linear_logp_params")
 
 
 def fixture_id(man):
@@ -85,6 +89,18 @@ def case_list(quick):
                 cases.append({"operator": "linear_logp", "judgment": j, "workload": wl_name,
                               "workload_args": wl_args, "seed": 0,
                               "transform": {"class": t[0], **t[1]}})
+    # the same operator with the logits kept by the forward: the first fused
+    # workload, all four judgments
+    wl_name, wl_args = fused[0]
+    for j in ("forward_accuracy", "gradient_accuracy"):
+        cases.append({"operator": "linear_logp_kept", "judgment": j, "workload": wl_name,
+                      "workload_args": wl_args, "seed": 0})
+    for t in (("T1", {"size": 1, "start": 5}), ("T2", {"seed": 1}),
+              ("T4", {"left": 3, "right": 1, "every": 40, "seed": 4}), ("T5", {"chunk": 32})):
+        for j in ("forward_invariance", "gradient_invariance"):
+            cases.append({"operator": "linear_logp_kept", "judgment": j, "workload": wl_name,
+                          "workload_args": wl_args, "seed": 0,
+                          "transform": {"class": t[0], **t[1]}})
     # parameter gradients of the fused path: accuracy of both outputs; bitwise
     # invariance of grad_hidden rows; grad_weight over the same complete sample
     # set (masked rows appended after the batch) bitwise
@@ -190,6 +206,14 @@ class Runner:
             if backward:
                 out = {"dlogits": ilp.logp_backward(batch["x"], batch["targets"], lse,
                                                     batch["grad"], batch["mask"])}
+        elif man["operator"] == "linear_logp_kept":
+            w = shared["weight"]
+            logp, lse, z = ilp.linear_logp_with_logits(batch["x"], w, batch["targets"],
+                                                       batch["mask"])
+            out = {"logp": logp, "lse": lse}
+            if backward:
+                out = {"dlogits": ilp.logp_backward(z, batch["targets"], lse, batch["grad"],
+                                                    batch["mask"], out=z)}
         else:
             w = shared["weight"]
             logp, lse = ilp.linear_logp(batch["x"], w, batch["targets"], batch["mask"])
@@ -403,7 +427,7 @@ def run_gate(quick=False, only=None):
         results.append(rec)
         drift += recs
     table = {}
-    for op in ("logp", "linear_logp", "linear_logp_params"):
+    for op in OPERATORS:
         for j in ("forward_accuracy", "forward_invariance", "gradient_accuracy", "gradient_invariance"):
             sel = [r for r in results if r["operator"] == op and r["judgment"] == j]
             if sel:

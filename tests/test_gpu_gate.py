@@ -10,7 +10,7 @@ pytestmark = pytest.mark.gpu
 def test_gate_quick_passes():
     report = gate.run_gate(quick=True)
     assert report["status"] == "pass", [c for c in report["cases"] if c["status"] != "pass"][:3]
-    for op in ("logp", "linear_logp"):
+    for op in ("logp", "linear_logp", "linear_logp_kept"):
         assert set(report["judgments"][op]) == {"forward_accuracy", "forward_invariance",
                                                 "gradient_accuracy", "gradient_invariance"}
     assert set(report["judgments"]["linear_logp_params"]) == {"gradient_accuracy",
