@@ -29,7 +29,10 @@
 //
 // The backward kernel runs the same per-tile main loop (same copies, same
 // MFMA sequence), so its z is bit-identical to the forward's, and replaces
-// the epilogue by d = g (onehot - 2^(z log2 e - lse log2 e)).
+// the epilogue by d = g (onehot - 2^(z log2 e - lse log2 e)).  A caller that
+// can hold N x V fp32 may instead have the forward keep its logits (the
+// kStoreLogits instantiation) and form the same gradient from them with an
+// elementwise pass (logits_rows.hip).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
