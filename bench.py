@@ -79,6 +79,15 @@ def measured_traffic():
     return {k: v["read_bytes"] + v["write_bytes"] for k, v in rec.get("per_launch", {}).items()}
 
 
+def _device_desc(torch, dev):
+    """Name, architecture and size of the device (the marketing name can be
+    empty on some driver stacks)."""
+    p = torch.cuda.get_device_properties(dev)
+    arch = getattr(p, "gcnArchName", "")
+    return (f"{p.name or 'AMD GPU'} ({arch}, {p.multi_processor_count} CUs, "
+            f"{p.total_memory / 2**30:.0f} GiB)")
+
+
 def calibrate_copy(torch):
     nbytes = 1 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
@@ -177,6 +186,12 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = {l: sum(a.elapsed_time(b) for a, b in events[l]) / args.steps for l in legs}
+    # per-launch spread of each leg over the timed steps: median, min, p90
+    spread = {}
+    for l in legs:
+        ts = sorted(a.elapsed_time(b) for a, b in events[l])
+        spread[l] = {"ms_median": ts[len(ts) // 2], "ms_min": ts[0],
+                     "ms_p90": ts[min(len(ts) - 1, int(0.9 * len(ts)))]}
     ms_per_step = wall * 1e3 / args.steps
 
     out_legs = {}
@@ -341,6 +356,8 @@ def main():
     if not args.no_cpu_baseline and "logits_fwd" in legs:
         cpu = cpu_baseline(c3, torch)
 
+    for l in out_legs:
+        out_legs[l].update(spread.get(l, {}))
     value = out_legs["logits_fwd"]["tokens_per_s"] if "logits_fwd" in legs else None
     rec = {
         "metric": METRIC,
@@ -361,6 +378,7 @@ def main():
                         "V=151936",
             "legs": legs,
             "global_batch": n3,
+            "seed": 0,
             "parallelism": "none (1 GPU)",
         },
         "legs": out_legs,
@@ -375,7 +393,7 @@ def main():
                            if "fused_fwd" in out_legs else None),
         "cpu_baseline": cpu,
         "build": ilp.build_info(),
-        "device": torch.cuda.get_device_name(dev),
+        "device": _device_desc(torch, dev),
         "input_generation_s": t_gen,
     }
     print(json.dumps(rec))
