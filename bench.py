@@ -49,6 +49,10 @@ def parse():
     p.add_argument("--calibrate-copy", action="store_true",
                    help="instead of the hot path, run a plain 1 GiB device copy 5 times "
                         "(reference for hardware traffic counters)")
+    p.add_argument("--yardsticks", action="store_true",
+                   help="instead of the hot path, time attainable-rate yardsticks with torch "
+                        "kernels: a streaming read, a fill, and the bf16 GEMMs of the fused "
+                        "shapes (comparison only; nothing of the library runs)")
     return p.parse_args()
 
 
@@ -88,6 +92,53 @@ def _device_desc(torch, dev):
             f"{p.total_memory / 2**30:.0f} GiB)")
 
 
+def yardsticks(torch):
+    """Attainable rates of torch's own kernels on the step's shapes, as a
+    comparison for the library's roofline fractions (prints one JSON line)."""
+    dev = torch.device("cuda:0")
+
+    def timed(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {}
+    x = torch.ones((16384, 151936), dtype=torch.bfloat16, device=dev)
+    nbytes = x.numel() * 2
+    ms = timed(lambda: torch.amax(x, dim=1))
+    out["read_rowmax_bf16"] = {"ms": ms, "GB_per_s": nbytes / (ms * 1e-3) / 1e9}
+    y = torch.empty((16384, 151936), dtype=torch.float32, device=dev)
+    ms = timed(lambda: y.fill_(1.0))
+    out["fill_fp32"] = {"ms": ms, "GB_per_s": y.numel() * 4 / (ms * 1e-3) / 1e9}
+    ms = timed(lambda: y.copy_(x))
+    out["convert_bf16_to_fp32"] = {"ms": ms, "GB_per_s": (nbytes + y.numel() * 4) / (ms * 1e-3) / 1e9}
+    del x, y
+    for n, v, h in ((8192, 128256, 4096), (2048, 151936, 5120)):
+        a = torch.randn((n, h), device=dev).to(torch.bfloat16)
+        w = torch.randn((v, h), device=dev).to(torch.bfloat16)
+        for odt in (torch.bfloat16, torch.float32):
+            if odt == torch.float32:
+                fn = lambda: torch.mm(a, w.t(), out_dtype=torch.float32)
+                try:
+                    fn()
+                except (TypeError, RuntimeError):
+                    continue
+            else:
+                fn = lambda: a @ w.t()
+            ms = timed(fn, 5)
+            out[f"gemm_{n}x{v}x{h}_{str(odt).split('.')[-1]}_out"] = {
+                "ms": ms, "TFLOP_per_s": 2.0 * n * v * h / (ms * 1e-3) / 1e12}
+        del a, w
+    print(json.dumps({"yardsticks": out, "torch": torch.__version__}))
+
+
 def calibrate_copy(torch):
     nbytes = 1 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
@@ -111,6 +162,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(torch)
+        return
+    if args.yardsticks:
+        yardsticks(torch)
         return
 
     import invariant_logprob_amd as ilp
