@@ -438,7 +438,7 @@ def main():
         "legs": out_legs,
         "extra_legs": extra,
         "roofline": roofline,
-        "fused_roofline": ({"kernel": "linear_tiles", "bound": "mfma",
+        "fused_roofline": ({"kernel": "linear_tiles_fwd", "bound": "mfma",
                             "achieved": out_legs["fused_fwd"]["TFLOP_per_s"],
                             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": out_legs["fused_fwd"]["mfma_frac"],

@@ -181,196 +181,154 @@ void linear_tiles_bwd(TileArgs args) {
   }
 }
 
-// Persistent forward: one workgroup per CU walks tiles blockIdx.x,
-// blockIdx.x + gridDim.x, ...; the LDS ring continues across tiles, so the
-// next tile's first K stage is in flight during this tile's last stage and
-// its epilogue.  The per-tile arithmetic (copies, MFMA sequence and K order)
-// is the same as linear_tiles_bwd's, so the backward recomputes the very same
-// logits.  With kStoreLogits the epilogue also writes the tile's fp32 logits
-// (every row below N, every column below V), straight from the accumulators.
+// Forward: one workgroup per tile, the tile core's main loop (the same copies
+// and MFMA sequence in the same K order as linear_tiles_bwd, so the backward
+// recomputes the very same logits), then the epilogue: per token, the (M, s)
+// partial of the tile's 256 logits (lane-local in (i, e) order, then the two
+// lane halves, then the two vocabulary waves through LDS) and, where the
+// target falls in the tile, its fp32 logit.  With kStoreLogits the epilogue
+// also writes the tile's fp32 logits (every row below N, every column below
+// V), straight from the accumulators.
 template <bool kStoreLogits>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void linear_tiles_fwd_persistent(TileArgs args) {
+void linear_tiles_fwd(TileArgs args) {
   __shared__ uint4 smem[2 * kStageVec];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wv = wave / kWQ;
   const int wt = wave % kWQ;
-  const int n_tiles = args.n_vtiles * args.n_tblocks;
-  const int H = args.H;
-  const int n_kt = (H + kBK - 1) / kBK;
-  const Loader ld = make_loader(wave, lane, args.ldw, args.ldh);
   struct Geo {
     int vt;
     int vocab0;
     int64_t tok0;
-    int V_tail;
-    int N_tail;
-    __amdgpu_buffer_rsrc_t wres;
-    __amdgpu_buffer_rsrc_t hres;
-  };
-  auto geo = [&](int t) {
-    Geo g;
-    int vt, tb;
-    tile_coords(t, args.n_vtiles, args.n_tblocks, vt, tb);
-    g.vt = vt;
-    g.vocab0 = vt * kBV;
-    g.tok0 = static_cast<int64_t>(tb) * kBT;
-    g.N_tail = static_cast<int>(min<int64_t>(args.N - g.tok0, kBT));
-    g.V_tail = min(args.V - g.vocab0, kBV);
-    g.wres = uniform_rsrc(args.weight + static_cast<int64_t>(g.vocab0) * args.ldw, g.V_tail * args.ldw * 2);
-    g.hres = uniform_rsrc(args.hidden + g.tok0 * args.ldh, g.N_tail * args.ldh * 2);
-    return g;
-  };
+    int V_tail;  // vocabulary entries of this tile below V
+    int N_tail;  // token rows of this tile below N
+  } cur;
+  int tb;
+  tile_coords(blockIdx.x, args.n_vtiles, args.n_tblocks, cur.vt, tb);
+  cur.vocab0 = cur.vt * kBV;
+  cur.tok0 = static_cast<int64_t>(tb) * kBT;
+  cur.N_tail = static_cast<int>(min<int64_t>(args.N - cur.tok0, kBT));
+  cur.V_tail = min(args.V - cur.vocab0, kBV);
+  // targets of this lane's token columns, loaded before the main loop's
+  // copies so that waiting for them never waits for a copy
+  int64_t tgt[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int tl = wt * kQW + j * 32 + (lane & 31);
+    tgt[j] = (tl < cur.N_tail) ? args.targets[cur.tok0 + tl] : -1;
+  }
+  // W rows past V and hidden rows past N lie outside the resources' ranges
+  // and read as zero.
+  const __amdgpu_buffer_rsrc_t wres = uniform_rsrc(
+      args.weight + static_cast<int64_t>(cur.vocab0) * args.ldw, cur.V_tail * args.ldw * 2);
+  const __amdgpu_buffer_rsrc_t hres =
+      uniform_rsrc(args.hidden + cur.tok0 * args.ldh, cur.N_tail * args.ldh * 2);
+  const Loader ld = make_loader(wave, lane, args.ldw, args.ldh);
+  f32x16_t acc[kI][kJ];
+  mainloop(smem, ld, wave, lane, wv, wt, wres, hres, args.H, acc);
 
-  int tile = blockIdx.x;
-  if (tile >= n_tiles) return;
-  Geo cur = geo(tile);
-  int g0 = 0;  // ring position of the current tile's stage 0
-  issue<0, kBlkPerWave>(smem, ld, wave, cur.wres, cur.hres, 0, 0, H);
-  for (;;) {
-    const int next = tile + gridDim.x;
-    const bool has_next = next < n_tiles;
-    const Geo nxt = geo(has_next ? next : tile);
-    // targets of this lane's token columns, loaded before any of this tile's
-    // copies so that waiting for them never waits for a copy
-    int64_t tgt[kJ];
+  const int half = lane >> 5;
+  const int vwave = cur.vocab0 + wv * 128;
+  // the main loop ended with a barrier: the whole LDS is free
+  float2* red = reinterpret_cast<float2*>(smem);
+  if constexpr (kStoreLogits) {
+    // Lane (l, l + 32) pairs write 32 contiguous bytes of a token's row; the
+    // four q steps of a block complete 128-byte lines.  The lane index and
+    // the row stride are opaque to the compiler here, or it hoists these
+    // per-lane offsets out of the tile loop, past the register budget.
+    int zl = lane;
+    asm volatile("" : "+v"(zl));
+    int64_t ldz = args.ldz;
+    asm volatile("" : "+s"(ldz));
+    const int zhalf = zl >> 5;
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
-      const int tl = wt * kQW + j * 32 + (lane & 31);
-      tgt[j] = (tl < cur.N_tail) ? args.targets[cur.tok0 + tl] : -1;
-    }
-    f32x16_t acc[kI][kJ];
-    zero(acc);
-    for (int kt = 0; kt < n_kt; ++kt) {
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-      const int buf = (g0 + kt) & 1;
-      const int nbuf = buf ^ 1;
-      const bool pf_same = (kt + 1) < n_kt;
-      const bool pf_next = !pf_same && has_next;
-      stage(
-          acc, smem + buf * kStageVec, wv, wt, lane,
-          [&] {
-            if (pf_same) issue<0, kBlkPerWave / 2>(smem, ld, wave, cur.wres, cur.hres, kt + 1, nbuf, H);
-            else if (pf_next) issue<0, kBlkPerWave / 2>(smem, ld, wave, nxt.wres, nxt.hres, 0, nbuf, H);
-          },
-          [&] {
-            if (pf_same)
-              issue<kBlkPerWave / 2, kBlkPerWave>(smem, ld, wave, cur.wres, cur.hres, kt + 1, nbuf, H);
-            else if (pf_next)
-              issue<kBlkPerWave / 2, kBlkPerWave>(smem, ld, wave, nxt.wres, nxt.hres, 0, nbuf, H);
-          });
-    }
-    // everyone is done reading the last stage's buffer; the next tile's
-    // stage 0 may still be landing in the other one
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const int free_buf = (g0 + n_kt - 1) & 1;
-    g0 += n_kt;
-
-    const int half = lane >> 5;
-    const int vwave = cur.vocab0 + wv * 128;
-    float2* red = reinterpret_cast<float2*>(smem + free_buf * kStageVec);
-    if constexpr (kStoreLogits) {
-      // Lane (l, l + 32) pairs write 32 contiguous bytes of a token's row; the
-      // four q steps of a block complete 128-byte lines.  The lane index and
-      // the row stride are opaque to the compiler here, or it hoists these
-      // per-lane offsets out of the tile loop, past the register budget.
-      int zl = lane;
-      asm volatile("" : "+v"(zl));
-      int64_t ldz = args.ldz;
-      asm volatile("" : "+s"(ldz));
-      const int zhalf = zl >> 5;
-#pragma unroll
-      for (int j = 0; j < kJ; ++j) {
-        const int tl = wt * kQW + j * 32 + (zl & 31);
-        if (tl < cur.N_tail) {
-          float* zrow = args.logits + (cur.tok0 + tl) * ldz + vwave + 4 * zhalf;
-#pragma unroll
-          for (int i = 0; i < kI; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int m = wv * 128 + i * 32 + 8 * q + 4 * zhalf;  // column - vocab0
-              float* dst = zrow + i * 32 + 8 * q;
-              if (m + 4 <= cur.V_tail) {
-                *reinterpret_cast<float4*>(dst) = make_float4(
-                    acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-              } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                  if (m + e < cur.V_tail) dst[e] = acc[i][j][4 * q + e];
-              }
-            }
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) {
-      const int tl = wt * kQW + j * 32 + (lane & 31);
-      const int64_t tok = cur.tok0 + tl;
-      // Row maximum, then the sum of exponentials in (i, e) order.  A full
-      // vocabulary tile (the common case, a uniform branch) needs no column
-      // test; a ragged last tile skips its columns past V.
-      float mx = neg_inf();
-      float M = neg_inf();
-      float s = 0.0f;
-      if (cur.V_tail >= kBV) {
-#pragma unroll
-        for (int i = 0; i < kI; ++i)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[i][j][e]);
-        const float Mu = lse_raise(M, s, mx);
-#pragma unroll
-        for (int i = 0; i < kI; ++i)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) s = s + lse_term(acc[i][j][e], Mu);
-      } else {
-#pragma unroll
-        for (int i = 0; i < kI; ++i)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int m = wv * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-            if (m < cur.V_tail) mx = fmaxf(mx, acc[i][j][e]);
-          }
-        const float Mu = lse_raise(M, s, mx);
-#pragma unroll
-        for (int i = 0; i < kI; ++i)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int m = wv * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-            if (m < cur.V_tail) s = s + lse_term(acc[i][j][e], Mu);
-          }
-      }
+      const int tl = wt * kQW + j * 32 + (zl & 31);
       if (tl < cur.N_tail) {
-        const int64_t t = tgt[j];
-        const int64_t d = t - vwave;
-        if (d >= 0 && d < 128) {
-          const int dd = static_cast<int>(d);
-          const int rem = dd & 31;
-          if (((rem >> 2) & 1) == half) {
-            // vocabulary row dd of this wave = block dd >> 5, element
-            // 4 ((dd & 31) >> 3) + (dd & 3)
-            const int idx = 16 * (dd >> 5) + (((rem >> 3) << 2) | (rem & 3));
-            args.zt[tok] = select_acc(acc, j, idx);
+        float* zrow = args.logits + (cur.tok0 + tl) * ldz + vwave + 4 * zhalf;
+#pragma unroll
+        for (int i = 0; i < kI; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int m = wv * 128 + i * 32 + 8 * q + 4 * zhalf;  // column - vocab0
+            float* dst = zrow + i * 32 + 8 * q;
+            if (m + 4 <= cur.V_tail) {
+              *reinterpret_cast<float4*>(dst) = make_float4(
+                  acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (m + e < cur.V_tail) dst[e] = acc[i][j][4 * q + e];
+            }
           }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int tl = wt * kQW + j * 32 + (lane & 31);
+    const int64_t tok = cur.tok0 + tl;
+    // Row maximum, then the sum of exponentials in (i, e) order.  A full
+    // vocabulary tile (the common case, a uniform branch) needs no column
+    // test; a ragged last tile skips its columns past V.
+    float mx = neg_inf();
+    float M = neg_inf();
+    float s = 0.0f;
+    if (cur.V_tail >= kBV) {
+#pragma unroll
+      for (int i = 0; i < kI; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[i][j][e]);
+      const float Mu = lse_raise(M, s, mx);
+#pragma unroll
+      for (int i = 0; i < kI; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s = s + lse_term(acc[i][j][e], Mu);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kI; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = wv * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+          if (m < cur.V_tail) mx = fmaxf(mx, acc[i][j][e]);
+        }
+      const float Mu = lse_raise(M, s, mx);
+#pragma unroll
+      for (int i = 0; i < kI; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = wv * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+          if (m < cur.V_tail) s = s + lse_term(acc[i][j][e], Mu);
+        }
+    }
+    if (tl < cur.N_tail) {
+      const int64_t t = tgt[j];
+      const int64_t d = t - vwave;
+      if (d >= 0 && d < 128) {
+        const int dd = static_cast<int>(d);
+        const int rem = dd & 31;
+        if (((rem >> 2) & 1) == half) {
+          // vocabulary row dd of this wave = block dd >> 5, element
+          // 4 ((dd & 31) >> 3) + (dd & 3)
+          const int idx = 16 * (dd >> 5) + (((rem >> 3) << 2) | (rem & 3));
+          args.zt[tok] = select_acc(acc, j, idx);
         }
       }
-      const float M2 = __shfl_xor(M, 32, 64);
-      const float s2 = __shfl_xor(s, 32, 64);
-      lse_merge(M, s, M2, s2);
-      if (half == 0) red[wv * kBT + tl] = make_float2(M, s);
     }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (tid < kBT) {
-      const int tl = tid;
-      float2 p0 = red[tl];
-      const float2 p1 = red[kBT + tl];
-      lse_merge(p0.x, p0.y, p1.x, p1.y);
-      if (tl < cur.N_tail) args.part[(cur.tok0 + tl) * args.n_vtiles + cur.vt] = p0;
-    }
-    if (!has_next) break;
-    tile = next;
-    cur = nxt;
+    const float M2 = __shfl_xor(M, 32, 64);
+    const float s2 = __shfl_xor(s, 32, 64);
+    lse_merge(M, s, M2, s2);
+    if (half == 0) red[wv * kBT + tl] = make_float2(M, s);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (tid < kBT) {
+    const int tl = tid;
+    float2 p0 = red[tl];
+    const float2 p1 = red[kBT + tl];
+    lse_merge(p0.x, p0.y, p1.x, p1.y);
+    if (tl < cur.N_tail) args.part[(cur.tok0 + tl) * args.n_vtiles + cur.vt] = p0;
   }
 }
 
@@ -458,26 +416,13 @@ hipError_t launch_linear_logp(const uint16_t* hidden, int64_t ldh, const uint16_
   const size_t part_bytes = ((static_cast<size_t>(n_vtiles) * N * sizeof(float2) + 255) / 256) * 256;
   a.part = reinterpret_cast<float2*>(workspace);
   a.zt = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + part_bytes);
-  // persistent forward: one workgroup per compute unit (the count only sets
-  // which workgroup runs which tile, never how a tile is computed)
-  const int64_t tiles = static_cast<int64_t>(a.n_vtiles) * a.n_tblocks;
-  int device = 0;
-  int cus = 256;
-  if (hipGetDevice(&device) == hipSuccess) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess &&
-        n > 0)
-      cus = n;
-  }
-  const int64_t grid = tiles < cus ? tiles : cus;
   a.logits = logits;
   a.ldz = ldz;
+  const uint32_t tiles = static_cast<uint32_t>(static_cast<int64_t>(a.n_vtiles) * a.n_tblocks);
   if (logits != nullptr)
-    hipLaunchKernelGGL(linear_tiles_fwd_persistent<true>, dim3(static_cast<uint32_t>(grid)),
-                       dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(linear_tiles_fwd<true>, dim3(tiles), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(linear_tiles_fwd_persistent<false>, dim3(static_cast<uint32_t>(grid)),
-                       dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(linear_tiles_fwd<false>, dim3(tiles), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(lse_chunk_combine,
