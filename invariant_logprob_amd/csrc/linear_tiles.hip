@@ -48,7 +48,7 @@ using namespace tile;
 
 constexpr int kBV = kLinearVocabTile;   // vocabulary entries per tile (= chunk): the P side
 constexpr int kBT = kLinearTokenTile;   // tokens per tile: the Q side
-constexpr int kStageStride = 132;       // floats per staged dlogits row (128 + 4 pad)
+constexpr int kStageStride = 132;       // floats per staged output row (128 + 4 pad)
 constexpr int kStagingVec = kWaves * 32 * kStageStride / 4;
 constexpr int kSmemVec = (2 * kStageVec > kStagingVec) ? 2 * kStageVec : kStagingVec;
 static_assert(kBV == kBP && kBT == kBQ, "vocabulary rows are the P side, tokens the Q side");
@@ -188,11 +188,12 @@ void linear_tiles_bwd(TileArgs args) {
 // lane halves, then the two vocabulary waves through LDS) and, where the
 // target falls in the tile, its fp32 logit.  With kStoreLogits the epilogue
 // also writes the tile's fp32 logits (every row below N, every column below
-// V), straight from the accumulators.
+// V), staged through the LDS as the backward stages its gradient.
 template <bool kStoreLogits>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void linear_tiles_fwd(TileArgs args) {
-  __shared__ uint4 smem[2 * kStageVec];
+  // the storing variant stages its logits through the LDS like the backward
+  __shared__ uint4 smem[kStoreLogits ? kSmemVec : 2 * kStageVec];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -234,36 +235,42 @@ void linear_tiles_fwd(TileArgs args) {
   // the main loop ended with a barrier: the whole LDS is free
   float2* red = reinterpret_cast<float2*>(smem);
   if constexpr (kStoreLogits) {
-    // Lane (l, l + 32) pairs write 32 contiguous bytes of a token's row; the
-    // four q steps of a block complete 128-byte lines.  The lane index and
-    // the row stride are opaque to the compiler here, or it hoists these
-    // per-lane offsets out of the tile loop, past the register budget.
-    int zl = lane;
-    asm volatile("" : "+v"(zl));
-    int64_t ldz = args.ldz;
-    asm volatile("" : "+s"(ldz));
-    const int zhalf = zl >> 5;
+    // the logits tile, staged through LDS one 32-token slice at a time so
+    // that each store instruction writes two 512-byte row segments (the main
+    // loop ended with a barrier, so the LDS is free)
+    float* stage = reinterpret_cast<float*>(smem) + wave * (32 * kStageStride);
+    float* srow = stage + (lane & 31) * kStageStride;
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
-      const int tl = wt * kQW + j * 32 + (zl & 31);
-      if (tl < cur.N_tail) {
-        float* zrow = args.logits + (cur.tok0 + tl) * ldz + vwave + 4 * zhalf;
 #pragma unroll
-        for (int i = 0; i < kI; ++i)
+      for (int i = 0; i < kI; ++i)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int m = wv * 128 + i * 32 + 8 * q + 4 * zhalf;  // column - vocab0
-            float* dst = zrow + i * 32 + 8 * q;
-            if (m + 4 <= cur.V_tail) {
-              *reinterpret_cast<float4*>(dst) = make_float4(
-                  acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-            } else {
+        for (int q = 0; q < 4; ++q) {
+          const int m0 = i * 32 + 8 * q + 4 * half;  // relative to vwave
+          *reinterpret_cast<float4*>(srow + m0) = make_float4(
+              acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        }
+      __syncthreads();
+#pragma unroll 4
+      for (int step = 0; step < 16; ++step) {
+        const int r = 2 * step + (lane >> 5);
+        const int c4 = lane & 31;
+        const int tr = wt * kQW + j * 32 + r;
+        if (tr < cur.N_tail) {
+          const float4 v = *reinterpret_cast<const float4*>(stage + r * kStageStride + 4 * c4);
+          const int mrel = wv * 128 + 4 * c4;  // relative to vocab0
+          float* dst = args.logits + (cur.tok0 + tr) * args.ldz + cur.vocab0 + mrel;
+          if (mrel + 4 <= cur.V_tail) {
+            store16_stream(dst, v.x, v.y, v.z, v.w);
+          } else {
+            const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (m + e < cur.V_tail) dst[e] = acc[i][j][4 * q + e];
-            }
+            for (int e = 0; e < 4; ++e)
+              if (mrel + e < cur.V_tail) dst[e] = vv[e];
           }
+        }
       }
+      __syncthreads();
     }
   }
 #pragma unroll
