@@ -106,7 +106,8 @@ int rlk_logp_entropy(const void* logits, int64_t ld, const int64_t* targets,
 
 /*
  * Dense log-softmax rows: out[i, j] = x_ij - lse_i, fp32 [N, ld_out]
- * (ld_out >= V, ld_out % 4 == 0, 16-B aligned; columns >= V not written),
+ * (ld_out >= V, ld_out % 4 == 0, 16-B aligned; columns >= V not written;
+ * a span that overlaps the logits' is RLK_ERR_INVALID_ARG),
  * with lse the forward's output for these rows (every log-probability of the
  * row: the dense path of page "[RFC] ...", section "Scope").  Inactive rows
  * are written as +0.0 and their logits are not read.  Elementwise, so each
@@ -151,6 +152,8 @@ int rlk_linear_logp(const void* hidden, int64_t ld_h, const void* weight,
  * involved, so each element depends only on its own row (page "[WS1 Test]
  * ...", section "Workstream 3 - #153": gradient batch invariance).
  *   Logits mode : `logits` non-NULL (bf16 [N, ld]); hidden/weight ignored.
+ *                 A grad_logits span that overlaps the logits' is
+ *                 RLK_ERR_INVALID_ARG.
  *   Fused mode  : `logits` NULL; x_i = W . h_i is recomputed with exactly
  *                 the tiles and K order rlk_linear_logp uses (hidden
  *                 [N, ld_h], weight [V, ld_w], H as there).

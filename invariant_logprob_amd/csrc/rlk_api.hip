@@ -62,6 +62,17 @@ int check_f32_rows(const void* p, int64_t ld, int64_t N, int64_t V) {
   return RLK_OK;
 }
 
+// Whether the byte spans of two row-major [N, ld] matrices (V elements of
+// each row used, N >= 1) intersect.
+bool rows_overlap(const void* a, int64_t lda, size_t asz, const void* b, int64_t ldb, size_t bsz,
+                  int64_t N, int64_t V) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a);
+  const uintptr_t a1 = a0 + static_cast<uintptr_t>((N - 1) * lda + V) * asz;
+  const uintptr_t b0 = reinterpret_cast<uintptr_t>(b);
+  const uintptr_t b1 = b0 + static_cast<uintptr_t>((N - 1) * ldb + V) * bsz;
+  return a0 < b1 && b0 < a1;
+}
+
 int check_sizes(int64_t N, int64_t V) {
   if (N < 0 || V < 1) return RLK_ERR_INVALID_ARG;
   if (N > kMaxN || V > kMaxV) return RLK_ERR_UNSUPPORTED;
@@ -157,6 +168,7 @@ int rlk_log_softmax(const void* logits, int64_t ld, const uint8_t* mask, const f
   if (ld_out > (int64_t(1) << 62) / N) return RLK_ERR_UNSUPPORTED;
   st = check_logits(logits, ld, N, V);
   if (st != RLK_OK) return st;
+  if (rows_overlap(logits, ld, 2, out, ld_out, sizeof(float), N, V)) return RLK_ERR_INVALID_ARG;
   return status_of(rlk::launch_log_softmax_rows(static_cast<const uint16_t*>(logits), ld, mask, lse,
                                                 N, static_cast<int>(V), out, ld_out, stream));
 }
@@ -219,13 +231,9 @@ int rlk_logp_backward_f32(const float* logits, int64_t ld, const int64_t* target
   if (st != RLK_OK) return st;
   // In place (the same buffer and stride) or disjoint; any other overlap of
   // the two [N, ld] spans would let a lane overwrite another lane's input.
-  if (grad_logits != logits || ld_g != ld) {
-    const uintptr_t a0 = reinterpret_cast<uintptr_t>(logits);
-    const uintptr_t a1 = a0 + static_cast<uintptr_t>((N - 1) * ld + V) * sizeof(float);
-    const uintptr_t b0 = reinterpret_cast<uintptr_t>(grad_logits);
-    const uintptr_t b1 = b0 + static_cast<uintptr_t>((N - 1) * ld_g + V) * sizeof(float);
-    if (a0 < b1 && b0 < a1) return RLK_ERR_INVALID_ARG;
-  }
+  if ((grad_logits != logits || ld_g != ld) &&
+      rows_overlap(logits, ld, sizeof(float), grad_logits, ld_g, sizeof(float), N, V))
+    return RLK_ERR_INVALID_ARG;
   return status_of(rlk::launch_logp_bwd_rows_f32(logits, ld, targets, mask, lse, grad_logp, N,
                                                  static_cast<int>(V), grad_logits, ld_g, stream));
 }
@@ -245,6 +253,9 @@ int rlk_logp_backward(const void* logits, int64_t ld, const void* hidden, int64_
   if (logits != nullptr) {
     st = check_logits(logits, ld, N, V);
     if (st != RLK_OK) return st;
+    // bf16 in, fp32 out: no overlap can be safe
+    if (rows_overlap(logits, ld, 2, grad_logits, ld_g, sizeof(float), N, V))
+      return RLK_ERR_INVALID_ARG;
     return status_of(rlk::launch_logp_bwd_rows(static_cast<const uint16_t*>(logits), ld, targets,
                                                mask, lse, grad_logp, N, static_cast<int>(V),
                                                grad_logits, ld_g, stream));

@@ -103,6 +103,18 @@ def test_backward_validation(lib):
     assert call(lg=NUL) == INVALID
     assert call(lg=NUL, h=A16, ldh=64, w=A16, ldw=64, H=0) == INVALID
     assert call(lg=NUL, h=A16, ldh=64, w=A2, ldw=64, H=64) == UNSUPPORTED
+    # logits mode reads bf16 and writes fp32: an output span that overlaps the
+    # logits' is refused (4 rows of 1024 bf16 span 8 KB from 0x10000)
+    assert call(out=A16) == INVALID
+    assert call(out=ctypes.c_void_p(0x10000 + 8 * 1024 - 16)) == INVALID   # ends of the spans
+    assert call(out=ctypes.c_void_p(0x10000 - 4 * (3 * 1024 + 1024) + 16)) == INVALID
+
+
+def test_dense_log_softmax_refuses_overlap(lib):
+    g = lib.rlk_log_softmax
+    assert g(A16, 1024, NUL, A16, 4, 1024, A16, 1024, NUL) == INVALID      # same base
+    assert g(A16, 1024, NUL, A16, 4, 1024, ctypes.c_void_p(0x10000 + 8 * 1024 - 16), 1024,
+             NUL) == INVALID
 
 
 def test_linear_logp_with_logits_validation(lib):
