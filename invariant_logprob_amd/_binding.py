@@ -146,6 +146,22 @@ def _mask(mask, n):
     return mask
 
 
+def _workspace(workspace, need, dev):
+    """The caller's workspace, or a new one: a contiguous GPU buffer of at
+    least `need` bytes on `dev`.  Returns (tensor, bytes)."""
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _device_of(workspace, "workspace")
+    if workspace.device != dev:
+        raise ValueError(f"workspace must be on {dev}, got {workspace.device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace too small: need {need} bytes, got {nbytes}")
+    return workspace, nbytes
+
+
 def _same_device(*ts):
     devs = {t.device for t in ts if t is not None}
     if len(devs) > 1:
@@ -266,17 +282,15 @@ def linear_logp(hidden, weight, targets, mask=None, *, workspace=None, logp=None
         logp = torch.empty(n, dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty(n, dtype=torch.float32, device=dev)
+    _rows(logp, "logp", n, torch.float32)
+    _rows(lse, "lse", n, torch.float32)
     if n == 0:
         return logp, lse
-    need = linear_logp_workspace_size(n, v, h)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    if workspace.numel() * workspace.element_size() < need:
-        raise ValueError(f"workspace too small: need {need} bytes")
+    workspace, ws_bytes = _workspace(workspace, linear_logp_workspace_size(n, v, h), dev)
     with torch.cuda.device(dev):
         st = lib.rlk_linear_logp(_ptr(hidden), ldh, _ptr(weight), ldw, _ptr(targets), _ptr(mask), n,
-                                 v, h, _ptr(logp), _ptr(lse), _ptr(workspace),
-                                 workspace.numel() * workspace.element_size(), _stream(dev))
+                                 v, h, _ptr(logp), _ptr(lse), _ptr(workspace), ws_bytes,
+                                 _stream(dev))
     _raise(st, "rlk_linear_logp")
     return logp, lse
 
@@ -301,19 +315,16 @@ def linear_logp_with_logits(hidden, weight, targets, mask=None, *, workspace=Non
         logp = torch.empty(n, dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty(n, dtype=torch.float32, device=dev)
+    _rows(logp, "logp", n, torch.float32)
+    _rows(lse, "lse", n, torch.float32)
     logits, ldz = _grad_out(logits, n, v, dev, "logits")
     if n == 0:
         return logp, lse, logits
-    need = linear_logp_workspace_size(n, v, h)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    if workspace.numel() * workspace.element_size() < need:
-        raise ValueError(f"workspace too small: need {need} bytes")
+    workspace, ws_bytes = _workspace(workspace, linear_logp_workspace_size(n, v, h), dev)
     with torch.cuda.device(dev):
         st = lib.rlk_linear_logp_with_logits(
             _ptr(hidden), ldh, _ptr(weight), ldw, _ptr(targets), _ptr(mask), n, v, h, _ptr(logp),
-            _ptr(lse), _ptr(logits), ldz, _ptr(workspace),
-            workspace.numel() * workspace.element_size(), _stream(dev))
+            _ptr(lse), _ptr(logits), ldz, _ptr(workspace), ws_bytes, _stream(dev))
     _raise(st, "rlk_linear_logp_with_logits")
     return logp, lse, logits
 
@@ -444,23 +455,20 @@ def linear_logp_param_grads(hidden, weight, targets, lse, grad_logp, mask=None, 
         gh, ld_gh = _param_out(grad_hidden, n, h, dev, "grad_hidden")
     if want_weight:
         gw, ld_gw = _param_out(grad_weight, v, h, dev, "grad_weight")
-    need = linear_logp_param_grads_workspace_size(n, v, h)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    if workspace.numel() * workspace.element_size() < need:
-        raise ValueError(f"workspace too small: need {need} bytes")
+    workspace, ws_bytes = _workspace(workspace, linear_logp_param_grads_workspace_size(n, v, h),
+                                     dev)
     with torch.cuda.device(dev):
         if logits is None:
             st = lib.rlk_linear_logp_param_grads(
                 _ptr(hidden), ldh, _ptr(weight), ldw, _ptr(targets), _ptr(mask), _ptr(lse),
                 _ptr(grad_logp), n, v, h, _ptr(gh), ld_gh, _ptr(gw), ld_gw, _ptr(workspace),
-                workspace.numel() * workspace.element_size(), _stream(dev))
+                ws_bytes, _stream(dev))
             _raise(st, "rlk_linear_logp_param_grads")
         else:
             st = lib.rlk_linear_logp_param_grads_from_logits(
                 _ptr(logits), ldz, _ptr(hidden), ldh, _ptr(weight), ldw, _ptr(targets),
                 _ptr(mask), _ptr(lse), _ptr(grad_logp), n, v, h, _ptr(gh), ld_gh, _ptr(gw), ld_gw,
-                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+                _ptr(workspace), ws_bytes, _stream(dev))
             _raise(st, "rlk_linear_logp_param_grads_from_logits")
     return gh, gw
 

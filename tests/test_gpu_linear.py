@@ -189,3 +189,42 @@ def test_fused_backward_schedules(dev):
         d_r = ilp.linear_logp_backward(b.hidden[r:r + 1], b.weight, b.targets[r:r + 1],
                                        lse[r:r + 1], b.grad[r:r + 1], b.mask[r:r + 1])
         assert _bits_equal(d_r, d[r:r + 1]), r
+
+
+def test_binding_refuses_bad_outputs_and_workspaces(dev):
+    """Caller-supplied outputs and workspaces are checked before any launch:
+    a short output or a workspace that is too small, strided or on the host
+    raises instead of letting a kernel write past it; an overlapping bf16
+    backward output is refused by the library."""
+    b = wl.fused_batch(40, 600, 64, seed=7, device=dev, w_sigma=0.05)
+    need = ilp.linear_logp_workspace_size(40, 600, 64)
+    short = torch.empty(39, dtype=torch.float32, device=dev)
+    for kw in ({"logp": short}, {"lse": short}):
+        with pytest.raises(ValueError):
+            ilp.linear_logp(b.hidden, b.weight, b.targets, **kw)
+        with pytest.raises(ValueError):
+            ilp.linear_logp_with_logits(b.hidden, b.weight, b.targets, **kw)
+    bad_ws = (torch.empty(need - 1, dtype=torch.uint8, device=dev),
+              torch.empty(2 * need, dtype=torch.uint8, device=dev)[::2],
+              torch.empty(need, dtype=torch.uint8))
+    for ws in bad_ws:
+        with pytest.raises(ValueError):
+            ilp.linear_logp(b.hidden, b.weight, b.targets, workspace=ws)
+        with pytest.raises(ValueError):
+            ilp.linear_logp_param_grads(b.hidden, b.weight, b.targets, b.grad, b.grad,
+                                        workspace=ws)
+    # a good caller workspace gives the same bits as an internal one
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    a = ilp.linear_logp(b.hidden, b.weight, b.targets, workspace=ws)
+    c = ilp.linear_logp(b.hidden, b.weight, b.targets)
+    torch.cuda.synchronize()
+    assert torch.equal(f32bits(a[0]), f32bits(c[0])) and torch.equal(f32bits(a[1]), f32bits(c[1]))
+    # bf16 logits and an fp32 output that shares their memory
+    buf = torch.zeros(8 * 1024, dtype=torch.float32, device=dev)
+    x = buf.view(torch.bfloat16)[: 4 * 1024].view(4, 1024)
+    t = torch.zeros(4, dtype=torch.int64, device=dev)
+    lse = torch.zeros(4, dtype=torch.float32, device=dev)
+    with pytest.raises(ilp.RlkError) as e:
+        ilp.logp_backward(x, t, lse, lse, out=buf[: 4 * 1024].view(4, 1024))
+    assert e.value.status == 1
+    torch.cuda.synchronize()
