@@ -8,9 +8,10 @@ One step is one pass of the whole hot path over resident synthetic inputs:
               V=151936                                    (kernel logp_fwd_rows)
   logits_bwd  its backward, fp32 dlogits [16384, 151936]  (logp_bwd_rows)
   fused_fwd   lm_head + selected logprob, hidden [8192, 4096], W [128256, 4096]
-                                                          (linear_tiles + lse_chunk_combine)
+                                                          (linear_tiles_fwd + lse_chunk_combine)
   fused_fb    fused forward + backward, hidden [2048, 5120], W [151936, 5120]
-                                                          (linear_tiles x2 + combine)
+                                                          (linear_tiles_fwd, lse_chunk_combine,
+                                                           linear_tiles_bwd)
 
 The headline value is the selected-logprob throughput at V=151936: active
 tokens per second of the logits forward.  Each leg is timed with HIP events
@@ -43,8 +44,8 @@ def parse():
     p.add_argument("--legs", default="logits_fwd,logits_bwd,fused_fwd,fused_fb")
     p.add_argument("--extra-legs",
                    default="logits_entropy,log_softmax,token_losses,fused_param_grads,"
-                           "fused_fb_kept_logits,fused_param_grads_kept_logits,logits_small,"
-                           "logits_varlen",
+                           "fused_fb_kept_logits,fused_param_grads_kept_logits,fused_fwd_n1,"
+                           "logits_small,logits_varlen",
                    help="rows beyond the hot path, timed after the steps (not part of a step)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="instead of the hot path, run a plain 1 GiB device copy 5 times "
@@ -281,7 +282,7 @@ def main():
                                 "dlogits_bytes": n5 * v5 * 4}
     if roofline is None and "fused_fwd" in legs:
         f = out_legs["fused_fwd"]
-        roofline = {"kernel": "linear_tiles", "bound": "mfma", "achieved": f["TFLOP_per_s"],
+        roofline = {"kernel": "linear_tiles_fwd", "bound": "mfma", "achieved": f["TFLOP_per_s"],
                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": f["mfma_frac"],
                     "traffic": None}
 
@@ -337,6 +338,16 @@ def main():
             ilp.logp_backward(d5, c5.targets, lse5, c5.grad, c5.mask, out=d5)
         xfns["fused_fb_kept_logits"] = (kept, n5 * h5 * 2 + v5 * h5 * 2 + 2 * n5 * v5 * 4 * 2)
         xflops["fused_fb_kept_logits"] = 2.0 * n5 * v5 * h5
+    if c4 is not None and "fused_fwd_n1" in args.extra_legs.split(","):
+        # one row of the fused forward workload: the kernel and schedule are
+        # those of any N, and the W stream (V x H bf16) is the algorithmic
+        # traffic that bounds it
+        h41, t41, m41 = c4.hidden[:1], c4.targets[:1], c4.mask[:1]
+        lp41 = torch.empty(1, dtype=torch.float32, device=dev)
+        ls41 = torch.empty(1, dtype=torch.float32, device=dev)
+        xfns["fused_fwd_n1"] = (
+            lambda: ilp.linear_logp(h41, c4.weight, t41, m41, workspace=ws4, logp=lp41, lse=ls41),
+            v4 * h4 * 2 + h4 * 2 + 8 + 1 + 8)
     for name in [x for x in args.extra_legs.split(",") if x in xfns]:
         fn, nbytes = xfns[name]
         for _ in range(max(1, args.warmup)):

@@ -276,18 +276,51 @@ __device__ __forceinline__ LoaderG<LP, LQ> make_loader_g(int wave, int lane, int
   return L;
 }
 
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// The four words of a raw buffer resource over [base, base + bytes) (stride
+// 0), from wave-uniform values so that they live in scalar registers.
+__device__ __forceinline__ i32x4_t uniform_desc(const uint16_t* base, int64_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4_t d;
+  d.x = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(p)));
+  d.y = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(p >> 32) & 0xffffu));
+  d.z = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  d.w = kBufferResourceWord3;
+  return d;
+}
+
 // Buffer resource and scalar offset of one side for the stage starting at k0.
 template <Lay L>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t side_rsrc(const Side& s, int k0, int& soff) {
+__device__ __forceinline__ i32x4_t side_desc(const Side& s, int k0, int& soff) {
   if constexpr (L == Lay::kRows) {
     soff = k0 * 2;
-    return uniform_rsrc(s.ptr, static_cast<int64_t>(s.extent) * s.ld * 2);
+    return uniform_desc(s.ptr, static_cast<int64_t>(s.extent) * s.ld * 2);
   } else {
     soff = 0;
     const int rows = min(max(s.extent - k0, 0), kBK);
     const int64_t elems = rows > 0 ? static_cast<int64_t>(rows) * s.ld - s.col0 : 0;
-    return uniform_rsrc(s.ptr + static_cast<int64_t>(k0) * s.ld, elems * 2);
+    return uniform_desc(s.ptr + static_cast<int64_t>(k0) * s.ld, elems * 2);
   }
+}
+
+// One wave's 16-byte-per-lane copy from a buffer into the LDS at dst (lane l
+// writes dst + 16 l), written as the instruction itself.  The compiler,
+// seeing a direct-to-LDS load through its builtin, makes every later
+// transposing LDS read wait for it (vmcnt(0)) although the two touch
+// different stage buffers; the caller's stage-top wait and barrier are what
+// make the copied data visible.
+__device__ __forceinline__ void copy16_to_lds(i32x4_t desc, uint4* dst, int voff, int soff) {
+  const int m = __builtin_amdgcn_readfirstlane(
+      static_cast<int>(reinterpret_cast<uintptr_t>(to_lds(dst))));
+  // M0 holds the LDS destination (an input bound to that register); one
+  // wait state separates the M0 write from the copy that reads it
+  asm volatile(
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
+      : "v"(voff), "s"(desc), "s"(soff), "{m0}"(m)
+      : "memory");
 }
 
 template <int Q0, int Q1, Lay LP, Lay LQ>
@@ -298,8 +331,8 @@ __device__ __forceinline__ void issue_g(uint4* smem, const LoaderG<LP, LQ>& L, i
   uint4* a = smem + st * kStageVec;
   uint4* b = a + kPVec;
   int sp, sq;
-  const __amdgpu_buffer_rsrc_t pres = side_rsrc<LP>(P, k0, sp);
-  const __amdgpu_buffer_rsrc_t qres = side_rsrc<LQ>(Q, k0, sq);
+  const i32x4_t pres = side_desc<LP>(P, k0, sp);
+  const i32x4_t qres = side_desc<LQ>(Q, k0, sq);
 #pragma unroll
   for (int q = Q0; q < Q1; ++q) {
     const int blk = wave * kBlkPerWave + q;
@@ -310,8 +343,8 @@ __device__ __forceinline__ void issue_g(uint4* smem, const LoaderG<LP, LQ>& L, i
     if constexpr (LQ == Lay::kRows) {
       if (!full && (k0 + L.kcol_q[q]) >= K) vq = kOutOfRange;
     }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(pres, to_lds(a + blk * 64), 16, vp, sp, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(qres, to_lds(b + blk * 64), 16, vq, sq, 0, 0);
+    copy16_to_lds(pres, a + blk * 64, vp, sp);
+    copy16_to_lds(qres, b + blk * 64, vq, sq);
   }
 }
 
