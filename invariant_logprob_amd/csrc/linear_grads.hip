@@ -347,7 +347,7 @@ void grad_gemm_tiles(GemmArgs args) {
             const float4 o = *reinterpret_cast<const float4*>(dst);
             v = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
           }
-          *reinterpret_cast<float4*>(dst) = v;
+          store16_stream(dst, v.x, v.y, v.z, v.w);
         } else {
           const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
