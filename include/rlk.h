@@ -212,7 +212,10 @@ int rlk_logp_backward_f32(const float* logits, int64_t ld,
 /*
  * Bytes of device workspace rlk_linear_logp_param_grads needs for (N, V, H):
  * one vocabulary chunk of the logits gradient in bf16, [N, C] with
- * C = min(16384, V rounded up to 256), rounded up to 256 bytes.
+ * C = min(16384, V rounded up to 256), then a bf16 [N, H] copy of hidden
+ * with the inactive rows zeroed (used when a mask is given, so that an
+ * inactive row's contents, whatever they are, add nothing to grad_weight),
+ * each part rounded up to 256 bytes.
  */
 size_t rlk_linear_logp_param_grads_workspace_size(int64_t N, int64_t V,
                                                   int64_t H);

@@ -376,17 +376,43 @@ __global__ __launch_bounds__(256) void zero_rows_f32(float* __restrict__ out, in
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 
-// Workspace: one chunk of D in bf16, [N, chunk].
-size_t grad_workspace(int64_t N, int64_t V) {
+// dst[r][0, H) = src[r][0, H) for active rows, +0 for inactive ones
+// (H % 8 == 0, 16-byte aligned rows).  An inactive token's D row is zero,
+// but its hidden row may hold anything, and 0 x inf or 0 x NaN would still
+// reach every entry of grad_weight through the product; with the row zeroed
+// the inactive token adds exact zeros, as the definition (a sum over active
+// tokens) has it.
+__global__ __launch_bounds__(256) void active_rows_bf16(const uint16_t* __restrict__ src,
+                                                        int64_t lds, const uint8_t* __restrict__ mask,
+                                                        int64_t rows, int cols,
+                                                        uint16_t* __restrict__ dst, int64_t ldd) {
+  const int64_t vecs = static_cast<int64_t>(cols / 8);
+  const int64_t total = rows * vecs;
+  for (int64_t k = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; k < total;
+       k += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t r = k / vecs;
+    const int64_t c = (k - r * vecs) * 8;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (mask[r] != 0) v = *reinterpret_cast<const uint4*>(src + r * lds + c);
+    *reinterpret_cast<uint4*>(dst + r * ldd + c) = v;
+  }
+}
+
+// Workspace: one chunk of D in bf16, [N, chunk], then (used when a mask is
+// given) a copy of hidden, [N, H] bf16, with inactive rows zeroed.
+int64_t grad_d_bytes(int64_t N, int64_t V) {
   const int64_t chunk = min64(kGradChunk, round_up(V, kBP));
-  return static_cast<size_t>(round_up(N * chunk * 2, 256));
+  return round_up(N * chunk * 2, 256);
+}
+
+size_t grad_workspace(int64_t N, int64_t V, int64_t H) {
+  return static_cast<size_t>(grad_d_bytes(N, V) + round_up(N * H * 2, 256));
 }
 
 }  // namespace
 
 size_t linear_param_grads_workspace_bytes(int64_t N, int64_t V, int64_t H) {
-  (void)H;
-  return grad_workspace(N, V);
+  return grad_workspace(N, V, H);
 }
 
 hipError_t launch_linear_param_grads(const uint16_t* hidden, int64_t ldh, const uint16_t* weight,
@@ -410,6 +436,22 @@ hipError_t launch_linear_param_grads(const uint16_t* hidden, int64_t ldh, const 
   const int64_t chunk = min64(kGradChunk, round_up(V, kBP));
   const bool want_h = grad_hidden != nullptr;
   const bool want_w = grad_weight != nullptr;
+  // grad_weight's token operand: hidden itself, or with a mask a copy whose
+  // inactive rows are zero (made once for all chunks)
+  const uint16_t* hw = hidden;
+  int64_t ldhw = ldh;
+  if (want_w && mask != nullptr) {
+    uint16_t* hcopy = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) +
+                                                  grad_d_bytes(N, V));
+    const int64_t vecs = N * (H / 8);
+    const int64_t blocks = min64((vecs + 255) / 256, 65536);
+    hipLaunchKernelGGL(active_rows_bf16, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
+                       hidden, ldh, mask, N, H, hcopy, static_cast<int64_t>(H));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hw = hcopy;
+    ldhw = H;
+  }
   const int n_vtiles = (V + kBP - 1) / kBP;
   const int n_tblocks = static_cast<int>((N + kBQ - 1) / kBQ);
   const int tiles_per_chunk = static_cast<int>(chunk / kBP);
@@ -481,8 +523,8 @@ hipError_t launch_linear_param_grads(const uint16_t* hidden, int64_t ldh, const 
       // grad_weight[vocab rows, H] = D_c^T . h: P = hidden and Q = D_c, both
       // read K-major (token rows)
       GemmOp& o = ga.op[ga.n_ops++];
-      o.p = hidden;
-      o.ldp = ldh;
+      o.p = hw;
+      o.ldp = ldhw;
       o.P = H;
       o.kext_p = static_cast<int>(N);
       o.q = d;

@@ -281,3 +281,33 @@ def test_padded_leading_dimensions(dev):
     assert _bits_equal(gh2, gh) and _bits_equal(gw2, gw)
     # columns past H of the output buffers are never written
     assert bool(torch.isnan(gh_buf[:, h:]).all()) and bool(torch.isnan(gw_buf[:, h:]).all())
+
+
+def test_inactive_rows_may_hold_anything(dev):
+    """Inactive tokens add nothing, whatever their hidden rows hold: with NaN
+    and infinities in masked rows (padding is often uninitialised memory),
+    both gradients, the forward and the logits backward equal, bit for bit,
+    those of the same batch with those rows zeroed."""
+    n, v, h = 300, 17000, 136
+    b = wl.fused_batch(n, v, h, seed=77, device=dev, w_sigma=0.05, n_masked=30)
+    masked = torch.nonzero(b.mask == 0).flatten()[:3]
+    poisoned = b.hidden.clone()
+    poisoned[masked[0], 5] = float("nan")
+    poisoned[masked[1], :] = float("inf")
+    poisoned[masked[2], ::3] = float("-inf")
+    clean = b.hidden.clone()
+    clean[masked] = 0
+    outs = []
+    for hid in (poisoned, clean):
+        logp, lse = ilp.linear_logp(hid, b.weight, b.targets, b.mask)
+        d = ilp.linear_logp_backward(hid, b.weight, b.targets, lse, b.grad, b.mask)
+        gh, gw = ilp.linear_logp_param_grads(hid, b.weight, b.targets, lse, b.grad, b.mask)
+        _, _, z = ilp.linear_logp_with_logits(hid, b.weight, b.targets, b.mask)
+        gh2, gw2 = ilp.linear_logp_param_grads(hid, b.weight, b.targets, lse, b.grad, b.mask,
+                                               logits=z)
+        torch.cuda.synchronize()
+        outs.append([logp, lse, d, gh, gw, gh2, gw2])
+    assert bool(torch.isfinite(outs[0][4]).all()), "grad_weight took in an inactive row"
+    for name, a, c in zip(("logp", "lse", "dlogits", "grad_hidden", "grad_weight",
+                           "grad_hidden (kept)", "grad_weight (kept)"), outs[0], outs[1]):
+        assert _bits_equal(a, c), name
