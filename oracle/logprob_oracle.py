@@ -327,7 +327,11 @@ def linear_param_grads_from_f64(h, w, targets, mask, lse, grad_logp):
     if h.shape[1] != w.shape[1]:
         raise ValueError("hidden and weight disagree on H")
     d = logp_backward_from_f64(h @ w.T, targets, mask, lse, grad_logp)
-    return d @ w, d.T @ h
+    # grad_weight sums over the active tokens only: an inactive row's D is
+    # zero, and leaving its hidden row out keeps whatever that row holds
+    # (non-finite padding included) out of the sum
+    act = _active(mask, h.shape[0])
+    return d @ w, d[act].T @ h[act]
 
 
 def linear_param_grads(hidden_bits, weight_bits, targets, mask, lse, grad_logp):
@@ -388,4 +392,4 @@ def linear_grad_weight_rows(hidden_bits, weight_bits, targets, mask, lse, grad_l
     d[rows] = -g[rows, None] * np.exp(z[rows] - ls[rows, None])
     for i in rows:
         d[i, vocab_rows == t[i]] += g[i]
-    return d.T @ h
+    return d[rows].T @ h[rows]

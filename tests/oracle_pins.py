@@ -589,6 +589,19 @@ def pin_param_grads_invariants(o):
     gh_c, gw_c = o.linear_param_grads(hb[keep], wb, t[keep], None, lse[keep], g[keep])
     assert np.max(np.abs(gh_c - gh[keep])) <= 1e-13
     assert np.max(np.abs(gw_c - gw)) <= 1e-13
+    # what an inactive row holds does not matter, NaN and infinities included
+    # (grad_W is a sum over the active tokens)
+    hp = hb.copy()
+    hp[1, :] = 0x7FC0                 # NaN
+    hp[4, ::2] = 0x7F80               # +inf
+    hp[4, 1::2] = 0xFF80              # -inf
+    with np.errstate(invalid="ignore", over="ignore"):   # the poisoned rows' own logits
+        gh_p, gw_p = o.linear_param_grads(hp, wb, t, mask, lse, g)
+        vr = [int(t[0]), 3, v - 1]
+        gw_r = o.linear_grad_weight_rows(hp, wb, t, mask, lse, g, vr)
+    assert np.all(np.isfinite(gw_p)) and np.array_equal(gw_p, gw)
+    assert np.array_equal(gh_p, gh)
+    assert np.array_equal(gw_r, gw[vr])
 
 
 ALL_PINS += [pin_param_grads_finite_differences, pin_param_grads_closed_forms,
