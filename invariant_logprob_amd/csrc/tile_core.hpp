@@ -139,13 +139,11 @@ __device__ __forceinline__ void frag(const uint4* a, int kk, int wp, int wq, int
 
 __device__ __forceinline__ void mma(f32x16_t (&acc)[kI][kJ], const bf16x8_t (&fa)[kI],
                                     const bf16x8_t (&fb)[kJ]) {
-  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int i = 0; i < kI; ++i)
 #pragma unroll
     for (int j = 0; j < kJ; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-  __builtin_amdgcn_s_setprio(0);
 }
 
 __device__ __forceinline__ void zero(f32x16_t (&acc)[kI][kJ]) {
