@@ -31,13 +31,6 @@ COMMON = [
 ]
 
 
-# Per-source code-generation options.  The row kernels (logits forward,
-# backward, dense log-softmax) schedule for instruction-level parallelism:
-# their loads then issue earlier among the exponentials; it is an instruction
-# order only, so their results are unchanged.
-SOURCE_FLAGS = {"logits_rows.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
-
-
 def git_rev():
     try:
         rev = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"],
@@ -66,7 +59,7 @@ def build(verbose=False):
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([HIPCC, *COMMON, *SOURCE_FLAGS.get(src, []), *defs, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *COMMON, *defs, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
         for err in ex.map(_run, cmds):
             if verbose and err:
