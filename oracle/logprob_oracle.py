@@ -164,13 +164,24 @@ def logp_backward_from_f64(x, targets, mask, lse, grad_logp):
     padding is excluded and the upstream gradients are identical across
     configurations; the formula itself is the textbook derivative of the
     definition above).
+
+    ``lse`` is the log-sum-exp of each row.  ``None`` means the oracle's own,
+    computed here from the same logits: the gradient of the whole definition,
+    from the inputs alone (the end-to-end reference).  A given array makes
+    this the backward as a function of that lse.
     """
     x = np.asarray(x, dtype=np.float64)
     n, v = x.shape
     t = np.asarray(targets, dtype=np.int64).reshape(n)
     act = _active(mask, n)
     g = np.asarray(grad_logp, dtype=np.float64).reshape(n)
-    ls = np.asarray(lse, dtype=np.float64).reshape(n)
+    if lse is None:
+        ls = np.zeros(n)
+        rows_a = np.nonzero(act)[0]
+        if rows_a.size:
+            ls[rows_a] = logsumexp_rows(x[rows_a])
+    else:
+        ls = np.asarray(lse, dtype=np.float64).reshape(n)
     d = np.zeros((n, v))
     rows = np.nonzero(act)[0]
     if rows.size:
@@ -184,13 +195,14 @@ def logp_backward_from_f64(x, targets, mask, lse, grad_logp):
 
 
 def logp_backward(logits_bits, targets, mask, lse, grad_logp):
-    """Backward from bf16 logits (raw uint16 [N, V]); float64 [N, V]."""
+    """Backward from bf16 logits (raw uint16 [N, V]); float64 [N, V].
+    ``lse`` None: the oracle's own (see logp_backward_from_f64)."""
     return logp_backward_from_f64(bf16_to_f64(logits_bits), targets, mask, lse, grad_logp)
 
 
 def linear_logp_backward(hidden_bits, weight_bits, targets, mask, lse, grad_logp):
     """Backward of the fused path with respect to the (never materialised)
-    logits z = h . W^T; float64 [N, V]."""
+    logits z = h . W^T; float64 [N, V].  ``lse`` None: the oracle's own."""
     z = linear_logits(hidden_bits, weight_bits)
     return logp_backward_from_f64(z, targets, mask, lse, grad_logp)
 
@@ -321,7 +333,8 @@ def linear_param_grads_from_f64(h, w, targets, mask, lse, grad_logp):
     """(grad_hidden [N, H], grad_weight [V, H]) float64 for float64 h, W.
 
     ``lse`` is the forward's log-sum-exp per row (an input of the backward,
-    as for the logits gradient)."""
+    as for the logits gradient); None means the oracle's own from the same
+    h and W (the end-to-end reference)."""
     h = np.asarray(h, dtype=np.float64)
     w = np.asarray(w, dtype=np.float64)
     if h.shape[1] != w.shape[1]:
@@ -346,7 +359,7 @@ def linear_grad_hidden_rows(hidden_bits, weight_bits, targets, mask, lse, grad_l
 
     The same formula as linear_param_grads for a few token rows of a large
     problem; the weight is visited in blocks of vocabulary rows only to bound
-    host memory."""
+    host memory.  ``lse`` None: the oracle's own, for these rows."""
     hb = np.asarray(hidden_bits, dtype=np.uint16)
     wb = np.asarray(weight_bits, dtype=np.uint16)
     n = hb.shape[0]
@@ -354,8 +367,14 @@ def linear_grad_hidden_rows(hidden_bits, weight_bits, targets, mask, lse, grad_l
     t = np.asarray(targets, dtype=np.int64).reshape(n)
     act = _active(mask, n)
     g = np.asarray(grad_logp, dtype=np.float64).reshape(n)
-    ls = np.asarray(lse, dtype=np.float64).reshape(n)
     rows = [int(r) for r in rows]
+    if lse is None:
+        ls = np.zeros(n)
+        sel = np.asarray(rows, dtype=np.int64)
+        _, ls_rows = linear_logp(hb[sel], wb, t[sel], act[sel])
+        ls[sel] = ls_rows
+    else:
+        ls = np.asarray(lse, dtype=np.float64).reshape(n)
     out = np.zeros((len(rows), hh))
     h = bf16_to_f64(hb[rows])
     for k0 in range(0, v, block):
@@ -376,13 +395,17 @@ def linear_grad_hidden_rows(hidden_bits, weight_bits, targets, mask, lse, grad_l
 
 def linear_grad_weight_rows(hidden_bits, weight_bits, targets, mask, lse, grad_logp, vocab_rows):
     """Rows ``vocab_rows`` of grad_weight = D^T . h (float64 [len, H]): the
-    same formula as linear_param_grads for a few vocabulary rows."""
+    same formula as linear_param_grads for a few vocabulary rows.  ``lse``
+    None: the oracle's own (a full forward over every row)."""
     hb = np.asarray(hidden_bits, dtype=np.uint16)
     n = hb.shape[0]
     t = np.asarray(targets, dtype=np.int64).reshape(n)
     act = _active(mask, n)
     g = np.asarray(grad_logp, dtype=np.float64).reshape(n)
-    ls = np.asarray(lse, dtype=np.float64).reshape(n)
+    if lse is None:
+        _, ls = linear_logp(hb, weight_bits, t, act)
+    else:
+        ls = np.asarray(lse, dtype=np.float64).reshape(n)
     vocab_rows = np.asarray(vocab_rows, dtype=np.int64)
     h = bf16_to_f64(hb)
     w = bf16_to_f64(np.asarray(weight_bits, dtype=np.uint16)[vocab_rows])

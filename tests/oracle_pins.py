@@ -295,6 +295,8 @@ def pin_backward_finite_differences(o):
         g = float(rng.standard_normal())
         _, lse = o.selected_logp_from_f64(x, t)
         d = o.logp_backward_from_f64(x, t, None, lse, [g])
+        # with no lse given the oracle takes its own: the same gradient
+        d_own = o.logp_backward_from_f64(x, t, None, None, [g])
         eps = 1e-6
         for j in range(v):
             xp = x.copy()
@@ -305,6 +307,7 @@ def pin_backward_finite_differences(o):
             fm = o.selected_logp_from_f64(xm, t)[0][0]
             fd = g * (fp - fm) / (2 * eps)
             assert abs(d[0, j] - fd) <= 1e-7 * (1 + abs(g)), (v, j, d[0, j], fd)
+            assert abs(d_own[0, j] - fd) <= 1e-7 * (1 + abs(g)), (v, j, d_own[0, j], fd)
 
 
 def pin_backward_mask(o):
@@ -526,8 +529,10 @@ def pin_param_grads_finite_differences(o):
         lse[i] = math.log(math.fsum(math.exp(a) for a in z))
     gh, gw = o.linear_param_grads_from_f64(hf, wf, t, mask, lse, g)
     assert gh.shape == (n, hh) and gw.shape == (v, hh), (gh.shape, gw.shape)
+    # with no lse given the oracle takes its own from the same h and W
+    gh_own, gw_own = o.linear_param_grads_from_f64(hf, wf, t, mask, None, g)
     eps = 1e-6
-    for arr, grad in ((hf, gh), (wf, gw)):
+    for arr, grad in ((hf, gh), (wf, gw), (hf, gh_own), (wf, gw_own)):
         for idx in np.ndindex(arr.shape):
             keep = arr[idx]
             arr[idx] = keep + eps
@@ -627,6 +632,11 @@ def pin_param_grad_row_samplers(o):
     vr = [int(t[0]), 5, v - 1]
     gw_s = o.linear_grad_weight_rows(hb, wb, t, mask, lse, g, vr)
     assert np.max(np.abs(gw_s - gw[vr])) <= 1e-13
+    # with no lse given, the samplers take the oracle's own
+    gh_o = o.linear_grad_hidden_rows(hb, wb, t, mask, None, g, rows, block=16)
+    gw_o = o.linear_grad_weight_rows(hb, wb, t, mask, None, g, vr)
+    assert np.max(np.abs(gh_o - gh[rows])) <= 1e-13
+    assert np.max(np.abs(gw_o - gw[vr])) <= 1e-13
 
 
 ALL_PINS += [pin_param_grad_row_samplers]
