@@ -50,6 +50,15 @@
  *    owns every buffer.  Outputs are fully overwritten (no accumulation).
  *  - N == 0 is a no-op returning RLK_OK.  Arguments are validated before any
  *    launch; on error nothing is launched.
+ *  - Supported sizes (beyond them RLK_ERR_UNSUPPORTED, before any launch):
+ *    N <= 2^31 - 1 and V <= 2^28 everywhere (the row kernels loop over rows
+ *    beyond their grid, so any such N is launched, memory permitting);
+ *    N * ld < 2^62 for every [N, ld] matrix.  Fused entry points: H <= 2^22
+ *    - 8, ld_h, ld_w < 2^22, and ceil(N / 256) * ceil(V / 256) < 2^23 (one
+ *    workgroup per 256 x 256 tile, and a launch holds fewer than 2^32
+ *    work-items: at V = 151936 that is N up to about 3.6 million rows).
+ *    Parameter gradients: N <= 2^22 - 16 and ceil(H / 256) * (ceil(N / 256)
+ *    + min(V, 16384) / 256) within the same 2^23-tile launch bound.
  *  - There is no fallback path: the kernels exist for gfx950 only.
  */
 #ifndef RLK_H
@@ -70,8 +79,8 @@ enum rlk_status {
                               ld < V (or < H), workspace too small,
                               lse missing in the backward */
   RLK_ERR_UNSUPPORTED = 2, /* alignment / leading-dimension rule violated,
-                              or a size beyond the supported range
-                              (V, H < 2^31, N * ld < 2^62) */
+                              or a size beyond the supported range (see
+                              "Supported sizes" above) */
   RLK_ERR_LAUNCH = 3       /* the HIP runtime reported an error at launch */
 };
 
@@ -211,11 +220,12 @@ int rlk_logp_backward_f32(const float* logits, int64_t ld,
 
 /*
  * Bytes of device workspace rlk_linear_logp_param_grads needs for (N, V, H):
- * one vocabulary chunk of the logits gradient in bf16, [N, C] with
- * C = min(16384, V rounded up to 256), then a bf16 [N, H] copy of hidden
- * with the inactive rows zeroed (used when a mask is given, so that an
- * inactive row's contents, whatever they are, add nothing to grad_weight),
- * each part rounded up to 256 bytes.
+ * one vocabulary chunk of the logits gradient as two bf16 arrays (its bf16
+ * rounding and the rounding's remainder), each [N, C] with C = min(16384, V
+ * rounded up to 256), then a bf16 [N, H] copy of hidden with the inactive
+ * rows zeroed (used when a mask is given, so that an inactive row's
+ * contents, whatever they are, add nothing to grad_weight), each part
+ * rounded up to 256 bytes.
  */
 size_t rlk_linear_logp_param_grads_workspace_size(int64_t N, int64_t V,
                                                   int64_t H);
@@ -230,11 +240,15 @@ size_t rlk_linear_logp_param_grads_workspace_size(int64_t N, int64_t V,
  * invariance contract; parameter gradients are compared over the same
  * complete sample set).  D is never held whole: the vocabulary is walked in
  * fixed chunks of 16384 entries; per chunk the logits are recomputed with
- * exactly the forward's tiles and K order, D is formed in fp32 as in
- * rlk_logp_backward and rounded once to bf16 -- the MFMA operand type --
- * and both products run on bf16 MFMA with fp32 accumulation; W, hidden and D
- * are contracted over their rows by reading them through transposing LDS
- * loads, so nothing is transposed in memory.
+ * exactly the forward's tiles and K order and D is formed in fp32 as in
+ * rlk_logp_backward.  The products run on bf16 MFMA with fp32 accumulation
+ * (bf16 inputs, fp32 accumulation: page "[WS1 Test] ...", section
+ * "Workstream 1 - #154", scope table), so D enters as two bf16 operands,
+ * D_hi = bf16(D) and D_lo = bf16(D - D_hi), whose sum holds D to a relative
+ * 2^-16; each product is two passes over its K (D_hi, then D_lo) into the
+ * same fp32 accumulators.  W, hidden and D are contracted over their rows by
+ * reading them through transposing LDS loads, so nothing is transposed in
+ * memory.
  *   grad_hidden: chunk partial products are added in ascending chunk order,
  *     so each row depends on its own token only and is bit-identical for any
  *     batch composition.  Inactive rows are +0.0.
@@ -306,14 +320,24 @@ int rlk_token_losses(const float* logp, const float* logp_old,
                      float beta, float* ratio, float* loss, float* kl,
                      float* grad_logp, hipStream_t stream);
 
-/* Static string naming a status code ("RLK_OK", ...); "unknown" otherwise. */
+/*
+ * Static string naming a status code ("RLK_OK", ...); "unknown" otherwise.
+ * A gate report states the reason when the requested backend did not run
+ * (page "[WS1 Test] ...", section "Workstream 4 - #150", gate report
+ * contents: requested / actual backend, fallback reason); this is the name
+ * such a report carries for a failed call.  Never allocates; thread-safe.
+ */
 const char* rlk_status_string(int status);
 
 /*
  * Static string describing this build: library version, target
- * architecture, source revision and a hash of the kernel constants
- * (tile and chunk sizes).  Invariance records carry it, since bits are only
- * promised stable within one build.
+ * architecture, source revision and the schedule constants that fix every
+ * reduction order (row threads and vectors per step, tile shape, K stage,
+ * chunk sizes).  It is the "actual backend" a gate report records beside the
+ * requested one (same page and section as rlk_status_string), and
+ * invariance records carry it, since bits are only promised stable within
+ * one build (the pages' relation I compares a kernel with itself).  Never
+ * allocates; thread-safe; the string lives as long as the library.
  */
 const char* rlk_build_info(void);
 

@@ -15,12 +15,17 @@
 // chunk c, in ascending c on the caller's stream:
 //   1. grad_dl_tiles recomputes the chunk's logits with the forward's tile
 //      main loop (bit-identical z), forms D in fp32 exactly as the logits
-//      backward does, rounds it once to bf16 (the MFMA operand type) and
-//      writes D_c [N, chunk].  Given the fp32 logits the forward kept,
-//      grad_dl_from_logits forms the same D_c from them instead, element by
-//      element with the same arithmetic, so the gradients come out
-//      bit-identical at a fraction of the cost.
-//   2. grad_gemm_tiles runs both products of the chunk in one launch:
+//      backward does and writes it as two bf16 arrays, the MFMA operand type:
+//      D_hi = D rounded to bf16 and D_lo = (D - D_hi) rounded to bf16.  D -
+//      D_hi is exact in fp32, so D_hi + D_lo holds D to a relative 2^-16:
+//      the products see fp32-grade D (bf16 inputs, fp32 accumulation) rather
+//      than D rounded once to 8 significant bits.  Given the fp32 logits the
+//      forward kept, grad_dl_from_logits forms the same pair from them,
+//      element by element with the same arithmetic, so the gradients come
+//      out bit-identical at a fraction of the cost.
+//   2. grad_gemm_tiles runs both products of the chunk in one launch, each
+//      as two passes over its K into the same fp32 accumulators, first with
+//      D_hi, then with D_lo:
 //      grad_hidden (+)= D_c . W_c   (K = the chunk's vocabulary, ascending;
 //                                    chunk 0 writes, later chunks add)
 //      grad_weight[c] = D_c^T . h   (K = tokens, ascending)
@@ -66,6 +71,16 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x)));
 }
 
+// The bf16 word of part `lo` of x: x rounded to bf16 (lo = false), or the
+// rounding's remainder x - bf16(x), itself rounded to bf16 (lo = true).  The
+// remainder is exact in fp32 (x and bf16(x) are within a factor of 2), so the
+// two words sum to x within a relative 2^-16.  NaN gives NaN in both.
+__device__ __forceinline__ uint32_t bf16_part(float x, bool lo) {
+#pragma clang fp contract(off)
+  const uint32_t hi = bf16_bits(x);
+  return lo ? bf16_bits(x - __uint_as_float(hi << 16)) : hi;
+}
+
 struct DlArgs {
   const uint16_t* hidden;
   int64_t ldh;
@@ -81,15 +96,17 @@ struct DlArgs {
   int vt0;        // first vocabulary tile of the chunk
   int n_vt;       // vocabulary tiles in the chunk
   int n_tblocks;  // 256-token blocks
-  uint16_t* d;    // [N][ldd] bf16, chunk-local columns
+  uint16_t* d;    // [N][ldd] bf16 D_hi, chunk-local columns
+  uint16_t* d_lo; // [N][ldd] bf16 D_lo
   int64_t ldd;
 };
 
-// D for one 256-vocabulary x 256-token tile of the chunk.  The main loop is
-// the forward's (same operands, same K order), so z is bit-identical to the
-// logits the forward reduced; the fp32 D formula is the logits backward's.
-// Entries past V, rows past N and inactive rows are written as zero; an
-// active row with an invalid target gets NaN.
+// D (as D_hi and D_lo) for one 256-vocabulary x 256-token tile of the chunk.
+// The main loop is the forward's (same operands, same K order), so z is
+// bit-identical to the logits the forward reduced; the fp32 D formula is the
+// logits backward's.  Entries past V, rows past N and inactive rows are
+// written as zero; an active row with an invalid target, or with non-finite
+// logits, gets NaN.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grad_dl_tiles(DlArgs a) {
   __shared__ uint4 smem[kDlSmemVec];
@@ -117,6 +134,7 @@ void grad_dl_tiles(DlArgs a) {
   // rel[j]: the target's offset from this lane's first vocabulary row
   // (128 wv + 4 (lane >> 5) of the tile), or -1 when outside this wave's rows
   int rel[kJ];
+  bool act[kJ];
   float ng[kJ], gg[kJ], off[kJ], pz[kJ];
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
@@ -127,32 +145,32 @@ void grad_dl_tiles(DlArgs a) {
     const bool tvalid = (t >= 0 && t < a.V);
     const int64_t r = t - (vocab0 + wv * 128 + 4 * half);
     rel[j] = (r >= 0 && r < 128) ? static_cast<int>(r) : -1;
+    act[j] = active;
     gg[j] = active ? a.grad[tok] : 0.0f;
     ng[j] = -gg[j];
     off[j] = active ? a.lse[tok] * kLog2e : 0.0f;
     pz[j] = (active && !tvalid) ? __builtin_nanf("") : 0.0f;
   }
-  // bf16 D of vocabulary rows m0 .. m0 + 3 (m0 = 128 wv + 32 i + 8 q +
-  // 4 (lane >> 5)) of token column j, two entries per word.  Evaluated once
-  // per staging layout rather than held: the accumulators stay the only
-  // large live state.  No branches: p is always evaluated and clamped to be
-  // finite, so a masked row (g = 0) or a column past V (multiplier 0) gives
-  // +0, and an active row with an invalid target carries NaN in the
-  // additive term.
+  // bf16 part `lo` of D for vocabulary rows m0 .. m0 + 3 (m0 = 128 wv +
+  // 32 i + 8 q + 4 (lane >> 5)) of token column j, two entries per word.
+  // Evaluated once per staging pass rather than held: the accumulators stay
+  // the only large live state.  No branches: p is always evaluated; a masked
+  // row or a column past V selects +0 whatever its logits hold, an active row
+  // with an invalid target carries NaN in the additive term, and NaN or
+  // infinite logits of an active row reach D unclamped.
   // kFull: the tile's 256 vocabulary rows are all < V (every tile but a
   // ragged last one), so no row test is needed -- a uniform branch picks it.
   auto epilogue = [&](auto full) {
   constexpr bool kFull = decltype(full)::value;
-  auto dpair = [&](int j, int i, int q) {
+  auto dpair = [&](int j, int i, int q, bool lo) {
     const int m0 = wv * 128 + i * 32 + 8 * q + 4 * half;
     uint32_t b[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float p =
-          fminf(fast_exp2(__builtin_fmaf(acc[i][j][4 * q + e], kLog2e, -off[j])), __FLT_MAX__);
+      const float p = fast_exp2(__builtin_fmaf(acc[i][j][4 * q + e], kLog2e, -off[j]));
       const float add = (i * 32 + 8 * q + e == rel[j]) ? gg[j] : 0.0f;
-      const bool col = kFull || m0 + e < V_tail;
-      b[e] = bf16_bits(__builtin_fmaf(col ? ng[j] : 0.0f, p, col ? add + pz[j] : 0.0f));
+      const bool keep = act[j] && (kFull || m0 + e < V_tail);
+      b[e] = bf16_part(keep ? __builtin_fmaf(ng[j], p, add + pz[j]) : 0.0f, lo);
     }
     return make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
   };
@@ -161,8 +179,11 @@ void grad_dl_tiles(DlArgs a) {
   // 16-byte pieces of a staged 256 x 256 tile: 32 per row, 16 per thread
   constexpr int kPieces = kBQ * (kBP / 8) / kThreads;
 
-  {
-    // S[token][vocab], then whole 512-byte token rows of D_c
+  // S[token][vocab], then whole 512-byte token rows of D_c: D_hi, then D_lo
+#pragma nounroll
+  for (int part = 0; part < 2; ++part) {
+    const bool lo = part != 0;
+    uint16_t* dst = lo ? a.d_lo : a.d;
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
       const int tl = wt * kQW + j * 32 + (lane & 31);
@@ -171,7 +192,7 @@ void grad_dl_tiles(DlArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int m0 = wv * 128 + i * 32 + 8 * q + 4 * half;
-          *reinterpret_cast<uint2*>(S + tl * kDlStride + m0) = dpair(j, i, q);
+          *reinterpret_cast<uint2*>(S + tl * kDlStride + m0) = dpair(j, i, q, lo);
         }
     }
     __syncthreads();
@@ -182,21 +203,23 @@ void grad_dl_tiles(DlArgs a) {
       const int c = idx & 31;
       if (r < N_tail) {
         const uint4 v = *reinterpret_cast<const uint4*>(S + r * kDlStride + 8 * c);
-        *reinterpret_cast<uint4*>(a.d + (tok0 + r) * a.ldd + vtl * kBP + 8 * c) = v;
+        *reinterpret_cast<uint4*>(dst + (tok0 + r) * a.ldd + vtl * kBP + 8 * c) = v;
       }
     }
+    __syncthreads();
   }
   };
   if (V_tail >= kBP) epilogue(std::true_type{});
   else epilogue(std::false_type{});
 }
 
-// D_c from kept fp32 logits [N, ldz]: entry (row, k) of the chunk is vocabulary
-// column vocab0 + k.  The per-element arithmetic is grad_dl_tiles' (so is
-// the bf16 rounding); columns at or past V within the padded chunk width
-// and inactive rows get +0, and an active row with an invalid target NaN.
-// Blocks of 2048 columns of one row: 128 threads x 4 groups of 4 columns,
-// 16-byte loads, 8-byte stores (512 contiguous bytes per wave instruction).
+// D_c (D_hi and D_lo) from kept fp32 logits [N, ldz]: entry (row, k) of the
+// chunk is vocabulary column vocab0 + k.  The per-element arithmetic is
+// grad_dl_tiles' (so is the split into two bf16 parts); columns at or past V
+// within the padded chunk width and inactive rows get +0, and an active row
+// with an invalid target NaN.  Blocks of 2048 columns of one row: 128 threads
+// x 4 groups of 4 columns, 16-byte loads, 8-byte stores (512 contiguous bytes
+// per wave instruction).
 constexpr int kDlzThreads = 128;
 constexpr int kDlzUnroll = 4;
 constexpr int kDlzBlockCols = kDlzThreads * kDlzUnroll * 4;
@@ -205,7 +228,7 @@ __global__ __launch_bounds__(kDlzThreads) void grad_dl_from_logits(
     const float* __restrict__ logits, int64_t ldz, const int64_t* __restrict__ targets,
     const uint8_t* __restrict__ mask, const float* __restrict__ lse,
     const float* __restrict__ grad, int64_t N, int V, int vocab0, int width, int nb,
-    uint16_t* __restrict__ d, int64_t ldd) {
+    uint16_t* __restrict__ d, uint16_t* __restrict__ d_lo, int64_t ldd) {
   const int tid = threadIdx.x;
   const int64_t total = N * nb;
   for (int64_t wid = blockIdx.x; wid < total; wid += gridDim.x) {
@@ -219,6 +242,7 @@ __global__ __launch_bounds__(kDlzThreads) void grad_dl_from_logits(
     const float pz = (active && !(t >= 0 && t < V)) ? __builtin_nanf("") : 0.0f;
     const float* zr = logits + row * ldz + vocab0;
     uint16_t* dr = d + row * ldd;
+    uint16_t* dlr = d_lo + row * ldd;
     float4 w[kDlzUnroll];
 #pragma unroll
     for (int u = 0; u < kDlzUnroll; ++u) {
@@ -239,15 +263,18 @@ __global__ __launch_bounds__(kDlzThreads) void grad_dl_from_logits(
       const int k = k0 + 4 * (u * kDlzThreads + tid);
       if (k >= width) break;
       const float x[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
-      uint32_t b[4];
+      uint32_t b[4], c[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = fminf(fast_exp2(__builtin_fmaf(x[e], kLog2e, -off)), __FLT_MAX__);
-        const bool col = vocab0 + k + e < V;
+        const float p = fast_exp2(__builtin_fmaf(x[e], kLog2e, -off));
+        const bool keep = active && vocab0 + k + e < V;
         const float add = (vocab0 + k + e == t) ? g : 0.0f;
-        b[e] = bf16_bits(__builtin_fmaf(col ? ng : 0.0f, p, col ? add + pz : 0.0f));
+        const float dv = keep ? __builtin_fmaf(ng, p, add + pz) : 0.0f;
+        b[e] = bf16_part(dv, false);
+        c[e] = bf16_part(dv, true);
       }
       *reinterpret_cast<uint2*>(dr + k) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+      *reinterpret_cast<uint2*>(dlr + k) = make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16));
     }
   }
 }
@@ -260,7 +287,8 @@ struct GemmOp {
   int64_t ldp;
   int P;              // tile rows of the P side present
   int kext_p;         // K-major P: K rows present
-  const uint16_t* q;  // Q side (output rows)
+  const uint16_t* q;  // Q side (output rows): D_hi
+  const uint16_t* q_lo;  // D_lo, the same layout: a second pass over K
   int64_t ldq;
   int Q;
   int kext_q;
@@ -305,16 +333,23 @@ void grad_gemm_tiles(GemmArgs args) {
   const int Q_tail = min(g.Q - q0, kBQ);
 
   f32x16_t acc[kI][kJ];
-  // P is K-major in both products (W_c over the vocabulary, h over tokens)
+  // P is K-major in both products (W_c over the vocabulary, h over tokens).
+  // Two passes over K into the same accumulators: D_hi, then D_lo.
   const Side Ps{g.p + p0, g.ldp, g.kext_p, p0};
   if (g.q_kmajor) {
-    const Side Qs{g.q + q0, g.ldq, g.kext_q, q0};
     const LoaderG<Lay::kCols, Lay::kCols> ld = make_loader_g<Lay::kCols, Lay::kCols>(wave, lane, g.ldp, g.ldq);
-    mainloop_g(smem, ld, wave, lane, wp, wq, Ps, Qs, g.K, acc);
+#pragma nounroll
+    for (int part = 0; part < 2; ++part) {
+      const Side Qs{(part ? g.q_lo : g.q) + q0, g.ldq, g.kext_q, q0};
+      mainloop_g(smem, ld, wave, lane, wp, wq, Ps, Qs, g.K, acc, part == 0);
+    }
   } else {
-    const Side Qs{g.q + static_cast<int64_t>(q0) * g.ldq, g.ldq, Q_tail, 0};
     const LoaderG<Lay::kCols, Lay::kRows> ld = make_loader_g<Lay::kCols, Lay::kRows>(wave, lane, g.ldp, g.ldq);
-    mainloop_g(smem, ld, wave, lane, wp, wq, Ps, Qs, g.K, acc);
+#pragma nounroll
+    for (int part = 0; part < 2; ++part) {
+      const Side Qs{(part ? g.q_lo : g.q) + static_cast<int64_t>(q0) * g.ldq, g.ldq, Q_tail, 0};
+      mainloop_g(smem, ld, wave, lane, wp, wq, Ps, Qs, g.K, acc, part == 0);
+    }
   }
 
   // Staged through LDS one 32-row slice at a time so that each store
@@ -398,15 +433,16 @@ __global__ __launch_bounds__(256) void active_rows_bf16(const uint16_t* __restri
   }
 }
 
-// Workspace: one chunk of D in bf16, [N, chunk], then (used when a mask is
-// given) a copy of hidden, [N, H] bf16, with inactive rows zeroed.
+// Workspace: one chunk of D as two bf16 arrays, D_hi [N, chunk] and D_lo
+// [N, chunk], then (used when a mask is given) a copy of hidden, [N, H] bf16,
+// with inactive rows zeroed.
 int64_t grad_d_bytes(int64_t N, int64_t V) {
   const int64_t chunk = min64(kGradChunk, round_up(V, kBP));
   return round_up(N * chunk * 2, 256);
 }
 
 size_t grad_workspace(int64_t N, int64_t V, int64_t H) {
-  return static_cast<size_t>(grad_d_bytes(N, V) + round_up(N * H * 2, 256));
+  return static_cast<size_t>(2 * grad_d_bytes(N, V) + round_up(N * H * 2, 256));
 }
 
 }  // namespace
@@ -433,6 +469,7 @@ hipError_t launch_linear_param_grads(const uint16_t* hidden, int64_t ldh, const 
     return hipSuccess;
   }
   uint16_t* d = static_cast<uint16_t*>(workspace);
+  uint16_t* d_lo = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + grad_d_bytes(N, V));
   const int64_t chunk = min64(kGradChunk, round_up(V, kBP));
   const bool want_h = grad_hidden != nullptr;
   const bool want_w = grad_weight != nullptr;
@@ -442,7 +479,7 @@ hipError_t launch_linear_param_grads(const uint16_t* hidden, int64_t ldh, const 
   int64_t ldhw = ldh;
   if (want_w && mask != nullptr) {
     uint16_t* hcopy = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) +
-                                                  grad_d_bytes(N, V));
+                                                  2 * grad_d_bytes(N, V));
     const int64_t vecs = N * (H / 8);
     const int64_t blocks = min64((vecs + 255) / 256, 65536);
     hipLaunchKernelGGL(active_rows_bf16, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
@@ -470,7 +507,7 @@ hipError_t launch_linear_param_grads(const uint16_t* hidden, int64_t ldh, const 
       const int64_t blocks = min64(N * nb, int64_t(1) << 22);
       hipLaunchKernelGGL(grad_dl_from_logits, dim3(static_cast<uint32_t>(blocks)),
                          dim3(kDlzThreads), 0, stream, logits, ldz, targets, mask, lse, grad, N, V,
-                         vocab0, width, nb, d, static_cast<int64_t>(chunk));
+                         vocab0, width, nb, d, d_lo, static_cast<int64_t>(chunk));
     } else {
       DlArgs da{};
       da.hidden = hidden;
@@ -488,6 +525,7 @@ hipError_t launch_linear_param_grads(const uint16_t* hidden, int64_t ldh, const 
       da.n_vt = n_vt;
       da.n_tblocks = n_tblocks;
       da.d = d;
+      da.d_lo = d_lo;
       da.ldd = chunk;
       hipLaunchKernelGGL(grad_dl_tiles, dim3(static_cast<uint32_t>(n_vt * n_tblocks)),
                          dim3(kThreads), 0, stream, da);
@@ -506,6 +544,7 @@ hipError_t launch_linear_param_grads(const uint16_t* hidden, int64_t ldh, const 
       o.P = H;
       o.kext_p = v_rows;
       o.q = d;
+      o.q_lo = d_lo;
       o.ldq = chunk;
       o.Q = static_cast<int>(N);
       o.kext_q = 0;
@@ -528,6 +567,7 @@ hipError_t launch_linear_param_grads(const uint16_t* hidden, int64_t ldh, const 
       o.P = H;
       o.kext_p = static_cast<int>(N);
       o.q = d;
+      o.q_lo = d_lo;
       o.ldq = chunk;
       o.Q = v_rows;
       o.kext_q = static_cast<int>(N);

@@ -135,10 +135,11 @@ void linear_tiles_bwd(TileArgs args) {
       // The target's offset from this lane's first vocabulary row, or -1.
       const int64_t rt = t - (vwave + 4 * half);
       const int rel = (rt >= 0 && rt < 128) ? static_cast<int>(rt) : -1;
-      // d = g ([j == t] - p) without branches: p is always evaluated and
-      // clamped to be finite, so a masked row (g = 0, whatever its logits)
-      // gives -0 p + 0 = +0, and an active row with an invalid target
-      // carries NaN in the additive term.
+      // d = g ([j == t] - p) without branches: p is always evaluated, a
+      // masked row (or a token column past N) selects +0 whatever its logits
+      // hold, an active row with an invalid target carries NaN in the
+      // additive term, and NaN or infinite logits of an active row reach its
+      // gradient unclamped.
       const float poison = (active && !tvalid) ? nan : 0.0f;
       float* srow = stage + (lane & 31) * kStageStride;
 #pragma unroll
@@ -149,10 +150,9 @@ void linear_tiles_bwd(TileArgs args) {
           float d[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float p =
-                fminf(fast_exp2(__builtin_fmaf(acc[i][j][4 * q + e], kLog2e, -off)), __FLT_MAX__);
+            const float p = fast_exp2(__builtin_fmaf(acc[i][j][4 * q + e], kLog2e, -off));
             const float add = (i * 32 + 8 * q + e == rel) ? g : 0.0f;
-            d[e] = __builtin_fmaf(ng, p, add + poison);
+            d[e] = active ? __builtin_fmaf(ng, p, add + poison) : 0.0f;
           }
           *reinterpret_cast<float4*>(srow + m0) = make_float4(d[0], d[1], d[2], d[3]);
         }
@@ -343,21 +343,23 @@ void linear_tiles_fwd(TileArgs args) {
 // l + 128, ... in ascending order, then the 64 lane states merge in the fixed
 // butterfly; the schedule depends on the number of chunks (that is, on V)
 // only.  Partials are row-major, so each step is one coalesced 512-byte load.
+// A launch of more rows than the grid holds loops (rows + gridDim.x * 4).
 constexpr int kCombineRows = 4;  // rows (waves) per workgroup
+constexpr int64_t kCombineMaxGrid = int64_t(1) << 22;
 
 __global__ __launch_bounds__(64 * kCombineRows) void lse_chunk_combine(
     const float2* __restrict__ part, int n_vtiles, const float* __restrict__ zt,
     const int64_t* __restrict__ targets, const uint8_t* __restrict__ mask, int64_t N, int V,
     float* __restrict__ logp, float* __restrict__ lse) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kCombineRows + (threadIdx.x >> 6);
-  if (row >= N) return;
+  for (int64_t row = static_cast<int64_t>(blockIdx.x) * kCombineRows + (threadIdx.x >> 6);
+       row < N; row += static_cast<int64_t>(gridDim.x) * kCombineRows) {
   if (mask != nullptr && mask[row] == 0) {
     if (lane == 0) {
       logp[row] = 0.0f;
       if (lse != nullptr) lse[row] = 0.0f;
     }
-    return;
+    continue;
   }
   const float2* rp = part + row * n_vtiles;
   float M = neg_inf();
@@ -384,6 +386,7 @@ __global__ __launch_bounds__(64 * kCombineRows) void lse_chunk_combine(
     const int64_t t = targets[row];
     logp[row] = (t >= 0 && t < V) ? zt[row] - l : __builtin_nanf("");
     if (lse != nullptr) lse[row] = l;
+  }
   }
 }
 
@@ -432,8 +435,9 @@ hipError_t launch_linear_logp(const uint16_t* hidden, int64_t ldh, const uint16_
     hipLaunchKernelGGL(linear_tiles_fwd<false>, dim3(tiles), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const int64_t cgrid = (N + kCombineRows - 1) / kCombineRows;
   hipLaunchKernelGGL(lse_chunk_combine,
-                     dim3(static_cast<uint32_t>((N + kCombineRows - 1) / kCombineRows)),
+                     dim3(static_cast<uint32_t>(cgrid < kCombineMaxGrid ? cgrid : kCombineMaxGrid)),
                      dim3(64 * kCombineRows), 0,
                      stream, a.part, a.n_vtiles, a.zt, targets, mask, N, V, logp, lse);
   return hipGetLastError();

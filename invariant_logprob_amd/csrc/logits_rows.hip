@@ -1,6 +1,8 @@
 // Selected-token logprob from materialised bf16 logits, and its backward.
 //
-// Forward (one workgroup per row).  The row is streamed once from HBM in
+// Forward (one workgroup per row; a launch of more rows than the grid limit
+// loops, each workgroup taking rows blockIdx.x, + gridDim.x, ... with the
+// same per-row schedule).  The row is streamed once from HBM in
 // 16-byte vectors of 8 bf16.  Vector k of a row always goes to thread
 // k % kRowThreads and is visited in ascending k, so every lane's partial
 // (M, s) is a function of the row's values and of V alone.  Lanes merge in a
@@ -106,18 +108,24 @@ __device__ __forceinline__ void consume3(float& M, float& s, float& t, const Vec
 template <int THREADS, int UNROLL, bool kEntropy>
 __global__ __launch_bounds__(THREADS) void logp_fwd_rows(
     const uint16_t* __restrict__ logits, int64_t ld, const int64_t* __restrict__ targets,
-    const uint8_t* __restrict__ mask, int V, float* __restrict__ logp, float* __restrict__ lse,
-    float* __restrict__ ent) {
+    const uint8_t* __restrict__ mask, int64_t N, int V, float* __restrict__ logp,
+    float* __restrict__ lse, float* __restrict__ ent) {
   constexpr int kWaves = THREADS / 64;
-  const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
+  // wave partials of a row, double-buffered by iteration parity so that the
+  // next row's writes never race the final merge of this one
+  __shared__ float sM[2][kWaves];
+  __shared__ float sS[2][kWaves];
+  __shared__ float sT[2][kWaves];
+  int par = 0;
+  for (int64_t row = blockIdx.x; row < N; row += gridDim.x, par ^= 1) {
   if (mask != nullptr && mask[row] == 0) {
     if (tid == 0) {
       logp[row] = 0.0f;
       if (lse != nullptr) lse[row] = 0.0f;
       if constexpr (kEntropy) ent[row] = 0.0f;
     }
-    return;
+    continue;
   }
   const uint16_t* rowp = logits + row * ld;
   const uint4* vp = reinterpret_cast<const uint4*>(rowp);
@@ -160,24 +168,21 @@ __global__ __launch_bounds__(THREADS) void logp_fwd_rows(
 
   if constexpr (kEntropy) wave_lse3_allreduce(M, s, tw);
   else wave_lse_allreduce(M, s);
-  __shared__ float sM[kWaves];
-  __shared__ float sS[kWaves];
-  __shared__ float sT[kWaves];
   const int wave = tid >> 6;
   if ((tid & 63) == 0) {
-    sM[wave] = M;
-    sS[wave] = s;
-    if constexpr (kEntropy) sT[wave] = tw;
+    sM[par][wave] = M;
+    sS[par][wave] = s;
+    if constexpr (kEntropy) sT[par][wave] = tw;
   }
   __syncthreads();
   if (tid == 0) {
-    float Mt = sM[0];
-    float st = sS[0];
-    float tt = kEntropy ? sT[0] : 0.0f;
+    float Mt = sM[par][0];
+    float st = sS[par][0];
+    float tt = kEntropy ? sT[par][0] : 0.0f;
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) {
-      if constexpr (kEntropy) lse3_merge(Mt, st, tt, sM[w], sS[w], sT[w]);
-      else lse_merge(Mt, st, sM[w], sS[w]);
+      if constexpr (kEntropy) lse3_merge(Mt, st, tt, sM[par][w], sS[par][w], sT[par][w]);
+      else lse_merge(Mt, st, sM[par][w], sS[par][w]);
     }
     const float l = lse_finish(Mt, st);
     if constexpr (kEntropy) {
@@ -193,6 +198,7 @@ __global__ __launch_bounds__(THREADS) void logp_fwd_rows(
     }
     logp[row] = lp;
     if (lse != nullptr) lse[row] = l;
+  }
   }
 }
 
@@ -287,7 +293,7 @@ __global__ __launch_bounds__(THREADS) void logp_bwd_rows(
 // The backward from fp32 logits (the storing fused forward's output), with
 // the access pattern and block order of logp_bwd_rows and the per-element
 // arithmetic of the fused backward's epilogue:
-//   d = fma(-g, min(2^(fma(x, log2 e, -lse log2 e)), FLT_MAX), [j == t] g + poison)
+//   d = fma(-g, 2^(fma(x, log2 e, -lse log2 e)), [j == t] g + poison)
 // so that for the same logits and lse its output is bit-identical to the
 // fused backward's.  A lane reads all of its elements before it writes any,
 // and lanes own disjoint elements, so logits and dl may be one buffer.
@@ -341,7 +347,7 @@ __global__ __launch_bounds__(THREADS) void logp_bwd_rows_f32(
       float d[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = fminf(fast_exp2(__builtin_fmaf(x[e], kLog2e, -off)), __FLT_MAX__);
+        const float p = fast_exp2(__builtin_fmaf(x[e], kLog2e, -off));
         const float add = (j + e == t) ? g : 0.0f;
         d[e] = __builtin_fmaf(-g, p, add + poison);
       }
@@ -407,6 +413,8 @@ constexpr int kBwdUnroll = 4;
 // Upper bound on the elementwise kernels' grid (a multiple of 8); larger
 // problems loop.
 constexpr int64_t kBwdMaxGrid = int64_t(1) << 22;
+// Upper bound on the forward's grid (rows per launch round); more rows loop.
+constexpr int64_t kRowMaxGrid = int64_t(1) << 22;
 
 int logits_schedule_threads() { return kRowThreads; }
 int logits_schedule_unroll() { return kRowUnroll; }
@@ -414,14 +422,15 @@ int logits_schedule_unroll() { return kRowUnroll; }
 hipError_t launch_logp_fwd_rows(const uint16_t* logits, int64_t ld, const int64_t* targets,
                                 const uint8_t* mask, int64_t N, int V, float* logp, float* lse,
                                 float* entropy, hipStream_t stream) {
+  const uint32_t grid = static_cast<uint32_t>(N < kRowMaxGrid ? N : kRowMaxGrid);
   if (entropy == nullptr) {
-    hipLaunchKernelGGL((logp_fwd_rows<kRowThreads, kRowUnroll, false>),
-                       dim3(static_cast<uint32_t>(N)), dim3(kRowThreads), 0, stream, logits, ld,
-                       targets, mask, V, logp, lse, nullptr);
+    hipLaunchKernelGGL((logp_fwd_rows<kRowThreads, kRowUnroll, false>), dim3(grid),
+                       dim3(kRowThreads), 0, stream, logits, ld, targets, mask, N, V, logp, lse,
+                       nullptr);
   } else {
-    hipLaunchKernelGGL((logp_fwd_rows<kRowThreads, kRowUnroll, true>),
-                       dim3(static_cast<uint32_t>(N)), dim3(kRowThreads), 0, stream, logits, ld,
-                       targets, mask, V, logp, lse, entropy);
+    hipLaunchKernelGGL((logp_fwd_rows<kRowThreads, kRowUnroll, true>), dim3(grid),
+                       dim3(kRowThreads), 0, stream, logits, ld, targets, mask, N, V, logp, lse,
+                       entropy);
   }
   return hipGetLastError();
 }

@@ -24,6 +24,13 @@ constexpr int64_t kMaxN = (int64_t(1) << 31) - 1;
 // The fused tiles address a 256-row slab of W or hidden with 32-bit byte
 // offsets, which bounds the leading dimensions.
 constexpr int64_t kMaxLinearLd = int64_t(1) << 22;
+// A launch covers fewer than 2^32 work-items: one tile kernel launch (one
+// workgroup of 512 threads per tile) holds fewer than 2^23 tiles.  The row
+// kernels loop over rows beyond their grid and have no such bound.
+constexpr int64_t kMaxTileGrid = int64_t(1) << 23;
+constexpr int64_t kTile = rlk::kLinearVocabTile;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -45,9 +52,8 @@ int check_linear(const void* hidden, int64_t ld_h, const void* weight, int64_t l
   if (H > kMaxH || ld_h >= kMaxLinearLd || ld_w >= kMaxLinearLd) return RLK_ERR_UNSUPPORTED;
   if ((H % 8) != 0 || (ld_h % 8) != 0 || (ld_w % 8) != 0) return RLK_ERR_UNSUPPORTED;
   if (!aligned16(hidden) || !aligned16(weight)) return RLK_ERR_UNSUPPORTED;
-  const int64_t tiles = ((V + rlk::kLinearVocabTile - 1) / rlk::kLinearVocabTile) *
-                        ((N + rlk::kLinearTokenTile - 1) / rlk::kLinearTokenTile);
-  if (tiles > kMaxN) return RLK_ERR_UNSUPPORTED;
+  const int64_t tiles = ceil_div(V, rlk::kLinearVocabTile) * ceil_div(N, rlk::kLinearTokenTile);
+  if (tiles >= kMaxTileGrid) return RLK_ERR_UNSUPPORTED;
   if (N > 0 && ld_h > (int64_t(1) << 62) / N) return RLK_ERR_UNSUPPORTED;
   if (ld_w > (int64_t(1) << 62) / V) return RLK_ERR_UNSUPPORTED;
   return RLK_OK;
@@ -109,6 +115,14 @@ int param_grads(const float* logits, int64_t ld_z, const void* hidden, int64_t l
   // the transposed hidden's rows (N rounded up to 8) are addressed like a
   // fused-tile operand
   if (N > kMaxLinearLd - 16) return RLK_ERR_UNSUPPORTED;
+  {
+    // the largest launch of the path: one chunk's two products, grad_hidden
+    // tiles (rounded up to 8) then grad_weight tiles
+    const int64_t htiles = ceil_div(H, kTile);
+    const int64_t chunk_tiles = ceil_div(V < rlk::kGradChunk ? V : rlk::kGradChunk, kTile);
+    const int64_t grid = ceil_div(htiles * ceil_div(N, kTile), 8) * 8 + htiles * chunk_tiles;
+    if (grid >= kMaxTileGrid) return RLK_ERR_UNSUPPORTED;
+  }
   if (grad_hidden != nullptr) {
     if (ld_gh < H) return RLK_ERR_INVALID_ARG;
     if ((ld_gh % 4) != 0 || !aligned16(grad_hidden)) return RLK_ERR_UNSUPPORTED;
@@ -313,6 +327,10 @@ int rlk_token_losses(const float* logp, const float* logp_old, const float* logp
   return status_of(rlk::launch_token_losses(a, stream));
 }
 
+// The gate report names its backend and any failure reason (page "[WS1
+// Test] #154 dtype pin + #152 KV path + #153 bwd invariance + #150 chain
+// gate", section "Workstream 4 - #150", gate report contents): a status code
+// is turned into the name a report can carry.
 const char* rlk_status_string(int status) {
   switch (status) {
     case RLK_OK: return "RLK_OK";
@@ -326,10 +344,13 @@ const char* rlk_status_string(int status) {
 #define RLK_STR2(x) #x
 #define RLK_STR(x) RLK_STR2(x)
 
+// The actual backend a gate report records beside the requested one (same
+// page and section as above).
+
 const char* rlk_build_info(void) {
   return "rlk 0.1.0; arch=gfx950; rev=" RLK_GIT_REV
          "; schedule=rows:256thr,8x16B/lane-step; bwd:128thr,4x8B,xcd-ordered; tile:" RLK_STR(256) "x" RLK_STR(
-             256) "x" RLK_STR(64) ",8waves,mfma32x32x16bf16,2stage,group8,wg-per-tile; combine:wave-per-row; grads:chunk" RLK_STR(16384) ",dl-bf16,kmajor-tr16";
+             256) "x" RLK_STR(64) ",8waves,mfma32x32x16bf16,2stage,group8,wg-per-tile; combine:wave-per-row; grads:chunk" RLK_STR(16384) ",dl-bf16x2,kmajor-tr16";
 }
 
 }  // extern "C"

@@ -382,13 +382,15 @@ __device__ __forceinline__ void frag_g(const uint4* a, int kk, int wp, int wq, i
 }
 
 // The main loop of `mainloop` for operands in any layout: same stage order,
-// same double buffering, same MFMA sequence.
+// same double buffering, same MFMA sequence.  With zero_acc false the
+// products are added to the accumulators' current values (a second pass over
+// the same K, continuing the same fixed order).
 template <Lay LP, Lay LQ>
 __device__ __forceinline__ void mainloop_g(uint4* smem, const LoaderG<LP, LQ>& L, int wave,
                                            int lane, int wp, int wq, const Side& P, const Side& Q,
-                                           int K, f32x16_t (&acc)[kI][kJ]) {
+                                           int K, f32x16_t (&acc)[kI][kJ], bool zero_acc = true) {
   const int n_kt = (K + kBK - 1) / kBK;
-  zero(acc);
+  if (zero_acc) zero(acc);
   if (n_kt <= 0) return;
   issue_g<0, kBlkPerWave>(smem, L, wave, P, Q, 0, 0, K);
   for (int kt = 0; kt < n_kt; ++kt) {

@@ -167,7 +167,23 @@ int main() {
          RLK_OK, true, "fused: largest H");
   expect(rlk_linear_logp(x, 64, x, 64, t, nullptr, kMaxN, int64_t(1) << 28, 64, f, nullptr, g,
                          SIZE_MAX, nullptr),
-         RLK_ERR_UNSUPPORTED, false, "fused: tile count beyond 2^31");
+         RLK_ERR_UNSUPPORTED, false, "fused: tile count beyond 2^23");
+  // a launch holds fewer than 2^32 work-items: fewer than 2^23 tiles of 512
+  expect(rlk_linear_logp(x, 64, x, 64, t, nullptr, 14122 * 256, 151936, 64, f, nullptr, g,
+                         SIZE_MAX, nullptr),
+         RLK_OK, true, "fused: 8388468 tiles (V = 151936)");
+  expect(rlk_linear_logp(x, 64, x, 64, t, nullptr, 14122 * 256 + 1, 151936, 64, f, nullptr, g,
+                         SIZE_MAX, nullptr),
+         RLK_ERR_UNSUPPORTED, false, "fused: 8389062 tiles (V = 151936)");
+  expect(rlk_linear_logp(x, 64, x, 64, t, nullptr, (int64_t(1) << 24) - 256, 32768, 64, f, nullptr,
+                         g, SIZE_MAX, nullptr),
+         RLK_OK, true, "fused: 2^23 - 128 tiles");
+  expect(rlk_linear_logp(x, 64, x, 64, t, nullptr, int64_t(1) << 24, 32768, 64, f, nullptr, g,
+                         SIZE_MAX, nullptr),
+         RLK_ERR_UNSUPPORTED, false, "fused: 2^23 tiles");
+  expect(rlk_logp_backward(nullptr, 0, x, 64, x, 64, 64, t, nullptr, f, f, int64_t(1) << 24, 32768,
+                           g, 32768, nullptr),
+         RLK_ERR_UNSUPPORTED, false, "fused bwd: 2^23 tiles");
   expect(rlk_linear_logp_with_logits(x, 64, x, 64, t, nullptr, 300, 1000, 64, f, nullptr, g, 1000,
                                      at(A + 0x30000000), ws, nullptr),
          RLK_OK, true, "kept logits: valid");
@@ -184,6 +200,19 @@ int main() {
   expect(rlk_linear_logp_param_grads(x, 64, x, 64, t, nullptr, f, f, 0, 1000, 64, nullptr, 0, g,
                                      64, nullptr, 0, nullptr),
          RLK_OK, true, "param grads: N = 0 clears grad_weight");
+  // the largest gradient launch: ceil(H/256) * ceil(N/256) (rounded up to 8)
+  // + ceil(H/256) * (chunk tiles) workgroups, fewer than 2^23
+  expect(rlk_linear_logp_param_grads(x, int64_t(1) << 19, x, int64_t(1) << 19, t, nullptr, f, f,
+                                     (int64_t(1) << 20) - 1280, 1000, int64_t(1) << 19, g,
+                                     int64_t(1) << 19, g, int64_t(1) << 19, g, SIZE_MAX, nullptr),
+         RLK_OK, true, "param grads: 8386560 workgroups");
+  expect(rlk_linear_logp_param_grads(x, int64_t(1) << 19, x, int64_t(1) << 19, t, nullptr, f, f,
+                                     (int64_t(1) << 20) - 1024, 1000, int64_t(1) << 19, g,
+                                     int64_t(1) << 19, g, int64_t(1) << 19, g, SIZE_MAX, nullptr),
+         RLK_ERR_UNSUPPORTED, false, "param grads: 2^23 workgroups");
+  // the row kernels loop over rows past their grid: any N < 2^31 launches
+  expect(rlk_logp_selected(x, 1024, t, nullptr, kMaxN, 1024, f, nullptr, nullptr), RLK_OK, true,
+         "logits: N = 2^31 - 1");
   expect(rlk_linear_logp_param_grads_from_logits(f, 1000, x, 64, x, 64, t, nullptr, f, f, 300,
                                                  1000, 64, g, 64, g, 64, g, wsg, nullptr),
          RLK_OK, true, "param grads from logits: valid");

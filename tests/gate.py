@@ -40,8 +40,8 @@ THRESHOLDS = {
     "forward_accuracy": {"logp": "2e-5 + 1e-5|r|", "linear_logp": "2e-3",
                          "linear_logp_kept": "2e-3"},
     "gradient_accuracy": {"logp": "1e-3", "linear_logp": "1e-3", "linear_logp_kept": "1e-3",
-                          "linear_logp_params": "2^-8 sum|D||W| + 1e-6 (grad_hidden), "
-                                                "2^-8 sum|D||h| + 1e-6 (grad_weight)"},
+                          "linear_logp_params": "min(1e-3, 1e-4 sum|D||W| + 1e-5) (grad_hidden), "
+                                                "min(1e-3, 1e-4 sum|D||h| + 1e-5) (grad_weight)"},
     "forward_invariance": {"atol": 0.0, "rtol": 0.0},
     "gradient_invariance": {"atol": 0.0, "rtol": 0.0},
 }
@@ -146,11 +146,13 @@ class Runner:
             base = {"x": b.logits, "targets": b.targets, "mask": b.mask, "grad": b.grad}
             shared = {}
         elif man["workload"] == "logits_varlen":
+            import invariance as inv
             b = wl.logits_varlen(man["seed"], self.dev)
             n = min(b.logits.shape[0], 160)
             base = {"x": b.logits[:n], "targets": b.targets[:n], "mask": b.mask[:n],
                     "grad": b.grad[:n]}
-            shared = {}
+            # drift records name (sequence, token position) of the packing
+            shared = {"positions": inv.canonical_positions(n, b.seq_lens)}
         elif man["workload"] == "logits_large_rows":
             b = wl.logits_batch(a["n"], 151936, 4.0, man["seed"], self.dev,
                                 n_masked=int(round(0.15 * a["n"])))
@@ -245,12 +247,13 @@ class Runner:
             m = base["mask"].cpu().numpy()
             act = m.astype(bool)
             t = base["targets"].cpu().numpy()
+            # gradient references are end to end: the oracle's own lse,
+            # never a value the GPU produced
             if man["operator"] == "logp":
                 rlogp, rlse = oracle.logp_selected(bits(base["x"]), t, m)
                 if backward:
-                    ref = {"dlogits": oracle.logp_backward(
-                        bits(base["x"]), t, m, self.run_op(man, shared, base, False)["lse"].cpu().numpy(),
-                        base["grad"].cpu().numpy())}
+                    ref = {"dlogits": oracle.logp_backward(bits(base["x"]), t, m, rlse,
+                                                           base["grad"].cpu().numpy())}
                 else:
                     ref = {"logp": rlogp, "lse": rlse}
                 tol = (lambda r: 2e-5 + 1e-5 * np.abs(r)) if not backward else (lambda r: 1e-3)
@@ -258,9 +261,8 @@ class Runner:
                 hb, wb = bits(base["x"]), bits(shared["weight"])
                 rlogp, rlse = oracle.linear_logp(hb, wb, t, m)
                 if backward:
-                    ref = {"dlogits": oracle.linear_logp_backward(
-                        hb, wb, t, m, self.run_op(man, shared, base, False)["lse"].cpu().numpy(),
-                        base["grad"].cpu().numpy())}
+                    ref = {"dlogits": oracle.linear_logp_backward(hb, wb, t, m, rlse,
+                                                                  base["grad"].cpu().numpy())}
                 else:
                     ref = {"logp": rlogp, "lse": rlse}
                 tol = (lambda r: 2e-3) if not backward else (lambda r: 1e-3)
@@ -311,7 +313,8 @@ class Runner:
                     "transform": {**t, "name": inv.TRANSFORM_NAMES[cls]}, "seed": man["seed"],
                     "device": str(self.dev), "direction": "backward" if backward else "forward",
                     "launch": {"calls": len(calls), "rows": [inv.nrows(c) for c in calls][:4]}}
-        recs, _ = inv.check(run, base, calls, row_map, manifest)
+        recs, _ = inv.check(run, base, calls, row_map, manifest,
+                            positions=shared.get("positions"))
         for r in recs:
             r["fixture_id"] = man["fixture_id"]
         rec.update({"status": "pass" if not recs else "fail",
@@ -322,9 +325,10 @@ class Runner:
 
 def _params_case(self, man, shared, base, rec):
     """Parameter gradients: accuracy of grad_hidden and grad_weight against
-    the oracle within the bound derived from the single bf16 rounding of D;
-    invariance of grad_hidden rows (harness) or of grad_weight over the same
-    complete sample set (masked rows appended), bitwise."""
+    the oracle's end-to-end gradients (its own lse) within min(1e-3, 1e-4 S +
+    1e-5), S the absolute sum of the summed terms; invariance of grad_hidden
+    rows (harness) or of grad_weight over the same complete sample set (masked
+    rows appended), bitwise."""
     import numpy as np
 
     import invariance as inv
@@ -341,10 +345,9 @@ def _params_case(self, man, shared, base, rec):
         hb, wb = bits(base["x"]), bits(w)
         t = base["targets"].cpu().numpy()
         m = base["mask"].cpu().numpy()
-        ls = lse.cpu().numpy()
         g = base["grad"].cpu().numpy()
-        rgh, rgw = oracle.linear_param_grads(hb, wb, t, m, ls, g)
-        d_abs = np.abs(oracle.linear_logp_backward(hb, wb, t, m, ls, g))
+        rgh, rgw = oracle.linear_param_grads(hb, wb, t, m, None, g)
+        d_abs = np.abs(oracle.linear_logp_backward(hb, wb, t, m, None, g))
         bounds = {"grad_hidden": d_abs @ np.abs(oracle.bf16_to_f64(wb)),
                   "grad_weight": d_abs.T @ np.abs(oracle.bf16_to_f64(hb))}
         worst = {"max_abs_error": 0.0, "max_rel_error": 0.0, "n_mismatched": 0, "n_compared": 0}
@@ -352,7 +355,7 @@ def _params_case(self, man, shared, base, rec):
         for k, got, ref in (("grad_hidden", gh, rgh), ("grad_weight", gw, rgw)):
             got = got.cpu().numpy().astype(np.float64)
             err = np.abs(got - ref)
-            bad = ~(err <= 2.0 ** -8 * bounds[k] + 1e-6)
+            bad = ~(err <= np.minimum(1e-3, 1e-4 * bounds[k] + 1e-5))
             worst["max_abs_error"] = max(worst["max_abs_error"], float(np.nanmax(err)))
             rel = err / np.maximum(np.abs(ref), 1e-30)
             worst["max_rel_error"] = max(worst["max_rel_error"], float(np.nanmax(rel)))

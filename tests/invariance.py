@@ -20,6 +20,13 @@ Fixture rules followed here (page "docs(ws1): ...", section
 Comparison is on raw 32-bit patterns, which is stricter than an all-close with
 zero tolerances: -0.0 differs from +0.0 and NaN payloads must match.
 
+Drift records name the logical token of a mismatch as (sample_id,
+token_position), whatever packing, padding or chunking the variant used: the
+drift report of page "[RFC] Batch-Invariant RL Kernel Suite for
+Train-Inference Consistency" (its list of proposed deliverables) carries the
+sequence id and token position, and page "[WS1 Test] #154 dtype pin + ...",
+section "Workstream 3 - #153", compares outputs by logical-workload identity.
+
 A batch here is a dict of row-aligned tensors -- ``x`` (logits or hidden
 rows), ``targets``, ``mask`` and optionally ``grad`` -- all with the same first
 dimension.  ``run(batch) -> dict`` returns row-aligned outputs (``logp``,
@@ -162,6 +169,28 @@ def t6_compacted(base):
     return [var], act
 
 
+def canonical_positions(n, seq_lens=None):
+    """(sample_id, token_position) of each of ``n`` base rows, int64 [n, 2].
+
+    With ``seq_lens`` the rows are sequences of those lengths packed back to
+    back (rows past them are padding: (-1, -1)); without, every row is a
+    sample of its own (position 0)."""
+    pos = torch.full((n, 2), -1, dtype=torch.int64)
+    if seq_lens is None:
+        pos[:, 0] = torch.arange(n)
+        pos[:, 1] = 0
+        return pos
+    off = 0
+    for s, L in enumerate(seq_lens):
+        L = int(L)
+        hi = min(n, off + L)
+        if hi > off:
+            pos[off:hi, 0] = s
+            pos[off:hi, 1] = torch.arange(hi - off)
+        off += L
+    return pos
+
+
 # ---------------------------------------------------------------------------
 # running and comparing
 
@@ -181,9 +210,13 @@ def _bits(t):
     return t
 
 
-def compare(base_out, var_out, row_map, base_mask, manifest):
+def compare(base_out, var_out, row_map, base_mask, manifest, positions=None):
     """Bitwise comparison of every output on the active base rows the
-    variant holds.  Returns a list of drift records (empty when invariant)."""
+    variant holds.  Returns a list of drift records (empty when invariant).
+    ``positions``: (sample_id, token_position) of each base row (see
+    canonical_positions; default: every row its own sample)."""
+    if positions is None:
+        positions = canonical_positions(nrows(base_out))
     row_map = torch.as_tensor(row_map, dtype=torch.int64)
     bm = base_mask.to("cpu") != 0
     held = torch.nonzero(row_map >= 0).flatten()
@@ -207,6 +240,8 @@ def compare(base_out, var_out, row_map, base_mask, manifest):
         finite = torch.isfinite(diff)
         nz = torch.nonzero(neq.reshape(neq.shape[0], -1))
         r, c = int(nz[0, 0]), int(nz[0, 1])
+        bad_rows = torch.unique(nz[:, 0])
+        logical = positions.index_select(0, base_rows.index_select(0, bad_rows))
         records.append({
             "relation": "invariance",
             "status": "fail",
@@ -227,17 +262,21 @@ def compare(base_out, var_out, row_map, base_mask, manifest):
             "n_mismatched": int(neq.sum()),
             "n_compared": int(neq.numel()),
             "units": "output elements",
-            "first_mismatch": {"logical_row": int(base_rows[r]), "variant_row": int(var_rows[r]),
+            "first_mismatch": {"sample_id": int(positions[base_rows[r], 0]),
+                               "token_position": int(positions[base_rows[r], 1]),
+                               "logical_row": int(base_rows[r]), "variant_row": int(var_rows[r]),
                                "column": c},
+            "n_tokens_mismatched": int(bad_rows.numel()),
+            "mismatched_tokens": [[int(a), int(b)] for a, b in logical[:16].tolist()],
             "launch": manifest.get("launch"),
             "seed": manifest.get("seed"),
         })
     return records
 
 
-def check(run, base, calls, row_map, manifest, base_out=None):
+def check(run, base, calls, row_map, manifest, base_out=None, positions=None):
     """Run baseline and variant, compare, return (records, base_out)."""
     if base_out is None:
         base_out = run(base)
     var_out = run_calls(run, calls)
-    return compare(base_out, var_out, row_map, base["mask"], manifest), base_out
+    return compare(base_out, var_out, row_map, base["mask"], manifest, positions), base_out

@@ -192,10 +192,11 @@ def test_linear_param_grads_validation(lib):
     f = lib.rlk_linear_logp_param_grads
     n, v, h = 300, 1000, 64
     ws = lib.rlk_linear_logp_param_grads_workspace_size(n, v, h)
-    # one vocabulary chunk of D in bf16, [N, C], C = V rounded up to 256 here,
-    # then a bf16 [N, H] copy of hidden with the inactive rows zeroed
+    # one vocabulary chunk of D as two bf16 arrays (D_hi, D_lo), each [N, C],
+    # C = V rounded up to 256 here, then a bf16 [N, H] copy of hidden with the
+    # inactive rows zeroed
     c = 1024
-    assert ws == (n * c * 2 + 255) // 256 * 256 + (n * h * 2 + 255) // 256 * 256
+    assert ws == 2 * ((n * c * 2 + 255) // 256 * 256) + (n * h * 2 + 255) // 256 * 256
     assert lib.rlk_linear_logp_param_grads_workspace_size(n, 200000, h) < \
         lib.rlk_linear_logp_param_grads_workspace_size(n, 20000, h) * 20   # chunked, not [N, V]
 

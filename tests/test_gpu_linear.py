@@ -1,6 +1,11 @@
 """GPU parity and bitwise invariance of the fused lm_head + selected logprob
 (linear_logp, K3 + K4) and of its backward to the logits (K5), through the C
-ABI, against the fp64 oracle."""
+ABI, against the fp64 oracle.
+
+Gradient references are end to end: the oracle's gradient from the bf16
+hidden, weight, targets, mask and upstream gradient alone (its own lse).  One
+separately named unit check feeds the kernel's lse to the oracle, to isolate
+K5."""
 import json
 import math
 
@@ -11,7 +16,7 @@ import torch
 import invariance as inv
 import invariant_logprob_amd as ilp
 import oracle
-from gpu_util import TOL_BWD, TOL_FUSED, assert_close, bits16, f32bits, require_gpu
+from gpu_util import TOL_BWD, TOL_FUSED, assert_close, bits16, f32bits, oracle_cached, require_gpu
 from invariant_logprob_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -42,9 +47,13 @@ def test_small_parity_fwd_bwd(dev, n, v, h):
     d = ilp.linear_logp_backward(b.hidden, b.weight, b.targets, lse, b.grad, b.mask)
     torch.cuda.synchronize()
     rd = oracle.linear_logp_backward(bits16(b.hidden), bits16(b.weight), b.targets.cpu().numpy(),
-                                     b.mask.cpu().numpy(), lse.cpu().numpy(), b.grad.cpu().numpy())
-    assert_close(d.cpu().numpy(), rd, TOL_BWD, f"fused dlogits {n}x{v}x{h}")
+                                     b.mask.cpu().numpy(), rlse, b.grad.cpu().numpy())
+    assert_close(d.cpu().numpy(), rd, TOL_BWD, f"fused dlogits {n}x{v}x{h} (end to end)")
     assert bool((f32bits(d)[~torch.from_numpy(act)] == 0).all())
+    # unit check of K5 alone: the oracle's backward given the kernel's lse
+    rd_k = oracle.linear_logp_backward(bits16(b.hidden), bits16(b.weight), b.targets.cpu().numpy(),
+                                       b.mask.cpu().numpy(), lse.cpu().numpy(), b.grad.cpu().numpy())
+    assert_close(d.cpu().numpy(), rd_k, TOL_BWD, f"K5 given the kernel's lse {n}x{v}x{h}")
 
 
 def test_closed_forms(dev):
@@ -132,18 +141,21 @@ def test_fused_transforms_small(dev):
 
 
 def test_fused_large_config(dev):
-    """hidden [8192, 4096], W [128256, 4096]: sampled rows against the oracle,
-    and the same rows bitwise at N = 1, 33 and 8192."""
+    """hidden [8192, 4096], W [128256, 4096]: against the oracle, two complete
+    256-token blocks (rows 0-255 and 4096-4351, every MFMA column position of
+    a tile) and rows 8160-8191 (the end of the last block), 544 rows; the same
+    rows bitwise at N = 1, 33 and 8192."""
     b = wl.fused_large(seed=0, device=dev)
     logp, lse = ilp.linear_logp(b.hidden, b.weight, b.targets, b.mask)
     torch.cuda.synchronize()
-    rows = [0, 1, 32, 255, 256, 4097, 8190, 8191]
+    rows = list(range(0, 256)) + list(range(4096, 4352)) + list(range(8160, 8192))
+    assert len(rows) == 544
     idx = torch.tensor(rows, device=dev)
     sub_h = b.hidden.index_select(0, idx)
     sub_t = b.targets.index_select(0, idx)
     rlogp, rlse = _oracle_fused(sub_h, b.weight, sub_t)
-    assert_close(logp.index_select(0, idx).cpu().numpy(), rlogp, TOL_FUSED, "C4 logp")
-    assert_close(lse.index_select(0, idx).cpu().numpy(), rlse, TOL_FUSED, "C4 lse")
+    assert_close(logp.index_select(0, idx).cpu().numpy(), rlogp, TOL_FUSED, "C4 logp (544 rows)")
+    assert_close(lse.index_select(0, idx).cpu().numpy(), rlse, TOL_FUSED, "C4 lse (544 rows)")
     for r in rows[:4]:
         one = ilp.linear_logp(b.hidden[r:r + 1], b.weight, b.targets[r:r + 1])
         assert _bits_equal(one[0], logp[r:r + 1]) and _bits_equal(one[1], lse[r:r + 1]), r
@@ -151,25 +163,38 @@ def test_fused_large_config(dev):
     assert _bits_equal(s33[0], logp[4090:4123]) and _bits_equal(s33[1], lse[4090:4123])
 
 
+def c5_oracle_forward(b):
+    """The oracle's (logp, lse) for every row of the hidden [2048, 5120],
+    W [151936, 5120] workload (computed once per session)."""
+    return oracle_cached(("fused_bwd", 0), lambda: _oracle_fused(b.hidden, b.weight, b.targets,
+                                                                 b.mask))
+
+
 def test_fused_backward_schedules(dev):
-    """hidden [2048, 5120], W [151936, 5120]: one prefill launch vs 4 chunks
-    of 512 vs 2048 single-row decode launches give identical logp, lse and
-    dlogits bits; sampled rows match the oracle."""
+    """hidden [2048, 5120], W [151936, 5120]: logp and lse of all 2048 rows
+    against the oracle; dlogits of 64 whole rows (both ends of each 512-row
+    chunk among them) element by element against the oracle's own gradient;
+    one prefill launch vs 4 chunks of 512 vs 2048 single-row decode launches
+    give identical logp, lse and dlogits bits."""
     b = wl.fused_bwd(seed=0, device=dev)
     n = b.hidden.shape[0]
     logp, lse = ilp.linear_logp(b.hidden, b.weight, b.targets, b.mask)
     d = ilp.linear_logp_backward(b.hidden, b.weight, b.targets, lse, b.grad, b.mask)
     torch.cuda.synchronize()
-    rows = [0, 5, 511, 512, 1500, 2047]
+    rlogp, rlse = c5_oracle_forward(b)
+    act = b.mask.cpu().numpy().astype(bool)
+    assert act.all()
+    assert_close(logp.cpu().numpy(), rlogp, TOL_FUSED, "C5 logp (all 2048 rows)")
+    assert_close(lse.cpu().numpy(), rlse, TOL_FUSED, "C5 lse (all 2048 rows)")
+    rows = sorted(set([0, 1, 511, 512, 1023, 1024, 1535, 1536, 2046, 2047] +
+                      torch.randperm(n, generator=torch.Generator().manual_seed(6))[:80].tolist()))[:64]
     idx = torch.tensor(rows, device=dev)
     sub_h = b.hidden.index_select(0, idx)
     sub_t = b.targets.index_select(0, idx)
-    rlogp, rlse = _oracle_fused(sub_h, b.weight, sub_t)
-    assert_close(logp.index_select(0, idx).cpu().numpy(), rlogp, TOL_FUSED, "C5 logp")
     rd = oracle.linear_logp_backward(bits16(sub_h), bits16(b.weight), sub_t.cpu().numpy(), None,
-                                     lse.index_select(0, idx).cpu().numpy(),
-                                     b.grad.index_select(0, idx).cpu().numpy())
-    assert_close(d.index_select(0, idx).cpu().numpy(), rd, TOL_BWD, "C5 dlogits")
+                                     rlse[rows], b.grad.index_select(0, idx).cpu().numpy())
+    assert_close(d.index_select(0, idx).cpu().numpy(), rd, TOL_BWD,
+                 "C5 dlogits (64 whole rows, end to end)")
     # 4 chunks of 512
     for c0 in range(0, n, 512):
         sl = slice(c0, c0 + 512)
@@ -228,3 +253,57 @@ def test_binding_refuses_bad_outputs_and_workspaces(dev):
         ilp.logp_backward(x, t, lse, lse, out=buf[: 4 * 1024].view(4, 1024))
     assert e.value.status == 1
     torch.cuda.synchronize()
+
+
+def test_nonfinite_active_rows_reach_the_gradient(dev):
+    """An active row whose hidden holds NaN (row 2) or +inf everywhere (row 5:
+    with mixed-sign weight rows every logit is NaN) gets an all-NaN gradient
+    row from the fused backward, from the backward over kept fp32 logits and
+    from the parameter gradients (its grad_hidden row; grad_weight sums over
+    it); on the bf16 logits path a row holding NaN or +inf likewise gets an
+    all-NaN row.  Masked rows with the same poison give +0.0 everywhere, and
+    the other rows keep the bits they have without the poisoned rows."""
+    n, v, h = 12, 700, 64
+    b = wl.fused_batch(n, v, h, seed=31, device=dev, w_sigma=0.05)
+    hid = b.hidden.clone()
+    hid[2, 7] = float("nan")
+    hid[5, :] = float("inf")
+    hid[8, ::2] = float("-inf")
+    hid[9, 3] = float("nan")
+    mask = torch.ones(n, dtype=torch.uint8, device=dev)
+    mask[8] = 0
+    mask[9] = 0
+    w, t, g = b.weight, b.targets, b.grad
+    _, lse = ilp.linear_logp(hid, w, t, mask)
+    d = ilp.linear_logp_backward(hid, w, t, lse, g, mask)
+    _, klse, z = ilp.linear_logp_with_logits(hid, w, t, mask)
+    dk = ilp.logp_backward(z, t, klse, g, mask)
+    gh, gw = ilp.linear_logp_param_grads(hid, w, t, lse, g, mask)
+    torch.cuda.synchronize()
+    clean_rows = [0, 1, 3, 4, 6, 7, 10, 11]
+    ci = torch.tensor(clean_rows, device=dev)
+    _, lse_c = ilp.linear_logp(hid[ci], w, t[ci])
+    d_c = ilp.linear_logp_backward(hid[ci], w, t[ci], lse_c, g[ci])
+    torch.cuda.synchronize()
+    for name, dd in (("fused", d), ("kept logits", dk)):
+        assert bool(torch.isnan(dd[2]).all()) and bool(torch.isnan(dd[5]).all()), name
+        assert bool((f32bits(dd[8:10]) == 0).all()), name
+        assert torch.equal(f32bits(dd[ci]), f32bits(d_c)), name
+    assert bool(torch.isnan(gh[2]).all()) and bool(torch.isnan(gh[5]).all())
+    assert bool((f32bits(gh[8:10]) == 0).all())
+    assert bool(torch.isfinite(gh[ci]).all()) and bool(torch.isnan(gw).all())
+    # bf16 logits path
+    # (a width of 704: bf16 rows need a multiple of 8 elements; targets < 700)
+    x = (torch.randn((n, 704), generator=torch.Generator(device=dev).manual_seed(3), device=dev)
+         * 2).to(torch.bfloat16)
+    x[2, 11] = float("nan")
+    x[5, 40] = float("inf")
+    x[6, ::5] = float("-inf")      # -inf entries only contribute zero
+    x[8, 0] = float("nan")
+    x[9, 1] = float("inf")
+    _, lse_x = ilp.logp_selected(x, t, mask)
+    dx = ilp.logp_backward(x, t, lse_x, g, mask)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(dx[2]).all()) and bool(torch.isnan(dx[5]).all())
+    assert bool(torch.isfinite(dx[6]).all())
+    assert bool((f32bits(dx[8:10]) == 0).all())

@@ -1,5 +1,10 @@
 """GPU parity of the logits path (forward K1, backward K2) against the fp64
-oracle, through the C ABI."""
+oracle, through the C ABI.
+
+Gradient references are end to end: the oracle's gradient of the whole
+definition from the bf16 logits, targets, mask and upstream gradient alone
+(its own log-sum-exp), never a value the GPU produced.  One separately named
+unit check feeds the kernel's lse to the oracle's backward, to isolate K2."""
 import math
 
 import numpy as np
@@ -8,7 +13,8 @@ import torch
 
 import invariant_logprob_amd as ilp
 import oracle
-from gpu_util import TOL_BWD, assert_close, bits16, f32bits, padded_bf16, require_gpu, tol_logits
+from gpu_util import (TOL_BWD, assert_close, bits16, f32bits, oracle_logp_rows, padded_bf16,
+                      require_gpu, tol_logits)
 from invariant_logprob_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -35,9 +41,8 @@ def _run_and_compare(logits, targets, mask, what, grad=None):
     if grad is not None:
         d = ilp.logp_backward(logits, targets, lse, grad, mask)
         torch.cuda.synchronize()
-        rd = oracle.logp_backward(bits, t, m, lse.cpu().numpy().astype(np.float64),
-                                  grad.cpu().numpy())
-        assert_close(d.cpu().numpy(), rd, TOL_BWD, f"{what} dlogits")
+        rd = oracle.logp_backward(bits, t, m, rlse, grad.cpu().numpy())
+        assert_close(d.cpu().numpy(), rd, TOL_BWD, f"{what} dlogits (end to end)")
         assert np.all(f32bits(d).numpy()[~act] == 0), "inactive rows must be +0.0"
     return logp, lse
 
@@ -61,65 +66,87 @@ def test_ragged_vocab_parity(dev, v):
 
 
 def test_varlen_config_parity(dev):
-    """8 packed varlen sequences, V=32000, 5% peaked rows, half argmax targets:
-    one launch over all rows; the oracle checks a seeded sample of 1024 rows
-    (peaked rows and the last rows included) and every padding row is +0.0."""
+    """8 packed varlen sequences, V=32000, 5% peaked rows, half argmax targets,
+    in one launch: logp and lse of every row against the oracle (all active
+    rows, over 4000 of them; more than 100 peaked), every padding row +0.0;
+    dlogits of the first 96 rows and of 32 peaked rows, element by element,
+    against the oracle's own gradient."""
     b = wl.logits_varlen(seed=0, device=dev)
     logp, lse = ilp.logp_selected(b.logits, b.targets, b.mask)
-    torch.cuda.synchronize()
-    n = b.logits.shape[0]
-    total = sum(b.seq_lens)
-    peaked = torch.nonzero(b.logits.float().amax(dim=1) > 15).flatten().cpu().tolist()
-    pick = torch.randperm(n, generator=torch.Generator().manual_seed(3))[:1024].tolist()
-    rows = sorted(set(pick + peaked[:64] + [0, total - 1, total, n - 1]))
-    idx = torch.tensor(rows, device=dev)
-    sub = b.logits.index_select(0, idx)
-    t = b.targets.index_select(0, idx).cpu().numpy()
-    m = b.mask.index_select(0, idx).cpu().numpy()
-    rlogp, rlse = oracle.logp_selected(bits16(sub), t, m)
-    act = m.astype(bool)
-    assert act.sum() > 900 and len(peaked) > 100
-    assert_close(logp.index_select(0, idx).cpu().numpy(), rlogp, tol_logits, "varlen logp", act)
-    assert_close(lse.index_select(0, idx).cpu().numpy(), rlse, tol_logits, "varlen lse", act)
-    assert bool((f32bits(logp)[total:] == 0).all()) and bool((f32bits(lse)[total:] == 0).all())
-    # backward on a bounded slice of rows (the oracle's dense [N, V] output)
-    sl = slice(0, 96)
-    lp, lse96 = ilp.logp_selected(b.logits[sl], b.targets[sl], b.mask[sl])
-    d = ilp.logp_backward(b.logits[sl], b.targets[sl], lse96, b.grad[sl], b.mask[sl])
-    rd = oracle.logp_backward(bits16(b.logits[sl]), b.targets[sl].cpu().numpy(),
-                              b.mask[sl].cpu().numpy(), lse96.cpu().numpy(), b.grad[sl].cpu().numpy())
-    assert_close(d.cpu().numpy(), rd, TOL_BWD, "varlen dlogits")
-
-
-def test_large_config_sampled_rows(dev):
-    """N=16384, V=151936 in one launch; rows sampled for the oracle."""
-    b = wl.logits_large(seed=0, device=dev)
-    logp, lse = ilp.logp_selected(b.logits, b.targets, b.mask)
-    torch.cuda.synchronize()
-    n = b.logits.shape[0]
-    rows = sorted(set([0, 1, 255, 256, 8191, n - 2, n - 1] +
-                      torch.randperm(n, generator=torch.Generator().manual_seed(5))[:40].tolist()))
-    idx = torch.tensor(rows, device=dev)
-    sub_bits = bits16(b.logits.index_select(0, idx))
-    t = b.targets.index_select(0, idx).cpu().numpy()
-    m = b.mask.index_select(0, idx).cpu().numpy()
-    rlogp, rlse = oracle.logp_selected(sub_bits, t, m)
-    act = m.astype(bool)
-    assert_close(logp.index_select(0, idx).cpu().numpy(), rlogp, tol_logits, "large logp", act)
-    assert_close(lse.index_select(0, idx).cpu().numpy(), rlse, tol_logits, "large lse", act)
-    inactive = (b.mask == 0)
-    assert int(inactive.sum()) == 2458
-    assert bool((f32bits(logp)[inactive.cpu()] == 0).all())
-    # backward at full size, sampled rows
     d = ilp.logp_backward(b.logits, b.targets, lse, b.grad, b.mask)
     torch.cuda.synchronize()
-    rd = oracle.logp_backward(sub_bits, t, m, lse.index_select(0, idx).cpu().numpy(),
-                              b.grad.index_select(0, idx).cpu().numpy())
-    assert_close(d.index_select(0, idx).cpu().numpy(), rd, TOL_BWD, "large dlogits")
+    total = sum(b.seq_lens)
+    peaked = torch.nonzero(b.logits.float().amax(dim=1) > 15).flatten().cpu().tolist()
+    bits = bits16(b.logits)
+    t = b.targets.cpu().numpy()
+    m = b.mask.cpu().numpy()
+    rlogp, rlse = oracle_logp_rows(bits, t, m)
+    act = m.astype(bool)
+    assert act.sum() == total and act.sum() > 4000 and len(peaked) > 100
+    assert_close(logp.cpu().numpy(), rlogp, tol_logits, "varlen logp (all rows)", act)
+    assert_close(lse.cpu().numpy(), rlse, tol_logits, "varlen lse (all rows)", act)
+    assert bool((f32bits(logp)[total:] == 0).all()) and bool((f32bits(lse)[total:] == 0).all())
+    rows = sorted(set(range(96)) | set(peaked[:32]))
+    idx = torch.tensor(rows, device=dev)
+    rd = oracle.logp_backward(bits[rows], t[rows], m[rows], None, b.grad[idx].cpu().numpy())
+    assert_close(d.index_select(0, idx).cpu().numpy(), rd, TOL_BWD, "varlen dlogits (end to end)")
+
+
+def test_large_config_all_rows(dev):
+    """N=16384, V=151936 in one launch: logp and lse of all 13926 active rows
+    against the oracle (run over row blocks in a thread pool), all 2458 masked
+    rows +0.0; dlogits of 64 whole active rows (the first and last rows of
+    several 256-row spans among them) element by element against the
+    oracle's own gradient, 8 masked rows all +0.0, and every active row of
+    the first 4096 summing to ~0."""
+    b = wl.logits_large(seed=0, device=dev)
+    logp, lse = ilp.logp_selected(b.logits, b.targets, b.mask)
+    d = ilp.logp_backward(b.logits, b.targets, lse, b.grad, b.mask)
+    torch.cuda.synchronize()
+    n = b.logits.shape[0]
+    bits = bits16(b.logits)
+    t = b.targets.cpu().numpy()
+    m = b.mask.cpu().numpy()
+    act = m.astype(bool)
+    assert int(act.sum()) == 13926 and int((~act).sum()) == 2458
+    rlogp, rlse = oracle_logp_rows(bits, t, m)
+    assert_close(logp.cpu().numpy(), rlogp, tol_logits, "large logp (all 13926 active rows)", act)
+    assert_close(lse.cpu().numpy(), rlse, tol_logits, "large lse (all 13926 active rows)", act)
+    assert bool((f32bits(logp)[~torch.from_numpy(act)] == 0).all())
+    assert bool((f32bits(lse)[~torch.from_numpy(act)] == 0).all())
+    active_rows = np.nonzero(act)[0]
+    edge = [int(r) for r in active_rows[[0, 1, -2, -1]]]
+    near = [int(active_rows[np.searchsorted(active_rows, k)]) for k in (255, 256, 8191, 8192)]
+    pick = torch.randperm(active_rows.size, generator=torch.Generator().manual_seed(5)).tolist()
+    rows = sorted(set(edge + near))
+    for k in pick:
+        if len(rows) == 64:
+            break
+        if int(active_rows[k]) not in rows:
+            rows = sorted(rows + [int(active_rows[k])])
+    assert len(rows) == 64
+    idx = torch.tensor(rows, device=dev)
+    rd = oracle.logp_backward(bits[rows], t[rows], m[rows], rlse[rows], b.grad[idx].cpu().numpy())
+    assert_close(d.index_select(0, idx).cpu().numpy(), rd, TOL_BWD,
+                 "large dlogits (64 whole rows, end to end)")
+    masked = torch.tensor(np.nonzero(~act)[0][:8], device=dev)
+    assert bool((f32bits(d.index_select(0, masked)) == 0).all())
     # property at any size: each active row of dlogits sums to ~0
     rs = d[:4096].double().sum(dim=1).cpu().numpy()
-    act4 = b.mask[:4096].cpu().numpy().astype(bool)
-    assert np.max(np.abs(rs[act4])) < 1e-3
+    assert np.max(np.abs(rs[act[:4096]])) < 1e-3
+
+
+def test_k2_unit_check_with_kernel_lse(dev):
+    """Unit check of K2 alone: the oracle's backward given the kernel's own
+    lse (the end-to-end checks above give it the oracle's)."""
+    b = wl.logits_varlen(seed=2, device=dev)
+    sl = slice(0, 128)
+    _, lse = ilp.logp_selected(b.logits[sl], b.targets[sl], b.mask[sl])
+    d = ilp.logp_backward(b.logits[sl], b.targets[sl], lse, b.grad[sl], b.mask[sl])
+    torch.cuda.synchronize()
+    rd = oracle.logp_backward(bits16(b.logits[sl]), b.targets[sl].cpu().numpy(),
+                              b.mask[sl].cpu().numpy(), lse.cpu().numpy(), b.grad[sl].cpu().numpy())
+    assert_close(d.cpu().numpy(), rd, TOL_BWD, "K2 given the kernel's lse")
 
 
 def test_closed_forms(dev):

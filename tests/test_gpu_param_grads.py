@@ -2,13 +2,14 @@
 grad_hidden = D . W and grad_weight = D^T . h (D the logits gradient),
 through the C ABI, against the fp64 oracle.
 
-Tolerance.  The pages give none for these outputs, so it is derived from the
-arithmetic: the library rounds each entry of D once to bf16 (relative error
-at most 2^-9) and multiplies on bf16 MFMA with fp32 accumulation.  Per
-element the rounding alone can move grad_hidden[i, k] by at most
-2^-9 * sum_j |D_ij| |W_jk| (and grad_weight[j, k] by 2^-9 * sum_i |D_ij|
-|h_ik|).  The tests allow twice that bound plus 1e-6, which also covers the
-fp32 sums and the fp32 logits and lse feeding D.
+Tolerance, fixed before any measurement and independent of how the library
+forms its operands: the target's backward bound |delta| <= 1e-3 for every
+gradient entry, and an fp32-grade bound |delta| <= 1e-4 S + 1e-5, where S is
+the sum of the absolute values of the summed terms (sum_j |D_ij| |W_jk| for
+grad_hidden[i, k], sum_i |D_ij| |h_ik| for grad_weight[j, k]); see
+gpu_util.param_tol.  References are end to end: the oracle's gradients from
+the bf16 inputs, targets, mask and upstream gradient alone, with its own
+log-sum-exp.
 """
 import json
 
@@ -19,16 +20,10 @@ import torch
 import invariance as inv
 import invariant_logprob_amd as ilp
 import oracle
-from gpu_util import assert_close, bits16, f32bits, require_gpu
+from gpu_util import assert_close, bits16, f32bits, oracle_cached, param_tol, require_gpu
 from invariant_logprob_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
-
-ROUNDING = 2.0 ** -9
-
-
-def tol_from(bound):
-    return 2 * ROUNDING * bound + 1e-6
 
 
 @pytest.fixture(scope="module")
@@ -59,14 +54,14 @@ def test_small_parity(dev, n, v, h):
     hb, wb = bits16(b.hidden), bits16(b.weight)
     t = b.targets.cpu().numpy()
     m = b.mask.cpu().numpy()
-    ls = lse.cpu().numpy()
     g = b.grad.cpu().numpy()
-    rgh, rgw = oracle.linear_param_grads(hb, wb, t, m, ls, g)
-    d_abs = np.abs(oracle.linear_logp_backward(hb, wb, t, m, ls, g))
+    # end to end: lse=None makes the oracle take its own log-sum-exp
+    rgh, rgw = oracle.linear_param_grads(hb, wb, t, m, None, g)
+    d_abs = np.abs(oracle.linear_logp_backward(hb, wb, t, m, None, g))
     h_abs = np.abs(oracle.bf16_to_f64(hb))
     w_abs = np.abs(oracle.bf16_to_f64(wb))
-    assert_close(gh.cpu().numpy(), rgh, tol_from(d_abs @ w_abs), f"grad_hidden {n}x{v}x{h}")
-    assert_close(gw.cpu().numpy(), rgw, tol_from(d_abs.T @ h_abs), f"grad_weight {n}x{v}x{h}")
+    assert_close(gh.cpu().numpy(), rgh, param_tol(d_abs @ w_abs), f"grad_hidden {n}x{v}x{h}")
+    assert_close(gw.cpu().numpy(), rgw, param_tol(d_abs.T @ h_abs), f"grad_weight {n}x{v}x{h}")
     inactive = torch.from_numpy(m == 0)
     assert bool((f32bits(gh)[inactive] == 0).all()), "inactive rows must be +0.0"
     # one output at a time gives the same bits
@@ -88,9 +83,9 @@ def test_closed_forms(dev):
     torch.cuda.synchronize()
     w64 = w.double().cpu()
     ref = g.double().cpu()[:, None] * (w64[t.cpu()] - w64.mean(dim=0))
-    # D = g (onehot - 1/V) in bf16: 1/V rounds with relative error 2^-9
-    bound = (g.double().abs().cpu()[:, None] * (w64[t.cpu()].abs() + w64.abs().mean(dim=0)))
-    assert_close(gh.cpu().numpy(), ref.numpy(), tol_from(bound.numpy()), "zero-hidden grad_h")
+    # sum_j |D_ij| |W_jk| = |g_i| (|W_t,k| (1 - 1/V) + mean_j |W_jk| - |W_t,k| / V)
+    scale = (g.double().abs().cpu()[:, None] * (w64[t.cpu()].abs() + w64.abs().mean(dim=0)))
+    assert_close(gh.cpu().numpy(), ref.numpy(), param_tol(scale.numpy()), "zero-hidden grad_h")
     assert float(gw.abs().max()) == 0.0
     # a row with g = 0 has zero hidden gradient bits
     assert bool((f32bits(gh[3]) == 0).all())
@@ -183,16 +178,18 @@ def test_grad_weight_determinism_and_layouts(dev):
     torch.cuda.synchronize()
     hb, wb = bits16(b.hidden), bits16(b.weight)
     d_abs = np.abs(oracle.linear_logp_backward(hb, wb, b.targets.cpu().numpy(), b.mask.cpu().numpy(),
-                                               lse.cpu().numpy(), b.grad.cpu().numpy()))
-    bound = d_abs.T @ np.abs(oracle.bf16_to_f64(hb))
-    assert_close(gw_perm.cpu().numpy(), gw.cpu().numpy().astype(np.float64), 2 * tol_from(bound),
+                                               None, b.grad.cpu().numpy()))
+    scale = d_abs.T @ np.abs(oracle.bf16_to_f64(hb))
+    # two sums of the same terms, each within param_tol of the exact value
+    assert_close(gw_perm.cpu().numpy(), gw.cpu().numpy().astype(np.float64), 2 * param_tol(scale),
                  "grad_weight under a permutation")
 
 
 def test_full_size_sampled(dev):
     """hidden [2048, 5120], W [151936, 5120]: sampled rows of both gradients
-    against the oracle; grad_hidden rows bitwise equal from a 512-row call and
-    from single-row calls."""
+    against the oracle's end-to-end gradients (its lse from its own forward
+    over all 2048 rows); grad_hidden rows bitwise equal from a 512-row call
+    and from single-row calls."""
     b = wl.fused_bwd(seed=0, device=dev)
     n = b.hidden.shape[0]
     _, lse = ilp.linear_logp(b.hidden, b.weight, b.targets, b.mask)
@@ -200,8 +197,8 @@ def test_full_size_sampled(dev):
     hb, wb = bits16(b.hidden), bits16(b.weight)
     t = b.targets.cpu().numpy()
     m = b.mask.cpu().numpy()
-    ls = lse.cpu().numpy()
     g = b.grad.cpu().numpy()
+    _, ls = oracle_cached(("fused_bwd", 0), lambda: oracle.linear_logp(hb, wb, t, m))
     rows = [0, 777, 2047]
     rgh = oracle.linear_grad_hidden_rows(hb, wb, t, m, ls, g, rows)
     w64 = oracle.bf16_to_f64(wb)
@@ -209,7 +206,7 @@ def test_full_size_sampled(dev):
                                            ls[rows], g[rows])
     bound_h = np.abs(d_rows) @ np.abs(w64)
     del w64
-    assert_close(gh[rows].cpu().numpy(), rgh, tol_from(bound_h), "C5 grad_hidden rows")
+    assert_close(gh[rows].cpu().numpy(), rgh, param_tol(bound_h), "C5 grad_hidden rows")
     vrows = sorted({int(t[0]), int(t[1000]), 0, 75000, 151935})
     rgw = oracle.linear_grad_weight_rows(hb, wb, t, m, ls, g, vrows)
     h64 = oracle.bf16_to_f64(hb)
@@ -219,7 +216,7 @@ def test_full_size_sampled(dev):
     onehot = (t[:, None] == np.asarray(vrows)[None, :]).astype(np.float64)
     d_cols = np.where(act[:, None], g[:, None] * (onehot - p), 0.0)
     bound_w = np.abs(d_cols).T @ np.abs(h64)
-    assert_close(gw[vrows].cpu().numpy(), rgw, tol_from(bound_w), "C5 grad_weight rows")
+    assert_close(gw[vrows].cpu().numpy(), rgw, param_tol(bound_w), "C5 grad_weight rows")
     sl = slice(512, 1024)
     gh_c, _ = ilp.linear_logp_param_grads(b.hidden[sl], b.weight, b.targets[sl], lse[sl], b.grad[sl],
                                           b.mask[sl], want_weight=False)

@@ -68,9 +68,11 @@ def test_small_parity_and_bits(dev, n, v, h):
     assert _bits_equal(d, d_re)
     assert bool(torch.isnan(dbuf[:, v:]).all()), "columns >= V of the gradient were written"
     act = b.mask.cpu().numpy().astype(bool)
+    _, rlse = oracle.linear_logp(bits16(b.hidden), bits16(b.weight), b.targets.cpu().numpy(),
+                                 act.astype(np.uint8))
     rd = oracle.linear_logp_backward(bits16(b.hidden), bits16(b.weight), b.targets.cpu().numpy(),
-                                     act.astype(np.uint8), lse.cpu().numpy(), b.grad.cpu().numpy())
-    assert_close(d.cpu().numpy(), rd, TOL_BWD, f"dlogits from kept logits {n}x{v}x{h}")
+                                     act.astype(np.uint8), rlse, b.grad.cpu().numpy())
+    assert_close(d.cpu().numpy(), rd, TOL_BWD, f"dlogits from kept logits {n}x{v}x{h} (end to end)")
     assert bool((f32bits(d)[~torch.from_numpy(act)] == 0).all()), "masked rows not +0.0"
     # in place: the gradient overwrites the logits
     z2 = zbuf.clone()[:, :v]

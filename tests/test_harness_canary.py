@@ -156,3 +156,30 @@ def test_large_recipe_mask_count():
     b = wl.logits_batch(2000, 8, 4.0, seed=0, n_masked=int(round(0.15 * 2000)))
     assert int((b.mask == 0).sum()) == 300
     assert bool((b.targets[b.mask == 0] == -100).all())
+
+
+def test_drift_records_name_sample_and_position():
+    """A planted mismatch in a packed batch is reported at its canonical
+    (sample_id, token_position), whatever row the variant held it in."""
+    base = _base(n=12, v=40, n_masked=0)
+    out = fixed_schedule(base)
+    seq_lens = [5, 4, 3]
+    pos = inv.canonical_positions(12, seq_lens)
+    assert pos[:, 0].tolist() == [0] * 5 + [1] * 4 + [2] * 3
+    assert pos[:, 1].tolist() == list(range(5)) + list(range(4)) + list(range(3))
+    # the variant holds the base rows reversed; base row 6 (sample 1, token 1)
+    # and base row 11 (sample 2, token 2) differ by one ulp
+    perm = torch.arange(11, -1, -1)
+    var = {k: v.index_select(0, perm).clone() for k, v in out.items()}
+    bits = var["lse"].view(torch.int32)
+    bits[5] ^= 1      # variant row 5 = base row 6
+    bits[0] ^= 1      # variant row 0 = base row 11
+    recs = inv.compare(out, var, perm, base["mask"], {"operator": "x"}, positions=pos)
+    assert len(recs) == 1 and recs[0]["output"] == "lse"
+    first = recs[0]["first_mismatch"]
+    assert (first["sample_id"], first["token_position"]) == (1, 1)
+    assert (first["logical_row"], first["variant_row"]) == (6, 5)
+    assert recs[0]["mismatched_tokens"] == [[1, 1], [2, 2]]
+    assert recs[0]["n_tokens_mismatched"] == 2
+    # padding rows past the sequences have no logical identity
+    assert inv.canonical_positions(14, seq_lens)[12:].tolist() == [[-1, -1], [-1, -1]]
