@@ -154,6 +154,29 @@ int rlk_linear_logp(const void* hidden, int64_t ld_h, const void* weight,
                     hipStream_t stream);
 
 /*
+ * rlk_linear_logp for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * It takes no workspace: the chunk partials live in a library-owned device
+ * array of 32 MiB (one per GPU, held until the process ends), so it
+ * allocates nothing and calls no allocating routine.  Arguments, outputs,
+ * kernels and results are those of rlk_linear_logp (the outputs are
+ * bit-identical to its outputs for the same inputs).
+ *   Limit: rlk_linear_logp_workspace_size(N, V, H) <= 32 MiB, otherwise
+ *   RLK_ERR_UNSUPPORTED before any launch (up to 7055 rows at V = 151936,
+ *   8363 rows at V = 128256).
+ *   The array serves the current HIP device (the caller makes the stream's
+ *   device current) and is shared by every call on that GPU: two calls that
+ *   overlap in time on one GPU (other streams, other host threads) race on
+ *   it; calls ordered on one stream are safe.  Nothing in it needs clearing
+ *   between calls.  RLK_ERR_LAUNCH if its device address cannot be found.
+ */
+int rlk_linear_logp_noalloc(const void* hidden, int64_t ld_h,
+                            const void* weight, int64_t ld_w,
+                            const int64_t* targets, const uint8_t* mask,
+                            int64_t N, int64_t V, int64_t H, float* logp,
+                            float* lse, hipStream_t stream);
+
+/*
  * Backward of the selected logprob with respect to the logits:
  *   grad_logits[i, j] = grad_logp[i] * ([j == t_i] - exp(x_ij - lse_i)),
  * fp32 [N, ld_g] (ld_g >= V, ld_g % 4 == 0, 16-B aligned); columns >= V are

@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     linear_logp_backward,
     linear_logp_param_grads,
     linear_logp_param_grads_workspace_size,
+    linear_logp_noalloc,
     linear_logp_with_logits,
     linear_logp_workspace_size,
     load_library,
@@ -28,6 +29,6 @@ from ._binding import (  # noqa: F401
 __all__ = [
     "LinearLogprob", "RlkError", "SelectedLogprob", "build_info", "library_path", "linear_logp",
     "linear_logp_backward", "linear_logp_param_grads", "linear_logp_param_grads_workspace_size",
-    "linear_logp_with_logits", "linear_logp_workspace_size", "load_library", "log_softmax", "logp_backward", "logp_entropy",
+    "linear_logp_noalloc", "linear_logp_with_logits", "linear_logp_workspace_size", "load_library", "log_softmax", "logp_backward", "logp_entropy",
     "logp_selected", "token_losses",
 ]

@@ -52,6 +52,8 @@ def load_library():
     lib.rlk_linear_logp_workspace_size.restype = sz
     lib.rlk_linear_logp.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
     lib.rlk_linear_logp.restype = ctypes.c_int
+    lib.rlk_linear_logp_noalloc.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, vp, vp, vp]
+    lib.rlk_linear_logp_noalloc.restype = ctypes.c_int
     lib.rlk_logp_backward.argtypes = [vp, i64, vp, i64, vp, i64, i64, vp, vp, vp, vp, i64, i64, vp,
                                       i64, vp]
     lib.rlk_logp_backward.restype = ctypes.c_int
@@ -292,6 +294,36 @@ def linear_logp(hidden, weight, targets, mask=None, *, workspace=None, logp=None
                                  v, h, _ptr(logp), _ptr(lse), _ptr(workspace), ws_bytes,
                                  _stream(dev))
     _raise(st, "rlk_linear_logp")
+    return logp, lse
+
+
+def linear_logp_noalloc(hidden, weight, targets, mask=None, *, logp=None, lse=None):
+    """linear_logp through rlk_linear_logp_noalloc: no workspace, the library's
+    own 32 MiB per-GPU array holds the partials (for callers that cannot
+    allocate; pass logp and lse to allocate nothing here either).  Calls that
+    overlap in time on one GPU race on that array.  Returns (logp, lse)."""
+    lib = load_library()
+    ldh = _matrix(hidden, "hidden", torch.bfloat16)
+    ldw = _matrix(weight, "weight", torch.bfloat16)
+    n, h = hidden.shape
+    v, h2 = weight.shape
+    if h != h2:
+        raise ValueError(f"hidden has H={h} but weight has H={h2}")
+    _rows(targets, "targets", n, torch.int64)
+    mask = _mask(mask, n)
+    dev = _same_device(hidden, weight, targets, mask)
+    if logp is None:
+        logp = torch.empty(n, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(n, dtype=torch.float32, device=dev)
+    _rows(logp, "logp", n, torch.float32)
+    _rows(lse, "lse", n, torch.float32)
+    if n == 0:
+        return logp, lse
+    with torch.cuda.device(dev):
+        st = lib.rlk_linear_logp_noalloc(_ptr(hidden), ldh, _ptr(weight), ldw, _ptr(targets),
+                                         _ptr(mask), n, v, h, _ptr(logp), _ptr(lse), _stream(dev))
+    _raise(st, "rlk_linear_logp_noalloc")
     return logp, lse
 
 

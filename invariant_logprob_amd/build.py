@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librlk.so")
-SOURCES = ["rlk_api.hip", "logits_rows.hip", "linear_tiles.hip", "linear_grads.hip", "token_losses.hip"]
+SOURCES = ["rlk_api.hip", "logits_rows.hip", "linear_tiles.hip", "linear_grads.hip", "token_losses.hip",
+           "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = [

@@ -12,6 +12,7 @@
 #include "rlk.h"
 #include "rlk_internal.hpp"
 
+
 #ifndef RLK_GIT_REV
 #define RLK_GIT_REV "unknown"
 #endif
@@ -85,6 +86,7 @@ int check_sizes(int64_t N, int64_t V) {
   return RLK_OK;
 }
 
+
 // Both parameter-gradient entry points: logits null (recomputed per chunk)
 // or the fp32 logits the forward kept.
 int param_grads(const float* logits, int64_t ld_z, const void* hidden, int64_t ld_h,
@@ -142,6 +144,21 @@ int param_grads(const float* logits, int64_t ld_z, const void* hidden, int64_t l
 
 }  // namespace
 
+namespace rlk {
+
+// Validation shared by rlk_linear_logp and its allocation-free variant
+// (everything but the workspace).
+int check_linear_logp_args(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
+                           const int64_t* targets, const float* logp, int64_t N, int64_t V,
+                           int64_t H) {
+  const int st = check_sizes(N, V);
+  if (st != RLK_OK || N == 0) return st;
+  if (targets == nullptr || logp == nullptr) return RLK_ERR_INVALID_ARG;
+  return check_linear(hidden, ld_h, weight, ld_w, N, V, H);
+}
+
+}  // namespace rlk
+
 extern "C" {
 
 int rlk_logp_selected(const void* logits, int64_t ld, const int64_t* targets, const uint8_t* mask,
@@ -197,12 +214,9 @@ int rlk_linear_logp(const void* hidden, int64_t ld_h, const void* weight, int64_
                     const int64_t* targets, const uint8_t* mask, int64_t N, int64_t V, int64_t H,
                     float* logp, float* lse, void* workspace, size_t workspace_bytes,
                     hipStream_t stream) {
-  int st = check_sizes(N, V);
-  if (st != RLK_OK) return st;
-  if (N == 0) return RLK_OK;
-  if (targets == nullptr || logp == nullptr || workspace == nullptr) return RLK_ERR_INVALID_ARG;
-  st = check_linear(hidden, ld_h, weight, ld_w, N, V, H);
-  if (st != RLK_OK) return st;
+  const int st = rlk::check_linear_logp_args(hidden, ld_h, weight, ld_w, targets, logp, N, V, H);
+  if (st != RLK_OK || N == 0) return st;
+  if (workspace == nullptr) return RLK_ERR_INVALID_ARG;
   if (workspace_bytes < rlk::linear_workspace_bytes(N, V)) return RLK_ERR_INVALID_ARG;
   if (!aligned16(workspace)) return RLK_ERR_UNSUPPORTED;
   return status_of(rlk::launch_linear_logp(

@@ -43,6 +43,12 @@ hipError_t launch_logp_bwd_rows_f32(const float* logits, int64_t ld, const int64
 
 size_t linear_workspace_bytes(int64_t N, int64_t V);
 
+// Argument checks of the fused forward, all but its workspace: an rlk_status
+// (RLK_OK for N == 0, which launches nothing).
+int check_linear_logp_args(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
+                           const int64_t* targets, const float* logp, int64_t N, int64_t V,
+                           int64_t H);
+
 struct TokenLossArgs {
   const float* logp;
   const float* logp_old;

@@ -240,3 +240,27 @@ def test_linear_param_grads_from_logits_validation(lib):
     assert f(*args(z=ctypes.c_void_p(0x10008))) == UNSUPPORTED   # misaligned
     assert f(*args(gh=NUL, gw=NUL)) == INVALID
     assert f(*args(wsb=ws - 1)) == INVALID
+
+
+def test_linear_logp_noalloc_validation(lib):
+    """The allocation-free fused forward checks its arguments like
+    rlk_linear_logp and refuses, before touching any device, a problem whose
+    chunk partials exceed its fixed 32 MiB array."""
+    f = lib.rlk_linear_logp_noalloc
+
+    def args(**k):
+        return [k.get("h", A16), k.get("ldh", 4096), k.get("w", A16), k.get("ldw", 4096),
+                k.get("t", A16), NUL, k.get("n", 8192), k.get("v", 128256), k.get("H", 4096),
+                k.get("lp", A16), NUL, NUL]
+    assert f(*args(n=0)) == OK                              # N == 0: no-op
+    assert f(*args(t=NUL)) == INVALID
+    assert f(*args(lp=NUL)) == INVALID
+    assert f(*args(h=A2)) == UNSUPPORTED
+    assert f(*args(ldh=4100)) == UNSUPPORTED
+    # 501 chunk partials of 8 bytes + a target logit per row: 8363 rows fit in
+    # 32 MiB at V = 128256, 8364 do not; at V = 151936 (594 chunks) 7055 fit
+    assert lib.rlk_linear_logp_workspace_size(8363, 128256, 4096) <= 32 << 20
+    assert lib.rlk_linear_logp_workspace_size(8364, 128256, 4096) > 32 << 20
+    assert f(*args(n=8364)) == UNSUPPORTED
+    assert lib.rlk_linear_logp_workspace_size(7055, 151936, 4096) <= 32 << 20
+    assert f(*args(n=7056, v=151936)) == UNSUPPORTED
