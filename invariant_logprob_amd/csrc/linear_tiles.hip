@@ -287,7 +287,7 @@ void linear_tiles_fwd(TileArgs args) {
 #pragma unroll
       for (int i = 0; i < kI; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[i][j][e]);
+        for (int e = 0; e < 16; ++e) mx = vmax(mx, acc[i][j][e]);
       const float Mu = lse_raise(M, s, mx);
 #pragma unroll
       for (int i = 0; i < kI; ++i)
@@ -299,7 +299,7 @@ void linear_tiles_fwd(TileArgs args) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int m = wv * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-          if (m < cur.V_tail) mx = fmaxf(mx, acc[i][j][e]);
+          if (m < cur.V_tail) mx = vmax(mx, acc[i][j][e]);
         }
       const float Mu = lse_raise(M, s, mx);
 #pragma unroll
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(64 * kCombineRows) void lse_chunk_combine(
     const float2 p = rp[c];
     lse_merge(M, s, p.x, p.y);
   }
-  wave_lse_allreduce(M, s);
+  wave_lse_allreduce(M, s, lane);
   if (lane == 0) {
     const float l = lse_finish(M, s);
     const int64_t t = targets[row];

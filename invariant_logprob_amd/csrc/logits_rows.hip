@@ -1,12 +1,12 @@
 // Selected-token logprob from materialised bf16 logits, and its backward.
 //
-// Forward (one workgroup per row; a launch of more rows than the grid limit
-// loops, each workgroup taking rows blockIdx.x, + gridDim.x, ... with the
-// same per-row schedule).  The row is streamed once from HBM in
-// 16-byte vectors of 8 bf16.  Vector k of a row always goes to thread
-// k % kRowThreads and is visited in ascending k, so every lane's partial
-// (M, s) is a function of the row's values and of V alone.  Lanes merge in a
-// fixed wave64 butterfly, waves merge in ascending wave order through LDS.
+// Forward (one workgroup per row; more rows than one launch's grid limit
+// take further launches from the host, with the same per-row schedule).  The
+// row is streamed once from HBM in 16-byte vectors of 8 bf16.  Vector k of a
+// row always goes to thread k % kRowThreads and is visited in ascending k, so
+// every lane's partial (M, s) is a function of the row's values and of V
+// alone.  Lanes merge in a fixed wave64 butterfly over register lane
+// exchanges, waves merge in ascending wave order through LDS.
 // Nothing depends on N, on the row's index or on other rows: the batch
 // invariance of page "[RFC] Batch-Invariant RL Kernel Suite for
 // Train-Inference Consistency" (relation I) holds by construction, and there
@@ -46,9 +46,21 @@ __device__ __forceinline__ Vec8 decode(const uint4& w) {
   return r;
 }
 
-__device__ __forceinline__ float max8(const Vec8& a) {
-  return fmaxf(fmaxf(fmaxf(a.v[0], a.v[1]), fmaxf(a.v[2], a.v[3])),
-               fmaxf(fmaxf(a.v[4], a.v[5]), fmaxf(a.v[6], a.v[7])));
+// Maximum of a lane's block of 8 U values: two chains of three-input maxima
+// (the maximum is exact, so the grouping does not change the result).
+template <int U>
+__device__ __forceinline__ float block_max(const Vec8 (&x)[U]) {
+  float m0 = vmax(vmax(x[0].v[0], x[0].v[1]), x[0].v[2]);
+  float m1 = vmax(vmax(x[0].v[3], x[0].v[4]), x[0].v[5]);
+  m0 = vmax(vmax(m0, x[0].v[6]), x[0].v[7]);
+#pragma unroll
+  for (int u = 1; u < U; ++u) {
+    m1 = vmax(vmax(m1, x[u].v[0]), x[u].v[1]);
+    m0 = vmax(vmax(m0, x[u].v[2]), x[u].v[3]);
+    m1 = vmax(vmax(m1, x[u].v[4]), x[u].v[5]);
+    m0 = vmax(vmax(m0, x[u].v[6]), x[u].v[7]);
+  }
+  return vmax(m0, m1);
 }
 
 // Sum of the 8 terms in a fixed pairwise tree.
@@ -66,10 +78,7 @@ __device__ __forceinline__ float sum8_terms(const Vec8& a, float Mu) {
 template <int U>
 __device__ __forceinline__ void consume(float& M, float& s, const Vec8 (&x)[U]) {
 #pragma clang fp contract(off)
-  float bm = max8(x[0]);
-#pragma unroll
-  for (int u = 1; u < U; ++u) bm = fmaxf(bm, max8(x[u]));
-  const float Mu = lse_raise(M, s, bm);
+  const float Mu = lse_raise(M, s, block_max<U>(x));
 #pragma unroll
   for (int u = 0; u < U; ++u) s = s + sum8_terms(x[u], Mu);
 }
@@ -92,10 +101,7 @@ __device__ __forceinline__ float sum8_weighted(const Vec8& a, float Mu, float& t
 template <int U>
 __device__ __forceinline__ void consume3(float& M, float& s, float& t, const Vec8 (&x)[U]) {
 #pragma clang fp contract(off)
-  float bm = max8(x[0]);
-#pragma unroll
-  for (int u = 1; u < U; ++u) bm = fmaxf(bm, max8(x[u]));
-  const float Mu = lse3_raise(M, s, t, bm);
+  const float Mu = lse3_raise(M, s, t, block_max<U>(x));
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     float tw;
@@ -108,27 +114,29 @@ __device__ __forceinline__ void consume3(float& M, float& s, float& t, const Vec
 template <int THREADS, int UNROLL, bool kEntropy>
 __global__ __launch_bounds__(THREADS) void logp_fwd_rows(
     const uint16_t* __restrict__ logits, int64_t ld, const int64_t* __restrict__ targets,
-    const uint8_t* __restrict__ mask, int64_t N, int V, float* __restrict__ logp,
+    const uint8_t* __restrict__ mask, int64_t row0, int V, float* __restrict__ logp,
     float* __restrict__ lse, float* __restrict__ ent) {
   constexpr int kWaves = THREADS / 64;
+  const int64_t row = row0 + blockIdx.x;
   const int tid = threadIdx.x;
-  // wave partials of a row, double-buffered by iteration parity so that the
-  // next row's writes never race the final merge of this one
-  __shared__ float sM[2][kWaves];
-  __shared__ float sS[2][kWaves];
-  __shared__ float sT[2][kWaves];
-  int par = 0;
-  for (int64_t row = blockIdx.x; row < N; row += gridDim.x, par ^= 1) {
   if (mask != nullptr && mask[row] == 0) {
     if (tid == 0) {
       logp[row] = 0.0f;
       if (lse != nullptr) lse[row] = 0.0f;
       if constexpr (kEntropy) ent[row] = 0.0f;
     }
-    continue;
+    return;
   }
   const uint16_t* rowp = logits + row * ld;
   const uint4* vp = reinterpret_cast<const uint4*>(rowp);
+  // the target and its logit are loaded first, so that their latency hides
+  // behind the row's stream instead of adding to the row's end
+  int64_t t = -1;
+  float xt = 0.0f;
+  if (tid == 0) {
+    t = targets[row];
+    if (t >= 0 && t < V) xt = bf16_to_f32(rowp[t]);
+  }
   const int nfull = V >> 3;                 // vectors lying wholly inside [0, V)
   const int nvec = (V + 7) >> 3;
   constexpr int kStep = THREADS * UNROLL;
@@ -166,39 +174,35 @@ __global__ __launch_bounds__(THREADS) void logp_fwd_rows(
     else consume<UNROLL>(M, s, x);
   }
 
-  if constexpr (kEntropy) wave_lse3_allreduce(M, s, tw);
-  else wave_lse_allreduce(M, s);
+  if constexpr (kEntropy) wave_lse3_allreduce(M, s, tw, tid & 63);
+  else wave_lse_allreduce(M, s, tid & 63);
+  __shared__ float sM[kWaves];
+  __shared__ float sS[kWaves];
+  __shared__ float sT[kWaves];
   const int wave = tid >> 6;
   if ((tid & 63) == 0) {
-    sM[par][wave] = M;
-    sS[par][wave] = s;
-    if constexpr (kEntropy) sT[par][wave] = tw;
+    sM[wave] = M;
+    sS[wave] = s;
+    if constexpr (kEntropy) sT[wave] = tw;
   }
   __syncthreads();
   if (tid == 0) {
-    float Mt = sM[par][0];
-    float st = sS[par][0];
-    float tt = kEntropy ? sT[par][0] : 0.0f;
+    float Mt = sM[0];
+    float st = sS[0];
+    float tt = kEntropy ? sT[0] : 0.0f;
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) {
-      if constexpr (kEntropy) lse3_merge(Mt, st, tt, sM[par][w], sS[par][w], sT[par][w]);
-      else lse_merge(Mt, st, sM[par][w], sS[par][w]);
+      if constexpr (kEntropy) lse3_merge(Mt, st, tt, sM[w], sS[w], sT[w]);
+      else lse_merge(Mt, st, sM[w], sS[w]);
     }
     const float l = lse_finish(Mt, st);
     if constexpr (kEntropy) {
 #pragma clang fp contract(off)
       ent[row] = l - tt / st;
     }
-    const int64_t t = targets[row];
-    float lp;
-    if (t >= 0 && t < V) {
-      lp = bf16_to_f32(rowp[t]) - l;
-    } else {
-      lp = __builtin_nanf("");
-    }
+    const float lp = (t >= 0 && t < V) ? xt - l : __builtin_nanf("");
     logp[row] = lp;
     if (lse != nullptr) lse[row] = l;
-  }
   }
 }
 
@@ -407,13 +411,14 @@ __global__ __launch_bounds__(THREADS) void log_softmax_rows(
 // Compile-time schedule of the logits path.  These constants fix every row's
 // reduction order; they are part of the build identity.
 constexpr int kRowThreads = 256;
-constexpr int kRowUnroll = 8;
+constexpr int kRowUnroll = 4;
 constexpr int kBwdThreads = 128;
 constexpr int kBwdUnroll = 4;
 // Upper bound on the elementwise kernels' grid (a multiple of 8); larger
 // problems loop.
 constexpr int64_t kBwdMaxGrid = int64_t(1) << 22;
-// Upper bound on the forward's grid (rows per launch round); more rows loop.
+// Rows per launch of the forward; more rows take further launches (the
+// kernel stays a straight-line one-row program: no loop-carried state).
 constexpr int64_t kRowMaxGrid = int64_t(1) << 22;
 
 int logits_schedule_threads() { return kRowThreads; }
@@ -422,17 +427,21 @@ int logits_schedule_unroll() { return kRowUnroll; }
 hipError_t launch_logp_fwd_rows(const uint16_t* logits, int64_t ld, const int64_t* targets,
                                 const uint8_t* mask, int64_t N, int V, float* logp, float* lse,
                                 float* entropy, hipStream_t stream) {
-  const uint32_t grid = static_cast<uint32_t>(N < kRowMaxGrid ? N : kRowMaxGrid);
-  if (entropy == nullptr) {
-    hipLaunchKernelGGL((logp_fwd_rows<kRowThreads, kRowUnroll, false>), dim3(grid),
-                       dim3(kRowThreads), 0, stream, logits, ld, targets, mask, N, V, logp, lse,
-                       nullptr);
-  } else {
-    hipLaunchKernelGGL((logp_fwd_rows<kRowThreads, kRowUnroll, true>), dim3(grid),
-                       dim3(kRowThreads), 0, stream, logits, ld, targets, mask, N, V, logp, lse,
-                       entropy);
+  for (int64_t row0 = 0; row0 < N; row0 += kRowMaxGrid) {
+    const uint32_t grid = static_cast<uint32_t>(N - row0 < kRowMaxGrid ? N - row0 : kRowMaxGrid);
+    if (entropy == nullptr) {
+      hipLaunchKernelGGL((logp_fwd_rows<kRowThreads, kRowUnroll, false>), dim3(grid),
+                         dim3(kRowThreads), 0, stream, logits, ld, targets, mask, row0, V, logp,
+                         lse, nullptr);
+    } else {
+      hipLaunchKernelGGL((logp_fwd_rows<kRowThreads, kRowUnroll, true>), dim3(grid),
+                         dim3(kRowThreads), 0, stream, logits, ld, targets, mask, row0, V, logp,
+                         lse, entropy);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 static uint32_t elementwise_grid(int64_t total) {

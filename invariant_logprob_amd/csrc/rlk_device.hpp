@@ -33,6 +33,12 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// NaN-propagating maximum (IEEE 754-2019 maximum; v_maximum3_f32 on gfx950).
+// Unlike fmaxf it needs no quieting of its inputs first, which fmaxf costs
+// one instruction per value; a NaN logit still makes its row's result NaN
+// (through its own exponential term as well).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -122,16 +128,6 @@ __device__ __forceinline__ float lse3_raise(float& M, float& s, float& t, float 
   return lse_offset(M);
 }
 
-__device__ __forceinline__ void wave_lse3_allreduce(float& M, float& s, float& t) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const float M2 = __shfl_xor(M, d, 64);
-    const float s2 = __shfl_xor(s, d, 64);
-    const float t2 = __shfl_xor(t, d, 64);
-    lse3_merge(M, s, t, M2, s2, t2);
-  }
-}
-
 // Natural-log LSE of a finished state.
 __device__ __forceinline__ float lse_finish(float M, float s) {
 #pragma clang fp contract(off)
@@ -139,14 +135,54 @@ __device__ __forceinline__ float lse_finish(float M, float s) {
   return l2 * kLn2;
 }
 
-// Wave64 butterfly: every lane ends with the merge of all 64 lanes, in a
-// fixed pairing order (distance 32, 16, ..., 1).
-__device__ __forceinline__ void wave_lse_allreduce(float& M, float& s) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const float M2 = __shfl_xor(M, d, 64);
-    const float s2 = __shfl_xor(s, d, 64);
+// The value lane (lane ^ m) holds, for the six exchanges of the wave
+// reduction: m = 32 and 16 through the gfx950 half-swap instructions
+// (v_permlane32_swap / v_permlane16_swap, then a select of the half that
+// came from the partner), m = 8 within each 16-lane row (DPP row_ror:8), m = 7
+// within each 8-lane half row (DPP row_half_mirror), m = 2 and 1 within each
+// quad (DPP quad_perm).  No LDS traffic; all lanes take part.
+template <int K>
+__device__ __forceinline__ float wave_partner(float v, int lane) {
+  const uint32_t u = __float_as_uint(v);
+  if constexpr (K == 0) {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+  } else if constexpr (K == 1) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+  } else if constexpr (K == 2) {
+    return __uint_as_float(__builtin_amdgcn_mov_dpp(u, 0x128, 0xF, 0xF, false));
+  } else if constexpr (K == 3) {
+    return __uint_as_float(__builtin_amdgcn_mov_dpp(u, 0x141, 0xF, 0xF, false));
+  } else if constexpr (K == 4) {
+    return __uint_as_float(__builtin_amdgcn_mov_dpp(u, 0x4E, 0xF, 0xF, false));
+  } else {
+    return __uint_as_float(__builtin_amdgcn_mov_dpp(u, 0xB1, 0xF, 0xF, false));
+  }
+}
+
+// Wave64 butterfly over the lane exchanges above, in the fixed order
+// xor 32, 16, 8, 7, 2, 1 (these six masks span all 64 lanes): every lane ends
+// with the merge of all 64 lanes, and since the merge is symmetric bit for
+// bit, with the same bits.
+template <int K = 0>
+__device__ __forceinline__ void wave_lse_allreduce(float& M, float& s, int lane) {
+  if constexpr (K < 6) {
+    const float M2 = wave_partner<K>(M, lane);
+    const float s2 = wave_partner<K>(s, lane);
     lse_merge(M, s, M2, s2);
+    wave_lse_allreduce<K + 1>(M, s, lane);
+  }
+}
+
+template <int K = 0>
+__device__ __forceinline__ void wave_lse3_allreduce(float& M, float& s, float& t, int lane) {
+  if constexpr (K < 6) {
+    const float M2 = wave_partner<K>(M, lane);
+    const float s2 = wave_partner<K>(s, lane);
+    const float t2 = wave_partner<K>(t, lane);
+    lse3_merge(M, s, t, M2, s2, t2);
+    wave_lse3_allreduce<K + 1>(M, s, t, lane);
   }
 }
 
