@@ -16,8 +16,10 @@ One step is one pass of the whole hot path over resident synthetic inputs:
 The headline value is the selected-logprob throughput at V=151936: active
 tokens per second of the logits forward.  Each leg is timed with HIP events
 on the stream its kernels run on (torch's current stream), and every leg's
-rate is reported beside it.  The CPU baseline is the fp64 oracle on a bounded
-sample of the same logits workload.
+rate is reported beside it, with the attainable rates measured in the same
+run (a plain streaming read, a bf16 MFMA loop with the shader clock it
+sustains, torch's GEMM on the fused shapes).  The CPU baseline is the fp64
+oracle on the host's cores, on a bounded sample of every configuration.
 """
 
 import argparse
@@ -50,10 +52,9 @@ def parse():
     p.add_argument("--calibrate-copy", action="store_true",
                    help="instead of the hot path, run a plain 1 GiB device copy 5 times "
                         "(reference for hardware traffic counters)")
-    p.add_argument("--yardsticks", action="store_true",
-                   help="instead of the hot path, time attainable-rate yardsticks with torch "
-                        "kernels: a streaming read, a fill, and the bf16 GEMMs of the fused "
-                        "shapes (comparison only; nothing of the library runs)")
+    p.add_argument("--no-yardsticks", action="store_true",
+                   help="skip the attainable-rate yardsticks (a plain streaming read, a bf16 "
+                        "MFMA loop with its shader clock, torch's GEMM on the fused shapes)")
     return p.parse_args()
 
 
@@ -93,12 +94,37 @@ def _device_desc(torch, dev):
             f"{p.total_memory / 2**30:.0f} GiB)")
 
 
-def yardsticks(torch):
-    """Attainable rates of torch's own kernels on the step's shapes, as a
-    comparison for the library's roofline fractions (prints one JSON line)."""
-    dev = torch.device("cuda:0")
+def _hip_clock_mhz(dev_index):
+    """The device's peak shader clock (hipDeviceAttributeClockRate, kHz)."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, dev_index) == 0:
+            return v.value / 1000.0
+    except OSError:
+        pass
+    return None
 
-    def timed(fn, reps=10):
+
+def measure_yardsticks(torch, dev, read_buf):
+    """Attainable rates on this device, as yardsticks for the roofline
+    fractions (comparison only: nothing of the library runs here).
+      stream_read    a plain 16-byte nontemporal read of ``read_buf``
+                     (yardstick/yardstick.hip), GB/s;
+      mfma_loop      back-to-back bf16 MFMAs on registers, TFLOP/s, and the
+                     shader clock it sustains (s_memtime against the 100 MHz
+                     real-time counter), MHz;
+      gemm           torch's bf16 GEMM (hipBLASLt) on the two fused shapes,
+                     fp32 output where torch offers it, TFLOP/s."""
+    import ctypes
+
+    import numpy as np
+    out = {"clock_max_mhz": _hip_clock_mhz(dev.index or 0)}
+    stream = torch.cuda.current_stream(dev)
+    path = os.path.join(ROOT, "yardstick", "libyardstick.so")
+
+    def ev_ms(fn, reps):
         fn()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -110,34 +136,49 @@ def yardsticks(torch):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    out = {}
-    x = torch.ones((16384, 151936), dtype=torch.bfloat16, device=dev)
-    nbytes = x.numel() * 2
-    ms = timed(lambda: torch.amax(x, dim=1))
-    out["read_rowmax_bf16"] = {"ms": ms, "GB_per_s": nbytes / (ms * 1e-3) / 1e9}
-    y = torch.empty((16384, 151936), dtype=torch.float32, device=dev)
-    ms = timed(lambda: y.fill_(1.0))
-    out["fill_fp32"] = {"ms": ms, "GB_per_s": y.numel() * 4 / (ms * 1e-3) / 1e9}
-    ms = timed(lambda: y.copy_(x))
-    out["convert_bf16_to_fp32"] = {"ms": ms, "GB_per_s": (nbytes + y.numel() * 4) / (ms * 1e-3) / 1e9}
-    del x, y
+    if os.path.exists(path):
+        ys = ctypes.CDLL(path)
+        ys.yardstick_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                             ctypes.c_void_p, ctypes.c_void_p]
+        ys.yardstick_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        nbytes = read_buf.numel() * read_buf.element_size()
+        grid = cus * 16
+        sink = torch.zeros(grid, dtype=torch.int32, device=dev)
+        ms = ev_ms(lambda: ys.yardstick_stream_read(read_buf.data_ptr(), nbytes // 16, grid,
+                                                    sink.data_ptr(), stream.cuda_stream), 5)
+        out["stream_read"] = {"bytes": nbytes, "ms": ms, "GB_per_s": nbytes / (ms * 1e-3) / 1e9}
+        mgrid, iters = 2 * cus, 20000
+        clocks = torch.zeros(4 * mgrid, dtype=torch.int64, device=dev)
+        msink = torch.zeros(mgrid * 256, dtype=torch.float32, device=dev)
+        ms = ev_ms(lambda: ys.yardstick_mfma_loop(mgrid, iters, clocks.data_ptr(),
+                                                  msink.data_ptr(), stream.cuda_stream), 3)
+        c = clocks.view(mgrid, 4).cpu().numpy().astype(np.float64)
+        mhz = float(np.median((c[:, 1] - c[:, 0]) / np.maximum(c[:, 3] - c[:, 2], 1.0) * 100.0))
+        flops = mgrid * 4 * 4 * iters * 32768.0
+        out["mfma_loop"] = {"ms": ms, "TFLOP_per_s": flops / (ms * 1e-3) / 1e12,
+                            "clock_mhz": mhz}
+    else:
+        out["missing"] = "yardstick/libyardstick.so not built"
+    out["gemm"] = {}
     for n, v, h in ((8192, 128256, 4096), (2048, 151936, 5120)):
-        a = torch.randn((n, h), device=dev).to(torch.bfloat16)
-        w = torch.randn((v, h), device=dev).to(torch.bfloat16)
-        for odt in (torch.bfloat16, torch.float32):
-            if odt == torch.float32:
-                fn = lambda: torch.mm(a, w.t(), out_dtype=torch.float32)
-                try:
-                    fn()
-                except (TypeError, RuntimeError):
-                    continue
-            else:
-                fn = lambda: a @ w.t()
-            ms = timed(fn, 5)
-            out[f"gemm_{n}x{v}x{h}_{str(odt).split('.')[-1]}_out"] = {
-                "ms": ms, "TFLOP_per_s": 2.0 * n * v * h / (ms * 1e-3) / 1e12}
+        g = torch.Generator(device=dev).manual_seed(7)
+        a = torch.randn((n, h), generator=g, device=dev).to(torch.bfloat16)
+        w = torch.randn((v, h), generator=g, device=dev).to(torch.bfloat16)
+        try:
+            fn = lambda: torch.mm(a, w.t(), out_dtype=torch.float32)
+            fn()
+            odt = "fp32"
+        except (TypeError, RuntimeError):
+            fn = lambda: a @ w.t()
+            odt = "bf16"
+        ms = ev_ms(fn, 3)
+        out["gemm"][f"{n}x{v}x{h}"] = {"ms": ms, "out": odt,
+                                       "TFLOP_per_s": 2.0 * n * v * h / (ms * 1e-3) / 1e12}
         del a, w
-    print(json.dumps({"yardsticks": out, "torch": torch.__version__}))
+    torch.cuda.synchronize()
+    return out
 
 
 def calibrate_copy(torch):
@@ -163,9 +204,6 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(torch)
-        return
-    if args.yardsticks:
-        yardsticks(torch)
         return
 
     import invariant_logprob_amd as ilp
@@ -417,9 +455,38 @@ def main():
                            "GB_per_s_cold": gbs, "hbm_frac_cold": gbs / HBM_PEAK_GBS}
         del flush
 
+    ys = None if args.no_yardsticks else measure_yardsticks(torch, dev, c3.logits)
+    clock = None
+    if ys is not None:
+        clock = {"max_mhz": ys.get("clock_max_mhz"),
+                 "under_mfma_load_mhz": ys.get("mfma_loop", {}).get("clock_mhz")}
+        if roofline is not None and "stream_read" in ys and roofline["unit"] == "GB/s":
+            att = ys["stream_read"]["GB_per_s"]
+            roofline.update({"attainable": att, "attainable_kind": "plain streaming read",
+                             "frac_attainable": roofline["achieved"] / att})
+    fused_roof = None
+    if "fused_fwd" in out_legs:
+        tf = out_legs["fused_fwd"]["TFLOP_per_s"]
+        fused_roof = {"kernel": "linear_tiles_fwd", "bound": "mfma", "achieved": tf,
+                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
+                      "traffic": traffic.get("linear_tiles_fwd_8192x128256x4096"),
+                      "traffic_unit": "bytes per launch"}
+        if ys is not None:
+            mhz = ys.get("mfma_loop", {}).get("clock_mhz")
+            if mhz:
+                fused_roof["peak_at_measured_clock"] = BF16_PEAK_TFLOPS * mhz / 2400.0
+                fused_roof["frac_at_measured_clock"] = tf / fused_roof["peak_at_measured_clock"]
+            if "mfma_loop" in ys:
+                fused_roof["attainable_mfma_loop"] = ys["mfma_loop"]["TFLOP_per_s"]
+                fused_roof["frac_attainable_mfma_loop"] = tf / ys["mfma_loop"]["TFLOP_per_s"]
+            gemm = ys["gemm"].get("8192x128256x4096")
+            if gemm:
+                fused_roof["gemm_yardstick"] = gemm["TFLOP_per_s"]
+                fused_roof["frac_gemm_yardstick"] = tf / gemm["TFLOP_per_s"]
+
     cpu = None
     if not args.no_cpu_baseline and "logits_fwd" in legs:
-        cpu = cpu_baseline(c3, torch)
+        cpu = cpu_baseline(torch, dev, c3)
 
     for l in out_legs:
         out_legs[l].update(spread.get(l, {}))
@@ -449,13 +516,9 @@ def main():
         "legs": out_legs,
         "extra_legs": extra,
         "roofline": roofline,
-        "fused_roofline": ({"kernel": "linear_tiles_fwd", "bound": "mfma",
-                            "achieved": out_legs["fused_fwd"]["TFLOP_per_s"],
-                            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                            "frac": out_legs["fused_fwd"]["mfma_frac"],
-                            "traffic": traffic.get("linear_tiles_fwd_8192x128256x4096"),
-                            "traffic_unit": "bytes per launch"}
-                           if "fused_fwd" in out_legs else None),
+        "fused_roofline": fused_roof,
+        "clock": clock,
+        "yardsticks": ys,
         "cpu_baseline": cpu,
         "build": ilp.build_info(),
         "device": _device_desc(torch, dev),
@@ -464,31 +527,102 @@ def main():
     print(json.dumps(rec))
 
 
-def cpu_baseline(c3, torch, budget_s=15.0, block=256):
-    """The fp64 oracle, as it stands, on a bounded sample of the same logits
-    workload: consecutive 256-row blocks from the first row until about
-    ``budget_s`` seconds of CPU work; tokens/s over the sample's active rows."""
+def _host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def cpu_baseline(torch, dev, c3):
+    """The fp64 oracle, as it stands, timed on the host's cores, one entry per
+    configuration on a bounded sample of its workload (about 10-20 s of CPU
+    work in all).  Row-wise oracle functions run over row blocks in a thread
+    pool with one thread per CPU this process may use (rows are independent);
+    the fused ones are called once on their sample, their fp64 products
+    running on the BLAS library's threads (one per CPU).  Rates count the
+    sample's active tokens, its algorithmic bytes (as the GPU legs count them)
+    and, for the fused configurations, 2 N V H flops per projection."""
     import numpy as np
 
     import oracle
-    n = c3.logits.shape[0]
-    done_rows = 0
-    active = 0
-    spent = 0.0
-    while done_rows < n and spent < budget_s:
-        r1 = min(n, done_rows + block)
-        bits = c3.logits[done_rows:r1].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
-        t = c3.targets[done_rows:r1].cpu().numpy()
-        m = c3.mask[done_rows:r1].cpu().numpy()
+    from oracle.parallel import host_threads, map_row_blocks
+    from invariant_logprob_amd import workloads as wl
+
+    threads = host_threads()
+
+    def bits(t):
+        return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    def timed(fn):
         t0 = time.perf_counter()
-        oracle.logp_selected(bits, t, m)
-        spent += time.perf_counter() - t0
-        active += int(m.astype(bool).sum())
-        done_rows = r1
-    return {"value": active / spent, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {done_rows} rows ({active} active) of the N=16384 V=151936 logits "
-                      f"workload, {spent:.1f} s of oracle time (numpy float64, one thread)",
-            "host_cpus": os.cpu_count(), "host": platform.processor() or platform.machine()}
+        fn()
+        return time.perf_counter() - t0
+
+    def pool(fn, n):
+        return map_row_blocks(fn, n, block_rows=64, workers=threads)
+
+    per = {}
+    # N=8, V=1024: whole, repeated for a stable time
+    b1 = wl.logits_small(seed=0, device=dev)
+    x1, t1 = bits(b1.logits), b1.targets.cpu().numpy()
+    oracle.logp_selected(x1, t1)
+    reps = 200
+    s = timed(lambda: [oracle.logp_selected(x1, t1) for _ in range(reps)]) / reps
+    per["logits_small"] = {"sample": "all 8 rows (x200)", "s": s, "tokens_per_s": 8 / s,
+                           "GB_per_s": 8 * 1024 * 2 / s / 1e9}
+    # packed varlen batch, V=32000: every row
+    b2 = wl.logits_varlen(seed=0, device=dev)
+    x2, t2, m2 = bits(b2.logits), b2.targets.cpu().numpy(), b2.mask.cpu().numpy()
+    n2 = x2.shape[0]
+    a2 = int(m2.astype(bool).sum())
+    pool(lambda r0, r1: oracle.logp_selected(x2[r0:r0 + 1], t2[r0:r0 + 1], m2[r0:r0 + 1]), 64)
+    s = timed(lambda: pool(lambda r0, r1: oracle.logp_selected(x2[r0:r1], t2[r0:r1], m2[r0:r1]), n2))
+    per["logits_varlen"] = {"sample": f"all {n2} rows ({a2} active)", "s": s,
+                            "tokens_per_s": a2 / s, "GB_per_s": a2 * 32000 * 2 / s / 1e9}
+    del x2
+    # N=16384, V=151936: every row forward; the backward on 512 active rows
+    x3, t3, m3 = bits(c3.logits), c3.targets.cpu().numpy(), c3.mask.cpu().numpy()
+    n3, v3 = x3.shape
+    a3 = int(m3.astype(bool).sum())
+    s = timed(lambda: pool(lambda r0, r1: oracle.logp_selected(x3[r0:r1], t3[r0:r1], m3[r0:r1]), n3))
+    per["logits_fwd"] = {"sample": f"all {n3} rows ({a3} active)", "s": s, "tokens_per_s": a3 / s,
+                         "GB_per_s": a3 * v3 * 2 / s / 1e9}
+    rows = np.nonzero(m3)[0][:512]
+    xb, tb, gb = x3[rows], t3[rows], c3.grad.cpu().numpy()[rows]
+    s = timed(lambda: pool(lambda r0, r1: oracle.logp_backward(xb[r0:r1], tb[r0:r1], None, None,
+                                                               gb[r0:r1]), rows.size))
+    per["logits_bwd"] = {"sample": "512 active rows (their own lse)", "s": s,
+                         "tokens_per_s": rows.size / s,
+                         "GB_per_s": rows.size * v3 * (2 + 4) / s / 1e9}
+    del x3, xb
+    # fused configurations: a 256-row forward and a 64-row backward sample
+    for name, gen, nf, nb in (("fused_fwd", wl.fused_large, 256, 0),
+                              ("fused_fb", wl.fused_bwd, 256, 64)):
+        c = gen(seed=0, device=dev)
+        hb, wb = bits(c.hidden[:nf]), bits(c.weight)
+        t = c.targets[:nf].cpu().numpy()
+        v, h = wb.shape
+        s = timed(lambda: oracle.linear_logp(hb, wb, t))
+        per[name] = {"sample": f"{nf} rows forward (the fp64 weight decoded in the call)", "s": s,
+                     "tokens_per_s": nf / s, "GFLOP_per_s": 2.0 * nf * v * h / s / 1e9}
+        if nb:
+            g = c.grad[:nb].cpu().numpy()
+            s = timed(lambda: oracle.linear_logp_backward(hb[:nb], wb, t[:nb], None, None, g))
+            per[name + "_bwd"] = {"sample": f"{nb} rows backward (their own lse)", "s": s,
+                                  "tokens_per_s": nb / s, "GFLOP_per_s": 2 * 2.0 * nb * v * h / s / 1e9}
+        del c, hb, wb
+    head = per["logits_fwd"]
+    return {"value": head["tokens_per_s"], "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"selected logprob from bf16 logits N=16384 V=151936: {head['sample']}, "
+                      f"{head['s']:.2f} s of numpy float64 oracle time on {threads} threads",
+            "host_cpus": os.cpu_count(), "host_cpu_model": _host_cpu_model(),
+            "blas_threads": os.environ.get("OMP_NUM_THREADS", "library default"),
+            "per_config": per}
 
 
 if __name__ == "__main__":

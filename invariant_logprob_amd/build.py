@@ -71,5 +71,19 @@ def build(verbose=False):
     return LIB
 
 
+YARDSTICK_SRC = os.path.join(ROOT, "yardstick", "yardstick.hip")
+YARDSTICK_LIB = os.path.join(ROOT, "yardstick", "libyardstick.so")
+
+
+def build_yardstick():
+    """The benchmark's measurement kernels (attainable read and matrix rates,
+    shader clock): a library of their own, never linked into librlk.so."""
+    tmp = YARDSTICK_LIB + ".tmp"
+    _run([HIPCC, *COMMON, "-shared", YARDSTICK_SRC, "-o", tmp])
+    os.replace(tmp, YARDSTICK_LIB)
+    return YARDSTICK_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_yardstick())
