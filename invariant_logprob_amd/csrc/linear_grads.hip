@@ -151,59 +151,59 @@ void grad_dl_tiles(DlArgs a) {
     off[j] = active ? a.lse[tok] * kLog2e : 0.0f;
     pz[j] = (active && !tvalid) ? __builtin_nanf("") : 0.0f;
   }
-  // bf16 part `lo` of D for vocabulary rows m0 .. m0 + 3 (m0 = 128 wv +
-  // 32 i + 8 q + 4 (lane >> 5)) of token column j, two entries per word.
-  // Evaluated once per staging pass rather than held: the accumulators stay
-  // the only large live state.  No branches: p is always evaluated; a masked
-  // row or a column past V selects +0 whatever its logits hold, an active row
-  // with an invalid target carries NaN in the additive term, and NaN or
-  // infinite logits of an active row reach D unclamped.
+  // D of every accumulator entry is formed once and split into its two bf16
+  // parts, both staged in LDS, one 32-token column block j of every wave at a
+  // time (128 tokens x 256 vocabulary rows x 2 parts), then stored as whole
+  // 512-byte token rows of D_hi and D_lo.  No branches: p is always
+  // evaluated; a masked row or a column past V gets +0 whatever its logits
+  // hold, an active row with an invalid target carries NaN in the additive
+  // term, and NaN or infinite logits of an active row reach D unclamped.
   // kFull: the tile's 256 vocabulary rows are all < V (every tile but a
   // ragged last one), so no row test is needed -- a uniform branch picks it.
   auto epilogue = [&](auto full) {
   constexpr bool kFull = decltype(full)::value;
-  auto dpair = [&](int j, int i, int q, bool lo) {
-    const int m0 = wv * 128 + i * 32 + 8 * q + 4 * half;
-    uint32_t b[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p = fast_exp2(__builtin_fmaf(acc[i][j][4 * q + e], kLog2e, -off[j]));
-      const float add = (i * 32 + 8 * q + e == rel[j]) ? gg[j] : 0.0f;
-      const bool keep = act[j] && (kFull || m0 + e < V_tail);
-      b[e] = bf16_part(keep ? __builtin_fmaf(ng[j], p, add + pz[j]) : 0.0f, lo);
-    }
-    return make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
-  };
-
   uint16_t* S = reinterpret_cast<uint16_t*>(smem);
-  // 16-byte pieces of a staged 256 x 256 tile: 32 per row, 16 per thread
-  constexpr int kPieces = kBQ * (kBP / 8) / kThreads;
-
-  // S[token][vocab], then whole 512-byte token rows of D_c: D_hi, then D_lo
-#pragma nounroll
-  for (int part = 0; part < 2; ++part) {
-    const bool lo = part != 0;
-    uint16_t* dst = lo ? a.d_lo : a.d;
+  constexpr int kHalfRows = kWQ * 32;                        // staged tokens per block j
+  constexpr int kPieces = 2 * kHalfRows * (kBP / 8) / kThreads;  // 16-byte pieces per thread
 #pragma unroll
-    for (int j = 0; j < kJ; ++j) {
-      const int tl = wt * kQW + j * 32 + (lane & 31);
+  for (int j = 0; j < kJ; ++j) {
+    const int sr = wt * 32 + (lane & 31);  // staged row of this lane's token
 #pragma unroll
-      for (int i = 0; i < kI; ++i)
+    for (int i = 0; i < kI; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int m0 = wv * 128 + i * 32 + 8 * q + 4 * half;
-          *reinterpret_cast<uint2*>(S + tl * kDlStride + m0) = dpair(j, i, q, lo);
+      for (int q = 0; q < 4; ++q) {
+        uint32_t hb[4], lb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int mrel = i * 32 + 8 * q + e;  // + 128 wv + 4 half
+          const float p = fast_exp2(__builtin_fmaf(acc[i][j][4 * q + e], kLog2e, -off[j]));
+          const float add = (mrel == rel[j]) ? gg[j] : 0.0f;
+          const bool keep = act[j] && (kFull || wv * 128 + mrel + 4 * half < V_tail);
+          // +0 for a dropped entry as a bit mask, not a select: a select lets
+          // the compiler move the exponential under a branch per entry
+          const float dv = __uint_as_float(
+              __float_as_uint(__builtin_fmaf(ng[j], p, add + pz[j])) & (keep ? 0xffffffffu : 0u));
+          hb[e] = bf16_part(dv, false);
+          lb[e] = bf16_part(dv, true);
         }
-    }
+        const int m0 = wv * 128 + i * 32 + 8 * q + 4 * half;
+        *reinterpret_cast<uint2*>(S + sr * kDlStride + m0) =
+            make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+        *reinterpret_cast<uint2*>(S + (kHalfRows + sr) * kDlStride + m0) =
+            make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+      }
     __syncthreads();
 #pragma unroll 4
     for (int it = 0; it < kPieces; ++it) {
       const int idx = it * kThreads + tid;
-      const int r = idx >> 5;
+      const int srow = idx >> 5;             // staged row: part * 128 + row
       const int c = idx & 31;
-      if (r < N_tail) {
-        const uint4 v = *reinterpret_cast<const uint4*>(S + r * kDlStride + 8 * c);
-        *reinterpret_cast<uint4*>(dst + (tok0 + r) * a.ldd + vtl * kBP + 8 * c) = v;
+      const int r = srow & (kHalfRows - 1);
+      const int tl = (r >> 5) * kQW + j * 32 + (r & 31);  // token within the tile
+      if (tl < N_tail) {
+        uint16_t* dst = (srow >= kHalfRows) ? a.d_lo : a.d;
+        const uint4 v = *reinterpret_cast<const uint4*>(S + srow * kDlStride + 8 * c);
+        *reinterpret_cast<uint4*>(dst + (tok0 + tl) * a.ldd + vtl * kBP + 8 * c) = v;
       }
     }
     __syncthreads();

@@ -1,7 +1,9 @@
 """No atomic instruction anywhere in the library's gfx950 code: every
 reduction must have a fixed order (page "[WS1 Test] #154 dtype pin + ...",
 section "Workstream 3 - #153", scope item 2: no atomicAdd).  Scans the AMD
-assembly of this repository's own sources (CPU only; hipcc cross-compiles)."""
+assembly of this repository's own sources (CPU only; hipcc cross-compiles).
+The same scan checks that no kernel spills registers to scratch memory: a
+spilling tile epilogue once cost the gradient path an eighth of its time."""
 import os
 import re
 import subprocess
@@ -30,3 +32,13 @@ def test_device_code_has_no_atomics(src, tmp_path):
         assert ".amdhsa_kernel" in asm
     if src == "noalloc.hip":
         assert "scratch" in asm
+    # kernel descriptors: no VGPR spills, no per-lane scratch
+    meta = asm[asm.index("amdhsa.kernels:"):] if "amdhsa.kernels:" in asm else ""
+    for blk in re.split(r"\n  - ", meta)[1:]:
+        name = re.search(r"\.name:\s+(\S+)", blk)
+        if name is None:
+            continue
+        spill = re.search(r"\.vgpr_spill_count:\s+(\d+)", blk)
+        priv = re.search(r"\.private_segment_fixed_size:\s+(\d+)", blk)
+        assert spill is not None and int(spill.group(1)) == 0, (name.group(1), spill)
+        assert priv is not None and int(priv.group(1)) == 0, (name.group(1), priv)
