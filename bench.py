@@ -342,6 +342,7 @@ def main():
         xfns["log_softmax"] = (lambda: ilp.log_softmax(c3.logits, lse3, c3.mask, out=d3),
                                act3 * v3 * 2 + n3 * v3 * 4 + n3 * 5)
     xflops = {}
+    xexec = {}  # MFMA flops executed, where they differ from the algorithmic count
     if c5 is not None and "fused_param_grads" in args.extra_legs.split(","):
         # parameter gradients of the fused path on the fwd+bwd workload: the
         # logits recompute plus the two products, 3 x 2 N V H flops
@@ -355,6 +356,8 @@ def main():
                                                 workspace=wsg5),
             n5 * h5 * 2 + v5 * h5 * 2 + n5 * h5 * 4 + v5 * h5 * 4)
         xflops["fused_param_grads"] = 3 * 2.0 * n5 * v5 * h5
+        # the MFMAs run each product twice, over D's bf16 parts D_hi and D_lo
+        xexec["fused_param_grads"] = 5 * 2.0 * n5 * v5 * h5
         if "fused_param_grads_kept_logits" in args.extra_legs.split(","):
             # the same gradients from logits the forward kept (computed once,
             # outside the timing): the two products only, 2 x 2 N V H flops
@@ -367,6 +370,7 @@ def main():
                                                     grad_weight=gw5, workspace=wsg5, logits=zk5),
                 n5 * h5 * 2 + v5 * h5 * 2 + n5 * v5 * 4 + n5 * h5 * 4 + v5 * h5 * 4)
             xflops["fused_param_grads_kept_logits"] = 2 * 2.0 * n5 * v5 * h5
+            xexec["fused_param_grads_kept_logits"] = 4 * 2.0 * n5 * v5 * h5
     if c5 is not None and "fused_fb_kept_logits" in args.extra_legs.split(","):
         # the fwd+bwd workload with the forward keeping its fp32 logits and the
         # backward computed from them in place (one projection, 2 N V H flops)
@@ -404,6 +408,10 @@ def main():
             tf = xflops[name] / (xms * 1e-3) / 1e12
             extra[name] = {"ms": xms, "flops": xflops[name], "TFLOP_per_s": tf,
                            "mfma_frac": tf / BF16_PEAK_TFLOPS}
+            if name in xexec:
+                te = xexec[name] / (xms * 1e-3) / 1e12
+                extra[name].update({"executed_flops": xexec[name], "executed_TFLOP_per_s": te,
+                                    "executed_mfma_frac": te / BF16_PEAK_TFLOPS})
         else:
             extra[name] = {"ms": xms, "algorithmic_bytes": nbytes, "GB_per_s": xgbs,
                            "hbm_frac": xgbs / HBM_PEAK_GBS}
