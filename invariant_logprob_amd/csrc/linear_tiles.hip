@@ -78,6 +78,67 @@ struct TileArgs {
   int64_t ldg;
 };
 
+// Forward epilogue of token column j of a wave's block column: the (M, s)
+// partial of the column's logits over the wave's 128 vocabulary rows -- the
+// lane's maximum, then its sum of exponentials in (i, e) order, then the two
+// lane halves merged -- and, where the column's target falls in these rows,
+// the target's fp32 logit written to zt[tok].  A full vocabulary tile (the
+// common case, a uniform branch) needs no row test; a ragged last tile skips
+// its rows past V.  Every forward kernel forms its partials here, so a
+// token's partial does not depend on which of them computed its tile.
+template <int j, int NJ>
+__device__ __forceinline__ float2 column_partial(const f32x16_t (&acc)[kI][NJ], int wv,
+                                                 int half, int V_tail, bool have, int64_t t,
+                                                 int vwave, float* zt, int64_t tok) {
+  float mx = neg_inf();
+  float M = neg_inf();
+  float s = 0.0f;
+  if (V_tail >= kBV) {
+#pragma unroll
+    for (int i = 0; i < kI; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = vmax(mx, acc[i][j][e]);
+    const float Mu = lse_raise(M, s, mx);
+#pragma unroll
+    for (int i = 0; i < kI; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s = s + lse_term(acc[i][j][e], Mu);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kI; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = wv * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+        if (m < V_tail) mx = vmax(mx, acc[i][j][e]);
+      }
+    const float Mu = lse_raise(M, s, mx);
+#pragma unroll
+    for (int i = 0; i < kI; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = wv * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+        if (m < V_tail) s = s + lse_term(acc[i][j][e], Mu);
+      }
+  }
+  if (have) {
+    const int64_t d = t - vwave;
+    if (d >= 0 && d < 128) {
+      const int dd = static_cast<int>(d);
+      const int rem = dd & 31;
+      if (((rem >> 2) & 1) == half) {
+        // vocabulary row dd of this wave = block dd >> 5, element
+        // 4 ((dd & 31) >> 3) + (dd & 3)
+        const int idx = 16 * (dd >> 5) + (((rem >> 3) << 2) | (rem & 3));
+        zt[tok] = select_acc(acc, j, idx);
+      }
+    }
+  }
+  const float M2 = __shfl_xor(M, 32, 64);
+  const float s2 = __shfl_xor(s, 32, 64);
+  lse_merge(M, s, M2, s2);
+  return make_float2(M, s);
+}
+
 // blockIdx -> (vocabulary tile, token block): XCD-contiguous ranges, then
 // groups of kLinearVocabGroup vocabulary tiles x all token blocks.
 __device__ __forceinline__ void tile_coords(int w, int n_vtiles, int n_tblocks, int& vt, int& tb) {
@@ -273,61 +334,20 @@ void linear_tiles_fwd(TileArgs args) {
       __syncthreads();
     }
   }
-#pragma unroll
-  for (int j = 0; j < kJ; ++j) {
-    const int tl = wt * kQW + j * 32 + (lane & 31);
-    const int64_t tok = cur.tok0 + tl;
-    // Row maximum, then the sum of exponentials in (i, e) order.  A full
-    // vocabulary tile (the common case, a uniform branch) needs no column
-    // test; a ragged last tile skips its columns past V.
-    float mx = neg_inf();
-    float M = neg_inf();
-    float s = 0.0f;
-    if (cur.V_tail >= kBV) {
-#pragma unroll
-      for (int i = 0; i < kI; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = vmax(mx, acc[i][j][e]);
-      const float Mu = lse_raise(M, s, mx);
-#pragma unroll
-      for (int i = 0; i < kI; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s = s + lse_term(acc[i][j][e], Mu);
-    } else {
-#pragma unroll
-      for (int i = 0; i < kI; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = wv * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-          if (m < cur.V_tail) mx = vmax(mx, acc[i][j][e]);
-        }
-      const float Mu = lse_raise(M, s, mx);
-#pragma unroll
-      for (int i = 0; i < kI; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = wv * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-          if (m < cur.V_tail) s = s + lse_term(acc[i][j][e], Mu);
-        }
-    }
-    if (tl < cur.N_tail) {
-      const int64_t t = tgt[j];
-      const int64_t d = t - vwave;
-      if (d >= 0 && d < 128) {
-        const int dd = static_cast<int>(d);
-        const int rem = dd & 31;
-        if (((rem >> 2) & 1) == half) {
-          // vocabulary row dd of this wave = block dd >> 5, element
-          // 4 ((dd & 31) >> 3) + (dd & 3)
-          const int idx = 16 * (dd >> 5) + (((rem >> 3) << 2) | (rem & 3));
-          args.zt[tok] = select_acc(acc, j, idx);
-        }
-      }
-    }
-    const float M2 = __shfl_xor(M, 32, 64);
-    const float s2 = __shfl_xor(s, 32, 64);
-    lse_merge(M, s, M2, s2);
-    if (half == 0) red[wv * kBT + tl] = make_float2(M, s);
+  // the column index is a template argument: with a run-time index the
+  // accumulators would be addressed as an array in scratch memory
+  static_assert(kJ == 2, "two token block columns per wave");
+  {
+    const int tl = wt * kQW + (lane & 31);
+    const float2 ms = column_partial<0>(acc, wv, half, cur.V_tail, tl < cur.N_tail, tgt[0], vwave,
+                                        args.zt, cur.tok0 + tl);
+    if (half == 0) red[wv * kBT + tl] = ms;
+  }
+  {
+    const int tl = wt * kQW + 32 + (lane & 31);
+    const float2 ms = column_partial<1>(acc, wv, half, cur.V_tail, tl < cur.N_tail, tgt[1], vwave,
+                                        args.zt, cur.tok0 + tl);
+    if (half == 0) red[wv * kBT + tl] = ms;
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   if (tid < kBT) {
@@ -336,6 +356,132 @@ void linear_tiles_fwd(TileArgs args) {
     const float2 p1 = red[kBT + tl];
     lse_merge(p0.x, p0.y, p1.x, p1.y);
     if (tl < cur.N_tail) args.part[(cur.tok0 + tl) * args.n_vtiles + cur.vt] = p0;
+  }
+}
+
+// Forward for a batch of at most 32 token rows: all of them lie in the
+// first 32-token block column of a tile, so of the tile's MFMA work only the
+// blocks (i, j = 0) of the two waves with token quarter 0 matter, and the
+// tile is bound by streaming its 256 W rows.  This kernel runs exactly those
+// blocks -- the same fragments, the same v_mfma_f32_32x32x16_bf16 sequence
+// in the same K order, hence the same fp32 logits -- and the same column
+// epilogue and wave merge (column_partial, then vocabulary half 0 before
+// half 1), so every row's partials, z_t, logp and lse are bit-identical to
+// those of linear_tiles_fwd<false>.  What differs is only how W reaches the
+// LDS: through registers (16-byte loads, eight lanes per 128-byte row
+// segment, the next stage's loads in flight while this stage is consumed)
+// instead of direct-to-LDS copies, which stream this pattern about a sixth
+// slower; and a stage holds only 32 hidden rows, so a workgroup needs 72 KB
+// and two fit on a compute unit.  Two waves, one per vocabulary half, one
+// workgroup per 256-entry vocabulary tile.
+constexpr int kSmallRows = 32;
+constexpr int kSmallWaves = 2;
+constexpr int kSmallThreads = 64 * kSmallWaves;
+constexpr int kSmallWVec = kBV * kRowChunks;           // uint4 of W per stage (32 KB)
+constexpr int kSmallHVec = kSmallRows * kRowChunks;    // uint4 of hidden per stage (4 KB)
+constexpr int kSmallStageVec = kSmallWVec + kSmallHVec;
+constexpr int kSmallWLoads = kSmallWVec / 64 / kSmallWaves;  // 16-byte loads per lane per stage
+constexpr int kSmallHLoads = kSmallHVec / 64 / kSmallWaves;
+static_assert(kSmallWLoads == 16 && kSmallHLoads == 2, "18 loads per lane and stage");
+static_assert(2 * kSmallStageVec * 16 * 2 <= 160 * 1024, "two workgroups per compute unit");
+
+// One operand's part of a stage for this lane: chunk idx = (wave * n + q) *
+// 64 + lane of the stage, row idx / 8, logical chunk idx % 8; rows at or
+// past `rows` and chunks at or past K read as zero.  W is read once
+// (streaming hint); the hidden rows are read by every tile (cached).
+template <bool kStream, int NL>
+__device__ __forceinline__ void small_load(uint4 (&v)[NL], const uint16_t* base, int64_t ld,
+                                           int rows, int wave, int lane, int k0, int K) {
+#pragma unroll
+  for (int q = 0; q < NL; ++q) {
+    const int idx = (wave * NL + q) * 64 + lane;
+    const int r = idx / kRowChunks;
+    const int c = idx % kRowChunks;
+    v[q] = make_uint4(0u, 0u, 0u, 0u);
+    if (r < rows && k0 + 8 * c < K) {
+      const uint16_t* p = base + r * ld + k0 + 8 * c;
+      v[q] = kStream ? load16_stream(p) : *reinterpret_cast<const uint4*>(p);
+    }
+  }
+}
+
+// ... written to the stage's LDS rows at the tile layout's swizzled chunk.
+template <int NL>
+__device__ __forceinline__ void small_store(uint4* dst, const uint4 (&v)[NL], int wave, int lane) {
+#pragma unroll
+  for (int q = 0; q < NL; ++q) {
+    const int idx = (wave * NL + q) * 64 + lane;
+    const int r = idx / kRowChunks;
+    dst[r * kRowChunks + swz(r, idx % kRowChunks)] = v[q];
+  }
+}
+
+__global__ __launch_bounds__(kSmallThreads) void linear_tiles_fwd_small(TileArgs args) {
+  __shared__ uint4 smem[2 * kSmallStageVec];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;  // vocabulary half of the tile
+  const int vt = blockIdx.x;
+  const int vocab0 = vt * kBV;
+  const int V_tail = min(args.V - vocab0, kBV);
+  const int N = static_cast<int>(args.N);  // at most kSmallRows
+  const int tl = lane & 31;                 // this lane's token column
+  const int64_t tgt = (tl < N) ? args.targets[tl] : -1;
+  const uint16_t* wbase = args.weight + static_cast<int64_t>(vocab0) * args.ldw;
+
+  f32x16_t acc[kI][1];
+#pragma unroll
+  for (int i = 0; i < kI; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][0][e] = 0.0f;
+  const int K = args.H;
+  const int n_kt = (K + kBK - 1) / kBK;
+  uint4 wr[kSmallWLoads], hr[kSmallHLoads];
+  small_load<true>(wr, wbase, args.ldw, V_tail, wv, lane, 0, K);
+  small_load<false>(hr, args.hidden, args.ldh, N, wv, lane, 0, K);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    // Stage kt goes from the registers to LDS buffer kt & 1 (its last
+    // readers, stage kt - 2, finished before the previous barrier), the
+    // loads of stage kt + 1 take the registers' place, and the barrier makes
+    // the stage visible to both waves.
+    uint4* a = smem + (kt & 1) * kSmallStageVec;
+    small_store(a, wr, wv, lane);
+    small_store(a + kSmallWVec, hr, wv, lane);
+    if (kt + 1 < n_kt) {
+      small_load<true>(wr, wbase, args.ldw, V_tail, wv, lane, (kt + 1) * kBK, K);
+      small_load<false>(hr, args.hidden, args.ldh, N, wv, lane, (kt + 1) * kBK, K);
+    }
+    __syncthreads();
+    const uint4* b = a + kSmallWVec;
+#pragma unroll
+    for (int kk = 0; kk < kSub; ++kk) {
+      const int c = 2 * kk + (lane >> 5);
+      bf16x8_t fa[kI];
+#pragma unroll
+      for (int i = 0; i < kI; ++i) {
+        const int r = wv * kPW + i * 32 + (lane & 31);
+        fa[i] = __builtin_bit_cast(bf16x8_t, a[r * kRowChunks + swz(r, c)]);
+      }
+      const int rq = lane & 31;
+      const bf16x8_t fb = __builtin_bit_cast(bf16x8_t, b[rq * kRowChunks + swz(rq, c)]);
+#pragma unroll
+      for (int i = 0; i < kI; ++i)
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb, acc[i][0], 0, 0, 0);
+    }
+  }
+  __syncthreads();
+
+  const int half = lane >> 5;
+  const float2 ms = column_partial<0>(acc, wv, half, V_tail, tl < N, tgt, vocab0 + wv * kPW,
+                                      args.zt, static_cast<int64_t>(tl));
+  float2* red = reinterpret_cast<float2*>(smem);
+  if (half == 0) red[wv * kSmallRows + tl] = ms;
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (tid < kSmallRows) {
+    float2 p0 = red[tid];
+    const float2 p1 = red[kSmallRows + tid];
+    lse_merge(p0.x, p0.y, p1.x, p1.y);
+    if (tid < N) args.part[static_cast<int64_t>(tid) * args.n_vtiles + vt] = p0;
   }
 }
 
@@ -431,6 +577,9 @@ hipError_t launch_linear_logp(const uint16_t* hidden, int64_t ldh, const uint16_
   const uint32_t tiles = static_cast<uint32_t>(static_cast<int64_t>(a.n_vtiles) * a.n_tblocks);
   if (logits != nullptr)
     hipLaunchKernelGGL(linear_tiles_fwd<true>, dim3(tiles), dim3(kThreads), 0, stream, a);
+  else if (N <= kSmallRows)
+    hipLaunchKernelGGL(linear_tiles_fwd_small, dim3(static_cast<uint32_t>(a.n_vtiles)),
+                       dim3(kSmallThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(linear_tiles_fwd<false>, dim3(tiles), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();

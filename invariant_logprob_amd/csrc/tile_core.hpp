@@ -415,19 +415,28 @@ __device__ __forceinline__ void mainloop_g(uint4* smem, const LoaderG<LP, LQ>& L
 
 // Element idx = 16 i + e of column block j of the accumulators, for a
 // per-lane idx in [0, 64): a six-level select tree on the bits of idx, so
-// that each level shares one lane mask.
-__device__ __forceinline__ float select_acc(const f32x16_t (&acc)[kI][kJ], int j, int idx) {
+// that each level shares one lane mask.  Each bit passes through an empty
+// asm statement: seen as the bits of one index, the tree can be folded back
+// into an indexed read, which puts the accumulators in scratch memory.
+template <int NJ>
+__device__ __forceinline__ float select_acc(const f32x16_t (&acc)[kI][NJ], int j, int idx) {
   static_assert(kI * 16 == 64, "select tree is sized for 64 elements per column block");
+  int bit[6];
+#pragma unroll
+  for (int lvl = 0; lvl < 6; ++lvl) {
+    bit[lvl] = (idx >> lvl) & 1;
+    asm volatile("" : "+v"(bit[lvl]));
+  }
   float v[32];
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
     const int a = 2 * k, b = 2 * k + 1;
-    v[k] = (idx & 1) ? acc[b >> 4][j][b & 15] : acc[a >> 4][j][a & 15];
+    v[k] = bit[0] ? acc[b >> 4][j][b & 15] : acc[a >> 4][j][a & 15];
   }
 #pragma unroll
   for (int lvl = 1, n = 16; lvl < 6; ++lvl, n >>= 1)
 #pragma unroll
-    for (int k = 0; k < n; ++k) v[k] = ((idx >> lvl) & 1) ? v[2 * k + 1] : v[2 * k];
+    for (int k = 0; k < n; ++k) v[k] = bit[lvl] ? v[2 * k + 1] : v[2 * k];
   return v[0];
 }
 
