@@ -359,31 +359,36 @@ void linear_tiles_fwd(TileArgs args) {
   }
 }
 
-// Forward for a batch of at most 32 token rows: all of them lie in the
-// first 32-token block column of a tile, so of the tile's MFMA work only the
-// blocks (i, j = 0) of the two waves with token quarter 0 matter, and the
-// tile is bound by streaming its 256 W rows.  This kernel runs exactly those
-// blocks -- the same fragments, the same v_mfma_f32_32x32x16_bf16 sequence
-// in the same K order, hence the same fp32 logits -- and the same column
-// epilogue and wave merge (column_partial, then vocabulary half 0 before
-// half 1), so every row's partials, z_t, logp and lse are bit-identical to
-// those of linear_tiles_fwd<false>.  What differs is only how W reaches the
-// LDS: through registers (16-byte loads, eight lanes per 128-byte row
-// segment, the next stage's loads in flight while this stage is consumed)
-// instead of direct-to-LDS copies, which stream this pattern about a sixth
-// slower; and a stage holds only 32 hidden rows, so a workgroup needs 72 KB
-// and two fit on a compute unit.  Two waves, one per vocabulary half, one
-// workgroup per 256-entry vocabulary tile.
-constexpr int kSmallRows = 32;
+// Forward for a batch of at most 64 token rows: all of them lie in token
+// quarter 0 of a tile (its first 32 or 64 rows, NJ = 1 or 2 block columns),
+// so of the tile's MFMA work only the blocks (i, j < NJ) of the two waves
+// with token quarter 0 matter, and the tile is bound by streaming its 256 W
+// rows.  This kernel runs exactly those blocks -- the same fragments, the
+// same v_mfma_f32_32x32x16_bf16 sequence in the same K order, hence the same
+// fp32 logits -- and the same column epilogue and wave merge
+// (column_partial, then vocabulary half 0 before half 1), so every row's
+// partials, z_t, logp and lse are bit-identical to those of
+// linear_tiles_fwd<false>.  What differs is only how W reaches the LDS:
+// through registers (16-byte loads, eight lanes per 128-byte row segment,
+// the next stage's loads in flight while this stage is consumed) instead of
+// direct-to-LDS copies, which stream this pattern about a sixth slower; and
+// a stage holds only the batch's 32 or 64 hidden rows, so a workgroup needs
+// 72 or 80 KB and two fit on a compute unit.  Two waves, one per vocabulary
+// half, one workgroup per 256-entry vocabulary tile.
 constexpr int kSmallWaves = 2;
 constexpr int kSmallThreads = 64 * kSmallWaves;
 constexpr int kSmallWVec = kBV * kRowChunks;           // uint4 of W per stage (32 KB)
-constexpr int kSmallHVec = kSmallRows * kRowChunks;    // uint4 of hidden per stage (4 KB)
-constexpr int kSmallStageVec = kSmallWVec + kSmallHVec;
 constexpr int kSmallWLoads = kSmallWVec / 64 / kSmallWaves;  // 16-byte loads per lane per stage
-constexpr int kSmallHLoads = kSmallHVec / 64 / kSmallWaves;
-static_assert(kSmallWLoads == 16 && kSmallHLoads == 2, "18 loads per lane and stage");
-static_assert(2 * kSmallStageVec * 16 * 2 <= 160 * 1024, "two workgroups per compute unit");
+static_assert(kSmallWLoads == 16, "16 W loads per lane and stage");
+
+template <int NJ>
+struct SmallGeo {
+  static constexpr int kRows = 32 * NJ;                         // token rows held
+  static constexpr int kHVec = kRows * kRowChunks;              // uint4 of hidden per stage
+  static constexpr int kStageVec = kSmallWVec + kHVec;
+  static constexpr int kHLoads = kHVec / 64 / kSmallWaves;
+  static_assert(2 * 2 * kStageVec * 16 <= 160 * 1024, "two workgroups per compute unit");
+};
 
 // One operand's part of a stage for this lane: chunk idx = (wave * n + q) *
 // 64 + lane of the stage, row idx / 8, logical chunk idx % 8; rows at or
@@ -416,27 +421,35 @@ __device__ __forceinline__ void small_store(uint4* dst, const uint4 (&v)[NL], in
   }
 }
 
+template <int NJ>
 __global__ __launch_bounds__(kSmallThreads) void linear_tiles_fwd_small(TileArgs args) {
-  __shared__ uint4 smem[2 * kSmallStageVec];
+  using G = SmallGeo<NJ>;
+  __shared__ uint4 smem[2 * G::kStageVec];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;  // vocabulary half of the tile
   const int vt = blockIdx.x;
   const int vocab0 = vt * kBV;
   const int V_tail = min(args.V - vocab0, kBV);
-  const int N = static_cast<int>(args.N);  // at most kSmallRows
-  const int tl = lane & 31;                 // this lane's token column
-  const int64_t tgt = (tl < N) ? args.targets[tl] : -1;
+  const int N = static_cast<int>(args.N);  // at most G::kRows
+  int64_t tgt[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int tl = j * 32 + (lane & 31);
+    tgt[j] = (tl < N) ? args.targets[tl] : -1;
+  }
   const uint16_t* wbase = args.weight + static_cast<int64_t>(vocab0) * args.ldw;
 
-  f32x16_t acc[kI][1];
+  f32x16_t acc[kI][NJ];
 #pragma unroll
   for (int i = 0; i < kI; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[i][0][e] = 0.0f;
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
   const int K = args.H;
   const int n_kt = (K + kBK - 1) / kBK;
-  uint4 wr[kSmallWLoads], hr[kSmallHLoads];
+  uint4 wr[kSmallWLoads], hr[G::kHLoads];
   small_load<true>(wr, wbase, args.ldw, V_tail, wv, lane, 0, K);
   small_load<false>(hr, args.hidden, args.ldh, N, wv, lane, 0, K);
   for (int kt = 0; kt < n_kt; ++kt) {
@@ -444,7 +457,7 @@ __global__ __launch_bounds__(kSmallThreads) void linear_tiles_fwd_small(TileArgs
     // readers, stage kt - 2, finished before the previous barrier), the
     // loads of stage kt + 1 take the registers' place, and the barrier makes
     // the stage visible to both waves.
-    uint4* a = smem + (kt & 1) * kSmallStageVec;
+    uint4* a = smem + (kt & 1) * G::kStageVec;
     small_store(a, wr, wv, lane);
     small_store(a + kSmallWVec, hr, wv, lane);
     if (kt + 1 < n_kt) {
@@ -456,32 +469,47 @@ __global__ __launch_bounds__(kSmallThreads) void linear_tiles_fwd_small(TileArgs
 #pragma unroll
     for (int kk = 0; kk < kSub; ++kk) {
       const int c = 2 * kk + (lane >> 5);
-      bf16x8_t fa[kI];
+      bf16x8_t fa[kI], fb[NJ];
 #pragma unroll
       for (int i = 0; i < kI; ++i) {
         const int r = wv * kPW + i * 32 + (lane & 31);
         fa[i] = __builtin_bit_cast(bf16x8_t, a[r * kRowChunks + swz(r, c)]);
       }
-      const int rq = lane & 31;
-      const bf16x8_t fb = __builtin_bit_cast(bf16x8_t, b[rq * kRowChunks + swz(rq, c)]);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int rq = j * 32 + (lane & 31);
+        fb[j] = __builtin_bit_cast(bf16x8_t, b[rq * kRowChunks + swz(rq, c)]);
+      }
 #pragma unroll
       for (int i = 0; i < kI; ++i)
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb, acc[i][0], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
   }
   __syncthreads();
 
   const int half = lane >> 5;
-  const float2 ms = column_partial<0>(acc, wv, half, V_tail, tl < N, tgt, vocab0 + wv * kPW,
-                                      args.zt, static_cast<int64_t>(tl));
+  const int vwave = vocab0 + wv * kPW;
   float2* red = reinterpret_cast<float2*>(smem);
-  if (half == 0) red[wv * kSmallRows + tl] = ms;
+  {
+    const int tl = lane & 31;
+    const float2 ms = column_partial<0>(acc, wv, half, V_tail, tl < N, tgt[0], vwave, args.zt,
+                                        static_cast<int64_t>(tl));
+    if (half == 0) red[wv * G::kRows + tl] = ms;
+  }
+  if constexpr (NJ == 2) {
+    const int tl = 32 + (lane & 31);
+    const float2 ms = column_partial<1>(acc, wv, half, V_tail, tl < N, tgt[1], vwave, args.zt,
+                                        static_cast<int64_t>(tl));
+    if (half == 0) red[wv * G::kRows + tl] = ms;
+  }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  if (tid < kSmallRows) {
-    float2 p0 = red[tid];
-    const float2 p1 = red[kSmallRows + tid];
+  for (int r = tid; r < G::kRows; r += kSmallThreads) {
+    float2 p0 = red[r];
+    const float2 p1 = red[G::kRows + r];
     lse_merge(p0.x, p0.y, p1.x, p1.y);
-    if (tid < N) args.part[static_cast<int64_t>(tid) * args.n_vtiles + vt] = p0;
+    if (r < N) args.part[static_cast<int64_t>(r) * args.n_vtiles + vt] = p0;
   }
 }
 
@@ -577,8 +605,11 @@ hipError_t launch_linear_logp(const uint16_t* hidden, int64_t ldh, const uint16_
   const uint32_t tiles = static_cast<uint32_t>(static_cast<int64_t>(a.n_vtiles) * a.n_tblocks);
   if (logits != nullptr)
     hipLaunchKernelGGL(linear_tiles_fwd<true>, dim3(tiles), dim3(kThreads), 0, stream, a);
-  else if (N <= kSmallRows)
-    hipLaunchKernelGGL(linear_tiles_fwd_small, dim3(static_cast<uint32_t>(a.n_vtiles)),
+  else if (N <= SmallGeo<1>::kRows)
+    hipLaunchKernelGGL(linear_tiles_fwd_small<1>, dim3(static_cast<uint32_t>(a.n_vtiles)),
+                       dim3(kSmallThreads), 0, stream, a);
+  else if (N <= SmallGeo<2>::kRows)
+    hipLaunchKernelGGL(linear_tiles_fwd_small<2>, dim3(static_cast<uint32_t>(a.n_vtiles)),
                        dim3(kSmallThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(linear_tiles_fwd<false>, dim3(tiles), dim3(kThreads), 0, stream, a);

@@ -106,24 +106,25 @@ def test_tile_offset_sweep(dev):
 
 @pytest.mark.parametrize("v,h", [(1300, 136), (777, 72), (2600, 4096)])
 def test_small_batch_forward_bits(dev, v, h):
-    """Batches of at most 32 rows take the small-batch forward (register-staged
-    W, two waves per tile); each of their rows must carry the bits the same
-    row gets inside a 300-row batch (the full tile forward), around the switch
-    (N = 1, 2, 31, 32 and 33), with a ragged last vocabulary tile and a ragged
-    last K stage, a masked row and an invalid target among them; and the
-    small batches agree with the oracle."""
+    """Batches of at most 64 rows take the small-batch forward (register-staged
+    W, two waves per tile, 32 or 64 token rows); each of their rows must carry
+    the bits the same row gets inside a 300-row batch (the full tile
+    forward), around both switches (N = 1, 2, 31, 32, 33, 63, 64, 65), with a
+    ragged last vocabulary tile and a ragged last K stage, a masked row and
+    an invalid target among them; and the small batches agree with the
+    oracle."""
     b = wl.fused_batch(300, v, h, seed=v + h, device=dev, w_sigma=0.05)
     t = b.targets.clone()
     t[2] = v + 5                      # invalid target on an active row
     m = b.mask.clone()
     m[4] = 0                          # masked row
     full_lp, full_ls = ilp.linear_logp(b.hidden, b.weight, t, m)
-    for n in (1, 2, 31, 32, 33):
+    for n in (1, 2, 31, 32, 33, 63, 64, 65):
         lp, ls = ilp.linear_logp(b.hidden[:n], b.weight, t[:n], m[:n])
         assert torch.equal(f32bits(lp), f32bits(full_lp[:n])), n
         assert torch.equal(f32bits(ls), f32bits(full_ls[:n])), n
-    lp, ls = ilp.linear_logp(b.hidden[:32], b.weight, t[:32], m[:32])
-    keep = [r for r in range(32) if r not in (2, 4)]
+    lp, ls = ilp.linear_logp(b.hidden[:64], b.weight, t[:64], m[:64])
+    keep = [r for r in range(64) if r not in (2, 4)]
     idx = torch.tensor(keep, device=dev)
     rlogp, rlse = _oracle_fused(b.hidden.index_select(0, idx), b.weight, t.index_select(0, idx))
     assert_close(lp.index_select(0, idx).cpu().numpy(), rlogp, TOL_FUSED, "small batch logp")
