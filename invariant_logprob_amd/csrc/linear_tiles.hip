@@ -25,7 +25,8 @@
 // reduction order and no atomics (page "[WS1 Test] #154 dtype pin + ...",
 // section "Workstream 3 - #153", scope item 2); bf16 inputs with fp32
 // accumulation (same page, "Workstream 1 - #154" scope table).  The tile
-// schedule, the MFMA instruction and the K order never depend on N.
+// schedule, the MFMA instruction and the K order never depend on N (a batch
+// of at most 64 rows runs the same per-row sequence in a smaller launch).
 //
 // The backward kernel runs the same per-tile main loop (same copies, same
 // MFMA sequence), so its z is bit-identical to the forward's, and replaces

@@ -1,11 +1,14 @@
 // C ABI of the batch-invariant selected-token logprob library (include/rlk.h).
 //
 // Host side only: argument validation, then launches on the caller's
-// stream.  The kernel and its schedule are chosen from V (and H) only, never
-// from N, so the batch shape cannot change how a row is reduced (page "[RFC]
-// Batch-Invariant RL Kernel Suite for Train-Inference Consistency", section
-// "Problem": dispatch by shape is one of the named drift sources).  No
-// allocation, no synchronisation, no mutable state.
+// stream.  How a row is reduced -- the kernel's arithmetic, its reduction
+// schedule and order -- is chosen from V (and H) only, never from N, so the
+// batch shape cannot change a row's bits (page "[RFC] Batch-Invariant RL
+// Kernel Suite for Train-Inference Consistency", section "Problem": dispatch
+// by shape is one of the named drift sources).  The one choice N makes is the
+// fused forward's launch form for batches of at most 64 rows, which runs the
+// full tile's instruction sequence for those rows and yields the same bits.
+// No allocation, no synchronisation, no mutable state.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
