@@ -2,7 +2,8 @@
 //
 // Forward (one workgroup per row; more rows than one launch's grid limit
 // take further launches from the host, with the same per-row schedule).  The
-// row is streamed once from HBM in 16-byte vectors of 8 bf16.  Vector k of a
+// row is streamed once from HBM in 16-byte vectors of 8 bf16; a row of at
+// most four steps (V <= 32768) is requested whole before it is consumed.  Vector k of a
 // row always goes to thread k % kRowThreads and is visited in ascending k, so
 // every lane's partial (M, s) is a function of the row's values and of V
 // alone.  Lanes merge in a fixed wave64 butterfly over register lane
@@ -111,7 +112,7 @@ __device__ __forceinline__ void consume3(float& M, float& s, float& t, const Vec
   }
 }
 
-template <int THREADS, int UNROLL, bool kEntropy>
+template <int THREADS, int UNROLL, bool kEntropy, int kShort = 0>
 __global__ __launch_bounds__(THREADS) void logp_fwd_rows(
     const uint16_t* __restrict__ logits, int64_t ld, const int64_t* __restrict__ targets,
     const uint8_t* __restrict__ mask, int64_t row0, int V, float* __restrict__ logp,
@@ -145,6 +146,39 @@ __global__ __launch_bounds__(THREADS) void logp_fwd_rows(
   float M = neg_inf();
   float s = 0.0f;
   float tw = 0.0f;  // entropy variant only
+  if constexpr (kShort > 0) {
+    // Short rows (at most kShort steps): every load of the row is issued
+    // before the first is consumed, so the row costs one memory round trip
+    // rather than one per step; the steps are then consumed in the same
+    // order, with the same tail handling, as the loop below (the same bits).
+    uint4 wv[kShort][UNROLL];
+#pragma unroll
+    for (int st = 0; st < kShort; ++st)
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int k = st * kStep + u * THREADS + tid;
+        wv[st][u] = make_uint4(kNegInfPair, kNegInfPair, kNegInfPair, kNegInfPair);
+        if (k < nvec) wv[st][u] = load16_stream(vp + k);
+      }
+#pragma unroll
+    for (int st = 0; st < kShort; ++st) {
+      const int base = st * kStep;
+      if (base >= nvec) break;
+      Vec8 x[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        x[u] = decode(wv[st][u]);
+        const int k = base + u * THREADS + tid;
+        if (base >= nmain && k == nfull) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (8 * k + e >= V) x[u].v[e] = neg_inf();
+        }
+      }
+      if constexpr (kEntropy) consume3<UNROLL>(M, s, tw, x);
+      else consume<UNROLL>(M, s, x);
+    }
+  } else {
   for (int base = 0; base < nmain; base += kStep) {
     uint4 w[UNROLL];
 #pragma unroll
@@ -172,6 +206,7 @@ __global__ __launch_bounds__(THREADS) void logp_fwd_rows(
     }
     if constexpr (kEntropy) consume3<UNROLL>(M, s, tw, x);
     else consume<UNROLL>(M, s, x);
+  }
   }
 
   if constexpr (kEntropy) wave_lse3_allreduce(M, s, tw, tid & 63);
@@ -420,6 +455,10 @@ constexpr int64_t kBwdMaxGrid = int64_t(1) << 22;
 // Rows per launch of the forward; more rows take further launches (the
 // kernel stays a straight-line one-row program: no loop-carried state).
 constexpr int64_t kRowMaxGrid = int64_t(1) << 22;
+// Rows of at most this many steps (V <= 32768 at 256 threads x 4 vectors)
+// have all their loads issued at once: a short row then costs one memory
+// round trip instead of one per step.
+constexpr int kShortSteps = 4;
 
 int logits_schedule_threads() { return kRowThreads; }
 int logits_schedule_unroll() { return kRowUnroll; }
@@ -429,7 +468,17 @@ hipError_t launch_logp_fwd_rows(const uint16_t* logits, int64_t ld, const int64_
                                 float* entropy, hipStream_t stream) {
   for (int64_t row0 = 0; row0 < N; row0 += kRowMaxGrid) {
     const uint32_t grid = static_cast<uint32_t>(N - row0 < kRowMaxGrid ? N - row0 : kRowMaxGrid);
-    if (entropy == nullptr) {
+    // rows of at most kShortSteps steps are requested whole (chosen by V)
+    const bool short_rows = (V + 7) / 8 <= kShortSteps * kRowThreads * kRowUnroll;
+    if (short_rows && entropy == nullptr) {
+      hipLaunchKernelGGL((logp_fwd_rows<kRowThreads, kRowUnroll, false, kShortSteps>), dim3(grid),
+                         dim3(kRowThreads), 0, stream, logits, ld, targets, mask, row0, V, logp,
+                         lse, nullptr);
+    } else if (short_rows) {
+      hipLaunchKernelGGL((logp_fwd_rows<kRowThreads, kRowUnroll, true, kShortSteps>), dim3(grid),
+                         dim3(kRowThreads), 0, stream, logits, ld, targets, mask, row0, V, logp,
+                         lse, entropy);
+    } else if (entropy == nullptr) {
       hipLaunchKernelGGL((logp_fwd_rows<kRowThreads, kRowUnroll, false>), dim3(grid),
                          dim3(kRowThreads), 0, stream, logits, ld, targets, mask, row0, V, logp,
                          lse, nullptr);

@@ -52,7 +52,7 @@ def test_small_config_parity(dev):
     _run_and_compare(b.logits, b.targets, b.mask, "N=8 V=1024", grad=b.grad)
 
 
-@pytest.mark.parametrize("v", [1, 2, 7, 8, 9, 15, 2047, 2049, 16384 + 3, 16384 * 3 + 8, 40001])
+@pytest.mark.parametrize("v", [1, 2, 7, 8, 9, 15, 2047, 2049, 16384 + 3, 32768, 32768 + 8, 16384 * 3 + 8, 40001])
 def test_ragged_vocab_parity(dev, v):
     n = 6
     g = torch.Generator(device=dev).manual_seed(v)
