@@ -86,15 +86,17 @@ __device__ __forceinline__ void consume(float& M, float& s, const Vec8 (&x)[U]) 
 
 // Entropy variant of consume: the same terms also weight the logits.  A -inf
 // logit is clamped to -FLT_MAX for the product, so its zero term adds 0
-// instead of 0 * -inf.
+// instead of 0 * -inf; the clamp is the NaN-propagating maximum (one
+// instruction, no quieting of its input), and a NaN logit makes the row NaN
+// through its own term either way.
 __device__ __forceinline__ float sum8_weighted(const Vec8& a, float Mu, float& tsum) {
   float e[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) e[k] = lse_term(a.v[k], Mu);
   // weighted terms as one explicit multiply-add chain in element order
-  float tw = e[0] * fmaxf(a.v[0], -3.402823466e38f);
+  float tw = e[0] * vmax(a.v[0], -3.402823466e38f);
 #pragma unroll
-  for (int k = 1; k < 8; ++k) tw = __builtin_fmaf(e[k], fmaxf(a.v[k], -3.402823466e38f), tw);
+  for (int k = 1; k < 8; ++k) tw = __builtin_fmaf(e[k], vmax(a.v[k], -3.402823466e38f), tw);
   tsum = tw;
   return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
 }
