@@ -1,9 +1,10 @@
 """The allocation-free fused forward (rlk_linear_logp_noalloc) against the
 workspace entry point (rlk_linear_logp), both through the C ABI: two calls in
 a row, the first at the size limit of the library's 32 MiB per-GPU array, the
-second smaller (so the array holds the first call's contents), each
-bit-identical to rlk_linear_logp's output on the same inputs; the smaller one
-also against the fp64 oracle within the fused tolerance."""
+second smaller (so the array holds the first call's contents), then a
+five-row batch (the small-batch forward), each bit-identical to
+rlk_linear_logp's output on the same inputs; the 300-row one also against the
+fp64 oracle within the fused tolerance."""
 import numpy as np
 import pytest
 import torch
@@ -52,6 +53,10 @@ def test_noalloc_matches_workspace_entry_point(dev):
     assert_close(lp_n.cpu().numpy(), rlogp, TOL_FUSED, "noalloc logp", act)
     assert_close(ls_n.cpu().numpy(), rlse, TOL_FUSED, "noalloc lse", act)
     assert bool((f32bits(lp_n)[torch.from_numpy(~act)] == 0).all())
+    # and a batch small enough for the small-batch forward
+    tiny = wl.fused_batch(5, 2600, 256, seed=54, device=dev, w_sigma=0.05)
+    lp_n, ls_n, lp_w, ls_w = _both(tiny)
+    assert torch.equal(f32bits(lp_n), f32bits(lp_w)) and torch.equal(f32bits(ls_n), f32bits(ls_w))
 
 
 def test_noalloc_refuses_beyond_its_array(dev):
