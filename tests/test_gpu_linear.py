@@ -169,22 +169,19 @@ def test_fused_transforms_small(dev):
 
 
 def test_fused_large_config(dev):
-    """hidden [8192, 4096], W [128256, 4096]: against the oracle, two complete
-    256-token blocks (rows 0-255 and 4096-4351, every MFMA column position of
-    a tile) and rows 8160-8191 (the end of the last block), 544 rows; the same
-    rows bitwise at N = 1, 33 and 8192."""
+    """hidden [8192, 4096], W [128256, 4096]: logp and lse of all 8192 rows
+    against the oracle (about 8.6 TFLOP of fp64 products on the host, row
+    blocks of 256 on all its cores: every MFMA column position of every token
+    block, the ragged last vocabulary tile included); rows bitwise equal at
+    N = 1, 33 and 8192."""
     b = wl.fused_large(seed=0, device=dev)
     logp, lse = ilp.linear_logp(b.hidden, b.weight, b.targets, b.mask)
     torch.cuda.synchronize()
-    rows = list(range(0, 256)) + list(range(4096, 4352)) + list(range(8160, 8192))
-    assert len(rows) == 544
-    idx = torch.tensor(rows, device=dev)
-    sub_h = b.hidden.index_select(0, idx)
-    sub_t = b.targets.index_select(0, idx)
-    rlogp, rlse = _oracle_fused(sub_h, b.weight, sub_t)
-    assert_close(logp.index_select(0, idx).cpu().numpy(), rlogp, TOL_FUSED, "C4 logp (544 rows)")
-    assert_close(lse.index_select(0, idx).cpu().numpy(), rlse, TOL_FUSED, "C4 lse (544 rows)")
-    for r in rows[:4]:
+    rlogp, rlse = _oracle_fused(b.hidden, b.weight, b.targets, b.mask)
+    assert rlogp.shape == (8192,)
+    assert_close(logp.cpu().numpy(), rlogp, TOL_FUSED, "C4 logp (all 8192 rows)")
+    assert_close(lse.cpu().numpy(), rlse, TOL_FUSED, "C4 lse (all 8192 rows)")
+    for r in (0, 1, 4095, 8191):
         one = ilp.linear_logp(b.hidden[r:r + 1], b.weight, b.targets[r:r + 1])
         assert _bits_equal(one[0], logp[r:r + 1]) and _bits_equal(one[1], lse[r:r + 1]), r
     s33 = ilp.linear_logp(b.hidden[4090:4123], b.weight, b.targets[4090:4123])
