@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--extra-legs",
                    default="logits_entropy,log_softmax,token_losses,fused_param_grads,"
                            "fused_fb_kept_logits,fused_param_grads_kept_logits,fused_fwd_n1,"
-                           "logits_small,logits_varlen",
+                           "fused_bwd_n1,logits_small,logits_varlen",
                    help="rows beyond the hot path, timed after the steps (not part of a step)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="instead of the hot path, run a plain 1 GiB device copy 5 times "
@@ -381,15 +381,24 @@ def main():
         xfns["fused_fb_kept_logits"] = (kept, n5 * h5 * 2 + v5 * h5 * 2 + 2 * n5 * v5 * 4 * 2)
         xflops["fused_fb_kept_logits"] = 2.0 * n5 * v5 * h5
     if c4 is not None and "fused_fwd_n1" in args.extra_legs.split(","):
-        # one row of the fused forward workload: the kernel and schedule are
-        # those of any N, and the W stream (V x H bf16) is the algorithmic
-        # traffic that bounds it
+        # one row of the fused forward workload: the row's reduction schedule
+        # is that of any N (batches of at most 64 rows take a smaller launch),
+        # and the W stream (V x H bf16) is the algorithmic traffic that bounds it
         h41, t41, m41 = c4.hidden[:1], c4.targets[:1], c4.mask[:1]
         lp41 = torch.empty(1, dtype=torch.float32, device=dev)
         ls41 = torch.empty(1, dtype=torch.float32, device=dev)
         xfns["fused_fwd_n1"] = (
             lambda: ilp.linear_logp(h41, c4.weight, t41, m41, workspace=ws4, logp=lp41, lse=ls41),
             v4 * h4 * 2 + h4 * 2 + 8 + 1 + 8)
+    if c5 is not None and "fused_bwd_n1" in args.extra_legs.split(","):
+        # one row of the fused backward workload (a decode step's gradient):
+        # the W stream plus the row's V fp32 gradients
+        h51, t51, m51, g51 = c5.hidden[:1], c5.targets[:1], c5.mask[:1], c5.grad[:1]
+        ls51 = lse5[:1].clone()
+        d51 = torch.empty((1, v5), dtype=torch.float32, device=dev)
+        xfns["fused_bwd_n1"] = (
+            lambda: ilp.linear_logp_backward(h51, c5.weight, t51, ls51, g51, m51, out=d51),
+            v5 * h5 * 2 + h5 * 2 + 8 + 1 + 4 + 4 + v5 * 4)
     for name in [x for x in args.extra_legs.split(",") if x in xfns]:
         fn, nbytes = xfns[name]
         for _ in range(max(1, args.warmup)):

@@ -189,7 +189,9 @@ int rlk_linear_logp_noalloc(const void* hidden, int64_t ld_h,
  *                 RLK_ERR_INVALID_ARG.
  *   Fused mode  : `logits` NULL; x_i = W . h_i is recomputed with exactly
  *                 the tiles and K order rlk_linear_logp uses (hidden
- *                 [N, ld_h], weight [V, ld_w], H as there).
+ *                 [N, ld_h], weight [V, ld_w], H as there); a batch of
+ *                 at most 64 rows runs the same per-row instruction
+ *                 sequence in a smaller launch (the same bits).
  *   lse        : fp32 [N], required -- the forward's output for these rows.
  *   grad_logp  : fp32 [N], required (the upstream gradient g).
  */

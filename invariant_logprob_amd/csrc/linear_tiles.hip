@@ -26,7 +26,8 @@
 // section "Workstream 3 - #153", scope item 2); bf16 inputs with fp32
 // accumulation (same page, "Workstream 1 - #154" scope table).  The tile
 // schedule, the MFMA instruction and the K order never depend on N (a batch
-// of at most 64 rows runs the same per-row sequence in a smaller launch).
+// of at most 64 rows runs the same per-row sequence in a smaller launch, in
+// the forward and in the backward).
 //
 // The backward kernel runs the same per-tile main loop (same copies, same
 // MFMA sequence), so its z is bit-identical to the forward's, and replaces
@@ -140,6 +141,50 @@ __device__ __forceinline__ float2 column_partial(const f32x16_t (&acc)[kI][NJ], 
   return make_float2(M, s);
 }
 
+// Per-token terms of the dlogits epilogue for token column tok of a lane
+// whose first vocabulary row is vlane (vwave + 4 * half).  d = g ([v == t] -
+// p) is formed without branches: p is always evaluated, a masked row (or a
+// token column past N) selects +0 whatever its logits hold, an active row
+// with an invalid target carries NaN in the additive term, and NaN or
+// infinite logits of an active row reach its gradient unclamped.
+struct DlogitsColumn {
+  bool active;
+  float g;
+  float ng;
+  float off;     // lse * log2(e)
+  float poison;  // NaN for an active row with an invalid target, else +0
+  int rel;       // the target's offset from vlane, or -1 when outside [0, 128)
+};
+
+__device__ __forceinline__ DlogitsColumn dlogits_column(const TileArgs& args, bool have,
+                                                        int64_t tok, int vlane) {
+  DlogitsColumn c;
+  c.active = have && ((args.mask == nullptr) || (args.mask[tok] != 0));
+  const int64_t t = c.active ? args.targets[tok] : -1;
+  const bool tvalid = (t >= 0 && t < args.V);
+  c.g = c.active ? args.grad[tok] : 0.0f;
+  c.ng = -c.g;
+  c.off = c.active ? args.lse[tok] * kLog2e : 0.0f;
+  const int64_t rt = t - vlane;
+  c.rel = (rt >= 0 && rt < 128) ? static_cast<int>(rt) : -1;
+  c.poison = (c.active && !tvalid) ? __builtin_nanf("") : 0.0f;
+  return c;
+}
+
+// dlogits of accumulator elements 4q .. 4q + 3 of block i, that is vocabulary
+// rows vlane + 32 i + 8 q + e, e = 0 .. 3.
+__device__ __forceinline__ float4 dlogits_quad(const f32x16_t& a, int i, int q,
+                                               const DlogitsColumn& c) {
+  float d[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float p = fast_exp2(__builtin_fmaf(a[4 * q + e], kLog2e, -c.off));
+    const float add = (i * 32 + 8 * q + e == c.rel) ? c.g : 0.0f;
+    d[e] = c.active ? __builtin_fmaf(c.ng, p, add + c.poison) : 0.0f;
+  }
+  return make_float4(d[0], d[1], d[2], d[3]);
+}
+
 // blockIdx -> (vocabulary tile, token block): XCD-contiguous ranges, then
 // groups of kLinearVocabGroup vocabulary tiles x all token blocks.
 __device__ __forceinline__ void tile_coords(int w, int n_vtiles, int n_tblocks, int& vt, int& tb) {
@@ -182,42 +227,16 @@ void linear_tiles_bwd(TileArgs args) {
     // dlogits tile, staged through LDS one 32-token slice at a time so that
     // each store instruction writes two 512-byte row segments.
     float* stage = reinterpret_cast<float*>(smem) + wave * (32 * kStageStride);
-    const float nan = __builtin_nanf("");
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
       const int tl = wt * kQW + j * 32 + (lane & 31);
-      const bool have = tl < N_tail;
-      const int64_t tok = tok0 + tl;
-      const bool active = have && ((args.mask == nullptr) || (args.mask[tok] != 0));
-      const int64_t t = active ? args.targets[tok] : -1;
-      const bool tvalid = (t >= 0 && t < args.V);
-      const float g = active ? args.grad[tok] : 0.0f;
-      const float ng = -g;
-      const float off = active ? args.lse[tok] * kLog2e : 0.0f;
-      // The target's offset from this lane's first vocabulary row, or -1.
-      const int64_t rt = t - (vwave + 4 * half);
-      const int rel = (rt >= 0 && rt < 128) ? static_cast<int>(rt) : -1;
-      // d = g ([j == t] - p) without branches: p is always evaluated, a
-      // masked row (or a token column past N) selects +0 whatever its logits
-      // hold, an active row with an invalid target carries NaN in the
-      // additive term, and NaN or infinite logits of an active row reach its
-      // gradient unclamped.
-      const float poison = (active && !tvalid) ? nan : 0.0f;
+      const DlogitsColumn c = dlogits_column(args, tl < N_tail, tok0 + tl, vwave + 4 * half);
       float* srow = stage + (lane & 31) * kStageStride;
 #pragma unroll
       for (int i = 0; i < kI; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int m0 = i * 32 + 8 * q + 4 * half;  // relative to vwave
-          float d[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p = fast_exp2(__builtin_fmaf(acc[i][j][4 * q + e], kLog2e, -off));
-            const float add = (i * 32 + 8 * q + e == rel) ? g : 0.0f;
-            d[e] = active ? __builtin_fmaf(ng, p, add + poison) : 0.0f;
-          }
-          *reinterpret_cast<float4*>(srow + m0) = make_float4(d[0], d[1], d[2], d[3]);
-        }
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(srow + i * 32 + 8 * q + 4 * half) = dlogits_quad(acc[i][j], i, q, c);
       __syncthreads();
 #pragma unroll 4
       for (int step = 0; step < 16; ++step) {
@@ -360,35 +379,38 @@ void linear_tiles_fwd(TileArgs args) {
   }
 }
 
-// Forward for a batch of at most 64 token rows: all of them lie in token
-// quarter 0 of a tile (its first 32 or 64 rows, NJ = 1 or 2 block columns),
-// so of the tile's MFMA work only the blocks (i, j < NJ) of the two waves
-// with token quarter 0 matter, and the tile is bound by streaming its 256 W
-// rows.  This kernel runs exactly those blocks -- the same fragments, the
-// same v_mfma_f32_32x32x16_bf16 sequence in the same K order, hence the same
-// fp32 logits -- and the same column epilogue and wave merge
-// (column_partial, then vocabulary half 0 before half 1), so every row's
-// partials, z_t, logp and lse are bit-identical to those of
-// linear_tiles_fwd<false>.  What differs is only how W reaches the LDS:
-// through registers (16-byte loads, eight lanes per 128-byte row segment,
-// the next stage's loads in flight while this stage is consumed) instead of
-// direct-to-LDS copies, which stream this pattern about a sixth slower; and
-// a stage holds only the batch's 32 or 64 hidden rows, so a workgroup needs
-// 72 or 80 KB and two fit on a compute unit.  Two waves, one per vocabulary
-// half, one workgroup per 256-entry vocabulary tile.
-constexpr int kSmallWaves = 2;
-constexpr int kSmallThreads = 64 * kSmallWaves;
-constexpr int kSmallWVec = kBV * kRowChunks;           // uint4 of W per stage (32 KB)
-constexpr int kSmallWLoads = kSmallWVec / 64 / kSmallWaves;  // 16-byte loads per lane per stage
-static_assert(kSmallWLoads == 16, "16 W loads per lane and stage");
-
+// Small batches (at most 64 token rows).  All rows lie in token quarter 0 of
+// a tile (its first 32 or 64 rows, NJ = 1 or 2 block columns), so of the
+// tile's MFMA work only the blocks (i, j < NJ) matter, and the tile is bound
+// by streaming its 256 W rows.  The small-batch kernels run exactly those
+// blocks -- the same fragments, the same v_mfma_f32_32x32x16_bf16 sequence
+// in the same K order, hence the same fp32 logits -- and the forward ends
+// with the same column epilogue and wave merge (column_partial, then
+// vocabulary half 0 before half 1), so every row's partials, z_t, logp and
+// lse, and every dlogits entry of the backward, are bit-identical to those
+// of the full tile kernels.  What differs is the launch: one workgroup of
+// 2 NJ waves per 256-entry vocabulary tile, wave (wv, jw) owning the blocks
+// (i, jw) of vocabulary half wv; W reaches the LDS through registers
+// (16-byte loads, eight lanes per 128-byte row segment, the next stage's
+// loads in flight while this stage is consumed) instead of direct-to-LDS
+// copies, which stream this pattern about a sixth slower; and the LDS holds
+// one stage of W and of the batch's hidden rows (36 or 40 KB), so four (NJ =
+// 1) or three (NJ = 2) workgroups fit on a compute unit and a vocabulary of
+// up to 1024 or 768 tiles streams in a single round.
 template <int NJ>
 struct SmallGeo {
-  static constexpr int kRows = 32 * NJ;                         // token rows held
-  static constexpr int kHVec = kRows * kRowChunks;              // uint4 of hidden per stage
-  static constexpr int kStageVec = kSmallWVec + kHVec;
-  static constexpr int kHLoads = kHVec / 64 / kSmallWaves;
-  static_assert(2 * 2 * kStageVec * 16 <= 160 * 1024, "two workgroups per compute unit");
+  static constexpr int kWaves = 2 * NJ;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kRows = 32 * NJ;                  // token rows held
+  static constexpr int kWVec = kBV * kRowChunks;         // uint4 of W per stage (32 KB)
+  static constexpr int kHVec = kRows * kRowChunks;       // uint4 of hidden per stage
+  static constexpr int kStageVec = kWVec + kHVec;
+  static constexpr int kWLoads = kWVec / 64 / kWaves;    // 16-byte loads per lane and stage
+  static constexpr int kHLoads = kHVec / 64 / kWaves;
+  static constexpr int kPerCU = NJ == 1 ? 4 : 3;         // workgroups per compute unit
+  static constexpr int kWavesPerSimd = kPerCU * kWaves / 4;
+  static_assert(kPerCU * kStageVec * 16 <= 160 * 1024, "LDS of the resident workgroups");
+  static_assert(kWLoads * 64 * kWaves == kWVec && kHLoads * 64 * kWaves == kHVec, "load split");
 };
 
 // One operand's part of a stage for this lane: chunk idx = (wave * n + q) *
@@ -422,96 +444,138 @@ __device__ __forceinline__ void small_store(uint4* dst, const uint4 (&v)[NL], in
   }
 }
 
+// The small-batch main loop of wave (wv, jw): each stage of W and of the
+// batch's hidden rows passes through registers into the tile layout in the
+// LDS (the next stage's loads are issued right after), and the wave runs
+// the blocks (i, jw) with the tile core's fragments and MFMA order.  Two
+// barriers per stage: the stage is visible before its reads, and its reads
+// end before the next stage overwrites it.  The LDS is free on return.
 template <int NJ>
-__global__ __launch_bounds__(kSmallThreads) void linear_tiles_fwd_small(TileArgs args) {
+__device__ __forceinline__ void small_mainloop(uint4* smem, const TileArgs& args, int wave,
+                                               int lane, int vocab0, int V_tail, int N,
+                                               f32x16_t (&acc)[kI][1]) {
   using G = SmallGeo<NJ>;
-  __shared__ uint4 smem[2 * G::kStageVec];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;  // vocabulary half of the tile
-  const int vt = blockIdx.x;
-  const int vocab0 = vt * kBV;
-  const int V_tail = min(args.V - vocab0, kBV);
-  const int N = static_cast<int>(args.N);  // at most G::kRows
-  int64_t tgt[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int tl = j * 32 + (lane & 31);
-    tgt[j] = (tl < N) ? args.targets[tl] : -1;
-  }
+  const int wv = wave & 1;
+  const int jw = wave >> 1;
   const uint16_t* wbase = args.weight + static_cast<int64_t>(vocab0) * args.ldw;
-
-  f32x16_t acc[kI][NJ];
 #pragma unroll
   for (int i = 0; i < kI; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    for (int e = 0; e < 16; ++e) acc[i][0][e] = 0.0f;
   const int K = args.H;
   const int n_kt = (K + kBK - 1) / kBK;
-  uint4 wr[kSmallWLoads], hr[G::kHLoads];
-  small_load<true>(wr, wbase, args.ldw, V_tail, wv, lane, 0, K);
-  small_load<false>(hr, args.hidden, args.ldh, N, wv, lane, 0, K);
+  uint4 wr[G::kWLoads], hr[G::kHLoads];
+  small_load<true>(wr, wbase, args.ldw, V_tail, wave, lane, 0, K);
+  small_load<false>(hr, args.hidden, args.ldh, N, wave, lane, 0, K);
+  const uint4* a = smem;
+  const uint4* b = smem + G::kWVec;
   for (int kt = 0; kt < n_kt; ++kt) {
-    // Stage kt goes from the registers to LDS buffer kt & 1 (its last
-    // readers, stage kt - 2, finished before the previous barrier), the
-    // loads of stage kt + 1 take the registers' place, and the barrier makes
-    // the stage visible to both waves.
-    uint4* a = smem + (kt & 1) * G::kStageVec;
-    small_store(a, wr, wv, lane);
-    small_store(a + kSmallWVec, hr, wv, lane);
+    small_store(smem, wr, wave, lane);
+    small_store(smem + G::kWVec, hr, wave, lane);
     if (kt + 1 < n_kt) {
-      small_load<true>(wr, wbase, args.ldw, V_tail, wv, lane, (kt + 1) * kBK, K);
-      small_load<false>(hr, args.hidden, args.ldh, N, wv, lane, (kt + 1) * kBK, K);
+      small_load<true>(wr, wbase, args.ldw, V_tail, wave, lane, (kt + 1) * kBK, K);
+      small_load<false>(hr, args.hidden, args.ldh, N, wave, lane, (kt + 1) * kBK, K);
     }
     __syncthreads();
-    const uint4* b = a + kSmallWVec;
 #pragma unroll
     for (int kk = 0; kk < kSub; ++kk) {
       const int c = 2 * kk + (lane >> 5);
-      bf16x8_t fa[kI], fb[NJ];
+      bf16x8_t fa[kI];
 #pragma unroll
       for (int i = 0; i < kI; ++i) {
         const int r = wv * kPW + i * 32 + (lane & 31);
         fa[i] = __builtin_bit_cast(bf16x8_t, a[r * kRowChunks + swz(r, c)]);
       }
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int rq = j * 32 + (lane & 31);
-        fb[j] = __builtin_bit_cast(bf16x8_t, b[rq * kRowChunks + swz(rq, c)]);
-      }
+      const int rq = jw * 32 + (lane & 31);
+      const bf16x8_t fb = __builtin_bit_cast(bf16x8_t, b[rq * kRowChunks + swz(rq, c)]);
 #pragma unroll
       for (int i = 0; i < kI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb, acc[i][0], 0, 0, 0);
     }
+    __syncthreads();
   }
-  __syncthreads();
+}
+
+template <int NJ>
+__global__ __launch_bounds__(SmallGeo<NJ>::kThreads)
+__attribute__((amdgpu_waves_per_eu(SmallGeo<NJ>::kWavesPerSimd)))
+void linear_tiles_fwd_small(TileArgs args) {
+  using G = SmallGeo<NJ>;
+  __shared__ uint4 smem[G::kStageVec];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wv = wave & 1;  // vocabulary half of the tile
+  const int vt = blockIdx.x;
+  const int vocab0 = vt * kBV;
+  const int V_tail = min(args.V - vocab0, kBV);
+  const int N = static_cast<int>(args.N);  // at most G::kRows
+  const int tl = (wave >> 1) * 32 + (lane & 31);  // this lane's token row
+  f32x16_t acc[kI][1];
+  small_mainloop<NJ>(smem, args, wave, lane, vocab0, V_tail, N, acc);
+  // (the target is read after the main loop: held across it, it would push
+  // the 64-row form past its register budget)
+  const int64_t tgt = (tl < N) ? args.targets[tl] : -1;
 
   const int half = lane >> 5;
   const int vwave = vocab0 + wv * kPW;
   float2* red = reinterpret_cast<float2*>(smem);
-  {
-    const int tl = lane & 31;
-    const float2 ms = column_partial<0>(acc, wv, half, V_tail, tl < N, tgt[0], vwave, args.zt,
-                                        static_cast<int64_t>(tl));
-    if (half == 0) red[wv * G::kRows + tl] = ms;
-  }
-  if constexpr (NJ == 2) {
-    const int tl = 32 + (lane & 31);
-    const float2 ms = column_partial<1>(acc, wv, half, V_tail, tl < N, tgt[1], vwave, args.zt,
-                                        static_cast<int64_t>(tl));
-    if (half == 0) red[wv * G::kRows + tl] = ms;
-  }
+  const float2 ms = column_partial<0>(acc, wv, half, V_tail, tl < N, tgt, vwave, args.zt,
+                                      static_cast<int64_t>(tl));
+  if (half == 0) red[wv * G::kRows + tl] = ms;
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  for (int r = tid; r < G::kRows; r += kSmallThreads) {
+  for (int r = tid; r < G::kRows; r += G::kThreads) {
     float2 p0 = red[r];
     const float2 p1 = red[G::kRows + r];
     lse_merge(p0.x, p0.y, p1.x, p1.y);
     if (r < N) args.part[static_cast<int64_t>(r) * args.n_vtiles + vt] = p0;
   }
+}
+
+// Backward for a batch of at most 64 token rows: the small-batch main loop
+// (the same logits as linear_tiles_bwd's, bit for bit), then each lane writes
+// its dlogits straight from the accumulators (dlogits_quad, the same formula
+// as the full tile's epilogue), 16 bytes at a time; a token's row gets 32
+// contiguous bytes per store instruction from the two lane halves.  At these
+// batch sizes the output is small beside the W stream.
+template <int NJ>
+__global__ __launch_bounds__(SmallGeo<NJ>::kThreads)
+__attribute__((amdgpu_waves_per_eu(SmallGeo<NJ>::kWavesPerSimd)))
+void linear_tiles_bwd_small(TileArgs args) {
+  using G = SmallGeo<NJ>;
+  __shared__ uint4 smem[G::kStageVec];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wv = wave & 1;  // vocabulary half of the tile
+  const int vt = blockIdx.x;
+  const int vocab0 = vt * kBV;
+  const int V_tail = min(args.V - vocab0, kBV);
+  const int N = static_cast<int>(args.N);  // at most G::kRows
+  const int half = lane >> 5;
+  const int vlane = vocab0 + wv * kPW + 4 * half;  // this lane's first vocabulary row
+  const int tl = (wave >> 1) * 32 + (lane & 31);   // this lane's token row
+  const DlogitsColumn col = dlogits_column(args, tl < N, tl, vlane);
+  f32x16_t acc[kI][1];
+  small_mainloop<NJ>(smem, args, wave, lane, vocab0, V_tail, N, acc);
+  if (tl >= N) return;
+  float* drow = args.dl + static_cast<int64_t>(tl) * args.ldg + vlane;
+#pragma unroll
+  for (int i = 0; i < kI; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 d = dlogits_quad(acc[i][0], i, q, col);
+      const int m = vlane - vocab0 + i * 32 + 8 * q;  // relative to vocab0
+      float* dst = drow + i * 32 + 8 * q;
+      if (m + 4 <= V_tail) {
+        store16_stream(dst, d.x, d.y, d.z, d.w);
+      } else {
+        const float dd[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (m + e < V_tail) dst[e] = dd[e];
+      }
+    }
 }
 
 // One wave per row: lane l merges the row's chunk partials l, l + 64,
@@ -608,10 +672,10 @@ hipError_t launch_linear_logp(const uint16_t* hidden, int64_t ldh, const uint16_
     hipLaunchKernelGGL(linear_tiles_fwd<true>, dim3(tiles), dim3(kThreads), 0, stream, a);
   else if (N <= SmallGeo<1>::kRows)
     hipLaunchKernelGGL(linear_tiles_fwd_small<1>, dim3(static_cast<uint32_t>(a.n_vtiles)),
-                       dim3(kSmallThreads), 0, stream, a);
+                       dim3(SmallGeo<1>::kThreads), 0, stream, a);
   else if (N <= SmallGeo<2>::kRows)
     hipLaunchKernelGGL(linear_tiles_fwd_small<2>, dim3(static_cast<uint32_t>(a.n_vtiles)),
-                       dim3(kSmallThreads), 0, stream, a);
+                       dim3(SmallGeo<2>::kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(linear_tiles_fwd<false>, dim3(tiles), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
@@ -634,8 +698,15 @@ hipError_t launch_linear_dlogits(const uint16_t* hidden, int64_t ldh, const uint
   a.dl = dl;
   a.ldg = ldg;
   const int64_t tiles = static_cast<int64_t>(a.n_vtiles) * a.n_tblocks;
-  hipLaunchKernelGGL(linear_tiles_bwd, dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0,
-                     stream, a);
+  if (N <= SmallGeo<1>::kRows)
+    hipLaunchKernelGGL(linear_tiles_bwd_small<1>, dim3(static_cast<uint32_t>(a.n_vtiles)),
+                       dim3(SmallGeo<1>::kThreads), 0, stream, a);
+  else if (N <= SmallGeo<2>::kRows)
+    hipLaunchKernelGGL(linear_tiles_bwd_small<2>, dim3(static_cast<uint32_t>(a.n_vtiles)),
+                       dim3(SmallGeo<2>::kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(linear_tiles_bwd, dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0,
+                       stream, a);
   return hipGetLastError();
 }
 

@@ -132,6 +132,38 @@ def test_small_batch_forward_bits(dev, v, h):
     assert math.isnan(float(lp[2])) and int(f32bits(lp[4:5])[0]) == 0
 
 
+@pytest.mark.parametrize("v,h", [(1300, 136), (777, 72), (2600, 4096)])
+def test_small_batch_backward_bits(dev, v, h):
+    """Batches of at most 64 rows take the small-batch backward (the small
+    forward's main loop, dlogits stored from the accumulators); each of their
+    dlogits rows must carry the bits the same row gets inside a 300-row batch
+    (the full tile backward), around both switches, with a ragged last
+    vocabulary tile and a ragged last K stage, a masked row (all +0.0) and an
+    invalid target on an active row (all NaN); and the 64-row batch agrees
+    with the oracle's own gradient."""
+    b = wl.fused_batch(300, v, h, seed=v + h + 1, device=dev, w_sigma=0.05)
+    t = b.targets.clone()
+    t[2] = v + 5                      # invalid target on an active row
+    m = b.mask.clone()
+    m[4] = 0                          # masked row
+    _, full_ls = ilp.linear_logp(b.hidden, b.weight, t, m)
+    full_d = ilp.linear_logp_backward(b.hidden, b.weight, t, full_ls, b.grad, m)
+    for n in (1, 2, 31, 32, 33, 63, 64, 65):
+        d = ilp.linear_logp_backward(b.hidden[:n], b.weight, t[:n], full_ls[:n], b.grad[:n], m[:n])
+        assert torch.equal(f32bits(d), f32bits(full_d[:n])), n
+    d = ilp.linear_logp_backward(b.hidden[:64], b.weight, t[:64], full_ls[:64], b.grad[:64], m[:64])
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(d[2]).all()) and bool((f32bits(d[4]) == 0).all())
+    keep = [r for r in range(64) if r not in (2, 4)]
+    idx = torch.tensor(keep, device=dev)
+    sub_h, sub_t = b.hidden.index_select(0, idx), t.index_select(0, idx)
+    _, rlse = _oracle_fused(sub_h, b.weight, sub_t)
+    rd = oracle.linear_logp_backward(bits16(sub_h), bits16(b.weight), sub_t.cpu().numpy(), None,
+                                     rlse, b.grad.index_select(0, idx).cpu().numpy())
+    assert_close(d.index_select(0, idx).cpu().numpy(), rd, TOL_BWD,
+                 f"small batch dlogits {v}x{h} (end to end)")
+
+
 def test_fused_transforms_small(dev):
     n, v, h = 600, 1500, 192
     b = wl.fused_batch(n, v, h, seed=5, device=dev, w_sigma=0.05, n_masked=40)
@@ -200,7 +232,8 @@ def test_fused_backward_schedules(dev):
     against the oracle; dlogits of 64 whole rows (both ends of each 512-row
     chunk among them) element by element against the oracle's own gradient;
     one prefill launch vs 4 chunks of 512 vs 2048 single-row decode launches
-    give identical logp, lse and dlogits bits."""
+    give identical logp, lse and dlogits bits (dlogits of single rows and of
+    32- and 64-row batches on a subset)."""
     b = wl.fused_bwd(seed=0, device=dev)
     n = b.hidden.shape[0]
     logp, lse = ilp.linear_logp(b.hidden, b.weight, b.targets, b.mask)
@@ -239,6 +272,12 @@ def test_fused_backward_schedules(dev):
         d_r = ilp.linear_logp_backward(b.hidden[r:r + 1], b.weight, b.targets[r:r + 1],
                                        lse[r:r + 1], b.grad[r:r + 1], b.mask[r:r + 1])
         assert _bits_equal(d_r, d[r:r + 1]), r
+    # small batches (the small-batch backward) at this shape
+    for r0, k in ((100, 32), (1000, 64), (1984, 64)):
+        sl = slice(r0, r0 + k)
+        d_k = ilp.linear_logp_backward(b.hidden[sl], b.weight, b.targets[sl], lse[sl], b.grad[sl],
+                                       b.mask[sl])
+        assert _bits_equal(d_k, d[sl]), (r0, k)
 
 
 def test_binding_refuses_bad_outputs_and_workspaces(dev):
