@@ -107,11 +107,14 @@ def _hip_clock_mhz(dev_index):
     return None
 
 
-def measure_yardsticks(torch, dev, read_buf):
+def measure_yardsticks(torch, dev, read_buf, write_buf=None):
     """Attainable rates on this device, as yardsticks for the roofline
     fractions (comparison only: nothing of the library runs here).
       stream_read    a plain 16-byte nontemporal read of ``read_buf``
                      (yardstick/yardstick.hip), GB/s;
+      stream_widen   ``read_buf``'s bf16 elements written as fp32 into
+                     ``write_buf`` (read 2, write 4 bytes per element), GB/s
+                     of bytes read + written;
       mfma_loop      back-to-back bf16 MFMAs on registers, TFLOP/s, and the
                      shader clock it sustains (s_memtime against the 100 MHz
                      real-time counter), MHz;
@@ -142,6 +145,8 @@ def measure_yardsticks(torch, dev, read_buf):
                                              ctypes.c_void_p, ctypes.c_void_p]
         ys.yardstick_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p]
+        ys.yardstick_stream_widen.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                              ctypes.c_void_p]
         cus = torch.cuda.get_device_properties(dev).multi_processor_count
         nbytes = read_buf.numel() * read_buf.element_size()
         grid = cus * 16
@@ -149,6 +154,12 @@ def measure_yardsticks(torch, dev, read_buf):
         ms = ev_ms(lambda: ys.yardstick_stream_read(read_buf.data_ptr(), nbytes // 16, grid,
                                                     sink.data_ptr(), stream.cuda_stream), 5)
         out["stream_read"] = {"bytes": nbytes, "ms": ms, "GB_per_s": nbytes / (ms * 1e-3) / 1e9}
+        if write_buf is not None and read_buf.dtype == torch.bfloat16:
+            n4 = min(read_buf.numel(), write_buf.numel()) // 4
+            ms = ev_ms(lambda: ys.yardstick_stream_widen(read_buf.data_ptr(), n4, write_buf.data_ptr(),
+                                                         stream.cuda_stream), 3)
+            moved = n4 * 4 * (2 + 4)
+            out["stream_widen"] = {"bytes": moved, "ms": ms, "GB_per_s": moved / (ms * 1e-3) / 1e9}
         mgrid, iters = 2 * cus, 20000
         clocks = torch.zeros(4 * mgrid, dtype=torch.int64, device=dev)
         msink = torch.zeros(mgrid * 256, dtype=torch.float32, device=dev)
@@ -472,7 +483,8 @@ def main():
                            "GB_per_s_cold": gbs, "hbm_frac_cold": gbs / HBM_PEAK_GBS}
         del flush
 
-    ys = None if args.no_yardsticks else measure_yardsticks(torch, dev, c3.logits)
+    ys = None if args.no_yardsticks else measure_yardsticks(
+        torch, dev, c3.logits, d3 if "logits_bwd" in legs else None)
     clock = None
     if ys is not None:
         clock = {"max_mhz": ys.get("clock_max_mhz"),
@@ -481,6 +493,13 @@ def main():
             att = ys["stream_read"]["GB_per_s"]
             roofline.update({"attainable": att, "attainable_kind": "plain streaming read",
                              "frac_attainable": roofline["achieved"] / att})
+        if "stream_widen" in ys:
+            # read-2 / write-4 bytes per element passes against the widening copy
+            att = ys["stream_widen"]["GB_per_s"]
+            for rec in (out_legs.get("logits_bwd"), extra.get("log_softmax")):
+                if isinstance(rec, dict) and "GB_per_s" in rec:
+                    rec["attainable_stream_widen"] = att
+                    rec["frac_attainable_stream_widen"] = rec["GB_per_s"] / att
     fused_roof = None
     if "fused_fwd" in out_legs:
         tf = out_legs["fused_fwd"]["TFLOP_per_s"]

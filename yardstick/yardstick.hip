@@ -3,6 +3,12 @@
 //   stream_read : a plain read of a buffer (16-byte nontemporal loads, a
 //                 grid-stride loop, an XOR of the words), the attainable HBM
 //                 read rate;
+//   stream_widen: reads bf16 elements and writes each widened to fp32 (8-byte
+//                 nontemporal loads, 16-byte nontemporal stores, one
+//                 workgroup per 16 KB written, each XCD walking one
+//                 contiguous eighth): the attainable rate of a pass that
+//                 reads 2 and writes 4 bytes per element, the traffic of the
+//                 logits backward and of the dense log-softmax;
 //   mfma_loop   : back-to-back v_mfma_f32_32x32x16_bf16 on register operands
 //                 (four independent accumulators per wave, two waves per
 //                 SIMD), the attainable bf16 matrix rate with no memory
@@ -33,6 +39,38 @@ __global__ __launch_bounds__(256) void stream_read(const u32x4_t* __restrict__ p
     for (int u = 0; u < 8; ++u) acc ^= w[u].x ^ w[u].y ^ w[u].z ^ w[u].w;
   }
   if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;  // keeps the loads; practically never taken
+}
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// One workgroup per block of 1024 groups (8 KB read, 16 KB written).
+// Workgroups are dispatched round-robin over the 8 XCDs; block ids are
+// regrouped so that each XCD walks one contiguous eighth of the buffer, and
+// the blocks in flight on an XCD are neighbours (long sequential write runs).
+__global__ __launch_bounds__(256) void stream_widen(const u32x2_t* __restrict__ in, int64_t n4,
+                                                    f32x4_t* __restrict__ out) {
+  const int64_t total = static_cast<int64_t>(gridDim.x);
+  const int64_t t8 = (total / 8) * 8;
+  const int64_t w = blockIdx.x;
+  const int64_t blk = (w < t8) ? (w & 7) * (t8 / 8) + (w >> 3) : w;
+  const int64_t base = blk * 1024;
+  u32x2_t v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t k = base + u * 256 + threadIdx.x;
+    v[u] = (u32x2_t){0u, 0u};
+    if (k < n4) v[u] = __builtin_nontemporal_load(in + k);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t k = base + u * 256 + threadIdx.x;
+    if (k < n4) {
+      const f32x4_t f = {__uint_as_float(v[u].x << 16), __uint_as_float(v[u].x & 0xffff0000u),
+                         __uint_as_float(v[u].y << 16), __uint_as_float(v[u].y & 0xffff0000u)};
+      __builtin_nontemporal_store(f, out + k);
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void mfma_loop(int iters, uint64_t* __restrict__ clocks,
@@ -73,6 +111,16 @@ extern "C" {
 int yardstick_stream_read(const void* p, int64_t n16, int grid, uint32_t* sink, hipStream_t s) {
   hipLaunchKernelGGL(stream_read, dim3(grid), dim3(256), 0, s, static_cast<const u32x4_t*>(p), n16,
                      sink);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+// Reads n4 groups of 4 bf16 at in and writes them as n4 groups of 4 fp32 at
+// out (16-byte aligned): one workgroup of 256 threads per 1024 groups.
+int yardstick_stream_widen(const void* in, int64_t n4, void* out, hipStream_t s) {
+  const int64_t grid = (n4 + 1023) / 1024;
+  if (grid <= 0 || grid > 0x7fffffff) return 1;
+  hipLaunchKernelGGL(stream_widen, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, s,
+                     static_cast<const u32x2_t*>(in), n4, static_cast<f32x4_t*>(out));
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
