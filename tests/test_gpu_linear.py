@@ -34,7 +34,8 @@ def _oracle_fused(hidden, weight, targets, mask=None):
                               None if mask is None else mask.cpu().numpy())
 
 
-@pytest.mark.parametrize("n,v,h", [(1, 256, 64), (37, 1000, 136), (300, 2600, 512), (257, 513, 8)])
+@pytest.mark.parametrize("n,v,h", [(1, 256, 64), (37, 1000, 136), (300, 2600, 512), (257, 513, 8),
+                                   (3, 1, 8), (40, 9, 16), (64, 257, 8)])
 def test_small_parity_fwd_bwd(dev, n, v, h):
     b = wl.fused_batch(n, v, h, seed=n + v + h, device=dev, w_sigma=0.05, n_masked=n // 10)
     logp, lse = ilp.linear_logp(b.hidden, b.weight, b.targets, b.mask)
