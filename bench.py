@@ -393,7 +393,7 @@ def main():
         xflops["fused_fb_kept_logits"] = 2.0 * n5 * v5 * h5
     if c4 is not None and "fused_fwd_n1" in args.extra_legs.split(","):
         # one row of the fused forward workload: the row's reduction schedule
-        # is that of any N (batches of at most 64 rows take a smaller launch),
+        # is that of any N (batches of at most 128 rows take a smaller launch),
         # and the W stream (V x H bf16) is the algorithmic traffic that bounds it
         h41, t41, m41 = c4.hidden[:1], c4.targets[:1], c4.mask[:1]
         lp41 = torch.empty(1, dtype=torch.float32, device=dev)

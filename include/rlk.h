@@ -138,7 +138,7 @@ size_t rlk_linear_logp_workspace_size(int64_t N, int64_t V, int64_t H);
  * z_i = W . h_i computed with bf16 MFMA and fp32 accumulation in a fixed K
  * order, never rounded to bf16, reduced by an online log-sum-exp per
  * 256-wide vocabulary chunk; chunk partials are merged per row in ascending
- * chunk order.  A batch of at most 64 rows runs the same per-row instruction
+ * chunk order.  A batch of at most 128 rows runs the same per-row instruction
  * sequence in a smaller launch (the same bits as inside a large batch).
  *   hidden : bf16 [N, ld_h], ld_h >= H, ld_h % 8 == 0, 16-B aligned.
  *   weight : bf16 [V, ld_w] (nn.Linear layout, H contiguous), ld_w >= H,
@@ -190,7 +190,7 @@ int rlk_linear_logp_noalloc(const void* hidden, int64_t ld_h,
  *   Fused mode  : `logits` NULL; x_i = W . h_i is recomputed with exactly
  *                 the tiles and K order rlk_linear_logp uses (hidden
  *                 [N, ld_h], weight [V, ld_w], H as there); a batch of
- *                 at most 64 rows runs the same per-row instruction
+ *                 at most 128 rows runs the same per-row instruction
  *                 sequence in a smaller launch (the same bits).
  *   lse        : fp32 [N], required -- the forward's output for these rows.
  *   grad_logp  : fp32 [N], required (the upstream gradient g).

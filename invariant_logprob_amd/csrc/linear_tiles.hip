@@ -26,7 +26,7 @@
 // section "Workstream 3 - #153", scope item 2); bf16 inputs with fp32
 // accumulation (same page, "Workstream 1 - #154" scope table).  The tile
 // schedule, the MFMA instruction and the K order never depend on N (a batch
-// of at most 64 rows runs the same per-row sequence in a smaller launch, in
+// of at most 128 rows runs the same per-row sequence in a smaller launch, in
 // the forward and in the backward).
 //
 // The backward kernel runs the same per-tile main loop (same copies, same
@@ -379,8 +379,8 @@ void linear_tiles_fwd(TileArgs args) {
   }
 }
 
-// Small batches (at most 64 token rows).  All rows lie in token quarter 0 of
-// a tile (its first 32 or 64 rows, NJ = 1 or 2 block columns), so of the
+// Small batches (at most 128 token rows).  All rows lie in the first 32, 64
+// or 128 token columns of a tile (NJ = 1, 2 or 4 blocks of 32), so of the
 // tile's MFMA work only the blocks (i, j < NJ) matter, and the tile is bound
 // by streaming its 256 W rows.  The small-batch kernels run exactly those
 // blocks -- the same fragments, the same v_mfma_f32_32x32x16_bf16 sequence
@@ -391,12 +391,14 @@ void linear_tiles_fwd(TileArgs args) {
 // of the full tile kernels.  What differs is the launch: one workgroup of
 // 2 NJ waves per 256-entry vocabulary tile, wave (wv, jw) owning the blocks
 // (i, jw) of vocabulary half wv; W reaches the LDS through registers
-// (16-byte loads, eight lanes per 128-byte row segment, the next stage's
-// loads in flight while this stage is consumed) instead of direct-to-LDS
-// copies, which stream this pattern about a sixth slower; and the LDS holds
-// one stage of W and of the batch's hidden rows (36 or 40 KB), so four (NJ =
-// 1) or three (NJ = 2) workgroups fit on a compute unit and a vocabulary of
-// up to 1024 or 768 tiles streams in a single round.
+// (16-byte buffer loads, eight lanes per 128-byte row segment, the next
+// stage's loads in flight while this stage is consumed) instead of
+// direct-to-LDS copies, which stream this pattern about a sixth slower; and
+// the LDS holds one stage of W and of the batch's hidden rows (36, 40 or
+// 48 KB), so four, three or two workgroups fit on a compute unit and a
+// vocabulary of up to 1024, 768 or 512 tiles streams in a single round.
+constexpr int kAuxNontemporal = 2;  // cache-policy bits of a buffer load: nt
+
 template <int NJ>
 struct SmallGeo {
   static constexpr int kWaves = 2 * NJ;
@@ -407,29 +409,28 @@ struct SmallGeo {
   static constexpr int kStageVec = kWVec + kHVec;
   static constexpr int kWLoads = kWVec / 64 / kWaves;    // 16-byte loads per lane and stage
   static constexpr int kHLoads = kHVec / 64 / kWaves;
-  static constexpr int kPerCU = NJ == 1 ? 4 : 3;         // workgroups per compute unit
+  static constexpr int kPerCU = NJ == 1 ? 4 : (NJ == 2 ? 3 : 2);  // workgroups per CU
   static constexpr int kWavesPerSimd = kPerCU * kWaves / 4;
   static_assert(kPerCU * kStageVec * 16 <= 160 * 1024, "LDS of the resident workgroups");
   static_assert(kWLoads * 64 * kWaves == kWVec && kHLoads * 64 * kWaves == kHVec, "load split");
 };
 
 // One operand's part of a stage for this lane: chunk idx = (wave * n + q) *
-// 64 + lane of the stage, row idx / 8, logical chunk idx % 8; rows at or
-// past `rows` and chunks at or past K read as zero.  W is read once
-// (streaming hint); the hidden rows are read by every tile (cached).
-template <bool kStream, int NL>
-__device__ __forceinline__ void small_load(uint4 (&v)[NL], const uint16_t* base, int64_t ld,
-                                           int rows, int wave, int lane, int k0, int K) {
+// 64 + lane of the stage, that is row 8 (wave * n + q) + lane / 8, logical
+// chunk lane % 8.  A buffer load whose resource ends after the operand's
+// last present row (so rows past it read as zero); the lane's byte offset
+// within its row group is fixed (voff), the row group and the K position go
+// in the scalar offset.  Chunks at or past K are zeroed after the load.  W is
+// read once (nontemporal); the hidden rows are read by every tile (cached).
+template <int kAux, int NL>
+__device__ __forceinline__ void small_load(uint4 (&v)[NL], __amdgpu_buffer_rsrc_t res, int voff,
+                                           int group_bytes, int wave, int lane, int k0, int K) {
+  const bool in_k = k0 + 8 * (lane & 7) < K;
+  const int s0 = __builtin_amdgcn_readfirstlane(wave * NL * group_bytes + 2 * k0);
 #pragma unroll
   for (int q = 0; q < NL; ++q) {
-    const int idx = (wave * NL + q) * 64 + lane;
-    const int r = idx / kRowChunks;
-    const int c = idx % kRowChunks;
-    v[q] = make_uint4(0u, 0u, 0u, 0u);
-    if (r < rows && k0 + 8 * c < K) {
-      const uint16_t* p = base + r * ld + k0 + 8 * c;
-      v[q] = kStream ? load16_stream(p) : *reinterpret_cast<const uint4*>(p);
-    }
+    const auto w = __builtin_amdgcn_raw_buffer_load_b128(res, voff, s0 + q * group_bytes, kAux);
+    v[q] = in_k ? make_uint4(w[0], w[1], w[2], w[3]) : make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
@@ -457,7 +458,14 @@ __device__ __forceinline__ void small_mainloop(uint4* smem, const TileArgs& args
   using G = SmallGeo<NJ>;
   const int wv = wave & 1;
   const int jw = wave >> 1;
-  const uint16_t* wbase = args.weight + static_cast<int64_t>(vocab0) * args.ldw;
+  // W rows past V and hidden rows past N lie outside the resources' ranges
+  const __amdgpu_buffer_rsrc_t wres =
+      uniform_rsrc(args.weight + static_cast<int64_t>(vocab0) * args.ldw, V_tail * args.ldw * 2);
+  const __amdgpu_buffer_rsrc_t hres = uniform_rsrc(args.hidden, N * args.ldh * 2);
+  const int wgrp = static_cast<int>(args.ldw) * 16;  // bytes of 8 rows
+  const int hgrp = static_cast<int>(args.ldh) * 16;
+  const int wvoff = (lane >> 3) * static_cast<int>(args.ldw) * 2 + 16 * (lane & 7);
+  const int hvoff = (lane >> 3) * static_cast<int>(args.ldh) * 2 + 16 * (lane & 7);
 #pragma unroll
   for (int i = 0; i < kI; ++i)
 #pragma unroll
@@ -465,16 +473,16 @@ __device__ __forceinline__ void small_mainloop(uint4* smem, const TileArgs& args
   const int K = args.H;
   const int n_kt = (K + kBK - 1) / kBK;
   uint4 wr[G::kWLoads], hr[G::kHLoads];
-  small_load<true>(wr, wbase, args.ldw, V_tail, wave, lane, 0, K);
-  small_load<false>(hr, args.hidden, args.ldh, N, wave, lane, 0, K);
+  small_load<kAuxNontemporal>(wr, wres, wvoff, wgrp, wave, lane, 0, K);
+  small_load<0>(hr, hres, hvoff, hgrp, wave, lane, 0, K);
   const uint4* a = smem;
   const uint4* b = smem + G::kWVec;
   for (int kt = 0; kt < n_kt; ++kt) {
     small_store(smem, wr, wave, lane);
     small_store(smem + G::kWVec, hr, wave, lane);
     if (kt + 1 < n_kt) {
-      small_load<true>(wr, wbase, args.ldw, V_tail, wave, lane, (kt + 1) * kBK, K);
-      small_load<false>(hr, args.hidden, args.ldh, N, wave, lane, (kt + 1) * kBK, K);
+      small_load<kAuxNontemporal>(wr, wres, wvoff, wgrp, wave, lane, (kt + 1) * kBK, K);
+      small_load<0>(hr, hres, hvoff, hgrp, wave, lane, (kt + 1) * kBK, K);
     }
     __syncthreads();
 #pragma unroll
@@ -532,50 +540,72 @@ void linear_tiles_fwd_small(TileArgs args) {
   }
 }
 
-// Backward for a batch of at most 64 token rows: the small-batch main loop
-// (the same logits as linear_tiles_bwd's, bit for bit), then each lane writes
-// its dlogits straight from the accumulators (dlogits_quad, the same formula
-// as the full tile's epilogue), 16 bytes at a time; a token's row gets 32
-// contiguous bytes per store instruction from the two lane halves.  At these
-// batch sizes the output is small beside the W stream.
+// Backward for a small batch: the small-batch main loop (the same logits as
+// linear_tiles_bwd's, bit for bit), then the dlogits of each wave's 128 x 32
+// block (dlogits_quad, the same formula as the full tile's epilogue),
+// staged through the LDS in two passes of 64 vocabulary rows so that each
+// store instruction writes four 256-byte row segments.
+constexpr int kSmallStageStride = 68;  // floats per staged token row (64 + 4 pad)
+
 template <int NJ>
 __global__ __launch_bounds__(SmallGeo<NJ>::kThreads)
 __attribute__((amdgpu_waves_per_eu(SmallGeo<NJ>::kWavesPerSimd)))
 void linear_tiles_bwd_small(TileArgs args) {
   using G = SmallGeo<NJ>;
-  __shared__ uint4 smem[G::kStageVec];
+  constexpr int kStagingVec = G::kWaves * 32 * kSmallStageStride / 4;
+  constexpr int kSmemVec = G::kStageVec > kStagingVec ? G::kStageVec : kStagingVec;
+  static_assert(G::kPerCU * kSmemVec * 16 <= 160 * 1024, "LDS of the resident workgroups");
+  __shared__ uint4 smem[kSmemVec];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wv = wave & 1;  // vocabulary half of the tile
+  const int jw = wave >> 1;  // token block of the wave
   const int vt = blockIdx.x;
   const int vocab0 = vt * kBV;
   const int V_tail = min(args.V - vocab0, kBV);
   const int N = static_cast<int>(args.N);  // at most G::kRows
   const int half = lane >> 5;
   const int vlane = vocab0 + wv * kPW + 4 * half;  // this lane's first vocabulary row
-  const int tl = (wave >> 1) * 32 + (lane & 31);   // this lane's token row
+  const int tl = jw * 32 + (lane & 31);            // this lane's token row
   const DlogitsColumn col = dlogits_column(args, tl < N, tl, vlane);
   f32x16_t acc[kI][1];
   small_mainloop<NJ>(smem, args, wave, lane, vocab0, V_tail, N, acc);
-  if (tl >= N) return;
-  float* drow = args.dl + static_cast<int64_t>(tl) * args.ldg + vlane;
+
+  // the main loop ended with a barrier: the whole LDS is free
+  float* stage = reinterpret_cast<float*>(smem) + wave * (32 * kSmallStageStride);
+  float* srow = stage + (lane & 31) * kSmallStageStride;
 #pragma unroll
-  for (int i = 0; i < kI; ++i)
+  for (int p = 0; p < 2; ++p) {
+    // blocks 2p and 2p + 1: vocabulary rows wv * 128 + 64 p .. + 63
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 d = dlogits_quad(acc[i][0], i, q, col);
-      const int m = vlane - vocab0 + i * 32 + 8 * q;  // relative to vocab0
-      float* dst = drow + i * 32 + 8 * q;
-      if (m + 4 <= V_tail) {
-        store16_stream(dst, d.x, d.y, d.z, d.w);
-      } else {
-        const float dd[4] = {d.x, d.y, d.z, d.w};
+    for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (m + e < V_tail) dst[e] = dd[e];
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(srow + ii * 32 + 8 * q + 4 * half) =
+            dlogits_quad(acc[2 * p + ii][0], 2 * p + ii, q, col);
+    __syncthreads();
+#pragma unroll
+    for (int step = 0; step < 8; ++step) {
+      const int r = 4 * step + (lane >> 4);  // staged token row
+      const int c4 = lane & 15;
+      const int tr = jw * 32 + r;
+      if (tr < N) {
+        const float4 v = *reinterpret_cast<const float4*>(stage + r * kSmallStageStride + 4 * c4);
+        const int m = wv * kPW + 64 * p + 4 * c4;  // relative to vocab0
+        float* dst = args.dl + static_cast<int64_t>(tr) * args.ldg + vocab0 + m;
+        if (m + 4 <= V_tail) {
+          store16_stream(dst, v.x, v.y, v.z, v.w);
+        } else {
+          const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (m + e < V_tail) dst[e] = vv[e];
+        }
       }
     }
+    __syncthreads();
+  }
 }
 
 // One wave per row: lane l merges the row's chunk partials l, l + 64,
@@ -676,6 +706,9 @@ hipError_t launch_linear_logp(const uint16_t* hidden, int64_t ldh, const uint16_
   else if (N <= SmallGeo<2>::kRows)
     hipLaunchKernelGGL(linear_tiles_fwd_small<2>, dim3(static_cast<uint32_t>(a.n_vtiles)),
                        dim3(SmallGeo<2>::kThreads), 0, stream, a);
+  else if (N <= SmallGeo<4>::kRows)
+    hipLaunchKernelGGL(linear_tiles_fwd_small<4>, dim3(static_cast<uint32_t>(a.n_vtiles)),
+                       dim3(SmallGeo<4>::kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(linear_tiles_fwd<false>, dim3(tiles), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
@@ -704,6 +737,9 @@ hipError_t launch_linear_dlogits(const uint16_t* hidden, int64_t ldh, const uint
   else if (N <= SmallGeo<2>::kRows)
     hipLaunchKernelGGL(linear_tiles_bwd_small<2>, dim3(static_cast<uint32_t>(a.n_vtiles)),
                        dim3(SmallGeo<2>::kThreads), 0, stream, a);
+  else if (N <= SmallGeo<4>::kRows)
+    hipLaunchKernelGGL(linear_tiles_bwd_small<4>, dim3(static_cast<uint32_t>(a.n_vtiles)),
+                       dim3(SmallGeo<4>::kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(linear_tiles_bwd, dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0,
                        stream, a);

@@ -6,7 +6,7 @@
 // batch shape cannot change a row's bits (page "[RFC] Batch-Invariant RL
 // Kernel Suite for Train-Inference Consistency", section "Problem": dispatch
 // by shape is one of the named drift sources).  The one choice N makes is the
-// fused kernels' launch form for batches of at most 64 rows, which runs the
+// fused kernels' launch form for batches of at most 128 rows, which runs the
 // full tile's instruction sequence for those rows and yields the same bits.
 // No allocation, no synchronisation, no mutable state.
 #include <hip/hip_runtime.h>
@@ -367,7 +367,7 @@ const char* rlk_status_string(int status) {
 const char* rlk_build_info(void) {
   return "rlk 0.1.0; arch=gfx950; rev=" RLK_GIT_REV
          "; schedule=rows:256thr,4x16B/lane-step,whole-row-if<=4steps,bfly:pl32,pl16,ror8,hmir,qp2,qp1; bwd:128thr,4x8B,xcd-ordered; tile:" RLK_STR(256) "x" RLK_STR(
-             256) "x" RLK_STR(64) ",8waves,mfma32x32x16bf16,2stage,group8,wg-per-tile; fused-n<=64:2-4waves,reg-staged-w,1stage,3-4wg-per-cu; combine:wave-per-row; grads:chunk" RLK_STR(16384) ",dl-bf16x2,kmajor-tr16";
+             256) "x" RLK_STR(64) ",8waves,mfma32x32x16bf16,2stage,group8,wg-per-tile; fused-n<=128:2-8waves,reg-staged-w,1stage,2-4wg-per-cu; combine:wave-per-row; grads:chunk" RLK_STR(16384) ",dl-bf16x2,kmajor-tr16";
 }
 
 }  // extern "C"

@@ -107,20 +107,20 @@ def test_tile_offset_sweep(dev):
 
 @pytest.mark.parametrize("v,h", [(1300, 136), (777, 72), (2600, 4096)])
 def test_small_batch_forward_bits(dev, v, h):
-    """Batches of at most 64 rows take the small-batch forward (register-staged
-    W, two waves per tile, 32 or 64 token rows); each of their rows must carry
-    the bits the same row gets inside a 300-row batch (the full tile
-    forward), around both switches (N = 1, 2, 31, 32, 33, 63, 64, 65), with a
-    ragged last vocabulary tile and a ragged last K stage, a masked row and
-    an invalid target among them; and the small batches agree with the
-    oracle."""
+    """Batches of at most 128 rows take the small-batch forward (register-staged
+    W, 2, 4 or 8 waves per tile, 32, 64 or 128 token rows); each of their rows
+    must carry the bits the same row gets inside a 300-row batch (the full
+    tile forward), around every switch (N = 1, 2, 31, 32, 33, 63, 64, 65, 100,
+    127, 128, 129), with a ragged last vocabulary tile and a ragged last K
+    stage, a masked row and an invalid target among them; and the small
+    batches agree with the oracle."""
     b = wl.fused_batch(300, v, h, seed=v + h, device=dev, w_sigma=0.05)
     t = b.targets.clone()
     t[2] = v + 5                      # invalid target on an active row
     m = b.mask.clone()
     m[4] = 0                          # masked row
     full_lp, full_ls = ilp.linear_logp(b.hidden, b.weight, t, m)
-    for n in (1, 2, 31, 32, 33, 63, 64, 65):
+    for n in (1, 2, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129):
         lp, ls = ilp.linear_logp(b.hidden[:n], b.weight, t[:n], m[:n])
         assert torch.equal(f32bits(lp), f32bits(full_lp[:n])), n
         assert torch.equal(f32bits(ls), f32bits(full_ls[:n])), n
@@ -135,7 +135,7 @@ def test_small_batch_forward_bits(dev, v, h):
 
 @pytest.mark.parametrize("v,h", [(1300, 136), (777, 72), (2600, 4096)])
 def test_small_batch_backward_bits(dev, v, h):
-    """Batches of at most 64 rows take the small-batch backward (the small
+    """Batches of at most 128 rows take the small-batch backward (the small
     forward's main loop, dlogits stored from the accumulators); each of their
     dlogits rows must carry the bits the same row gets inside a 300-row batch
     (the full tile backward), around both switches, with a ragged last
@@ -149,7 +149,7 @@ def test_small_batch_backward_bits(dev, v, h):
     m[4] = 0                          # masked row
     _, full_ls = ilp.linear_logp(b.hidden, b.weight, t, m)
     full_d = ilp.linear_logp_backward(b.hidden, b.weight, t, full_ls, b.grad, m)
-    for n in (1, 2, 31, 32, 33, 63, 64, 65):
+    for n in (1, 2, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129):
         d = ilp.linear_logp_backward(b.hidden[:n], b.weight, t[:n], full_ls[:n], b.grad[:n], m[:n])
         assert torch.equal(f32bits(d), f32bits(full_d[:n])), n
     d = ilp.linear_logp_backward(b.hidden[:64], b.weight, t[:64], full_ls[:64], b.grad[:64], m[:64])
