@@ -119,7 +119,8 @@ def measure_yardsticks(torch, dev, read_buf, write_buf=None):
                      shader clock it sustains (s_memtime against the 100 MHz
                      real-time counter), MHz;
       gemm           torch's bf16 GEMM (hipBLASLt) on the two fused shapes,
-                     fp32 output where torch offers it, TFLOP/s."""
+                     fp32 output where torch offers it, and with bf16 output
+                     and W as the row side (``bf16_out_w_rows``), TFLOP/s."""
     import ctypes
 
     import numpy as np
@@ -185,8 +186,12 @@ def measure_yardsticks(torch, dev, read_buf, write_buf=None):
             fn = lambda: a @ w.t()
             odt = "bf16"
         ms = ev_ms(fn, 3)
-        out["gemm"][f"{n}x{v}x{h}"] = {"ms": ms, "out": odt,
-                                       "TFLOP_per_s": 2.0 * n * v * h / (ms * 1e-3) / 1e12}
+        rec = {"ms": ms, "out": odt, "TFLOP_per_s": 2.0 * n * v * h / (ms * 1e-3) / 1e12}
+        # the same product with bf16 output and W as the row side (z^T = W h^T), the
+        # fastest form hipBLASLt offers for these shapes: the least output traffic
+        ms = ev_ms(lambda: w @ a.t(), 3)
+        rec["bf16_out_w_rows"] = {"ms": ms, "TFLOP_per_s": 2.0 * n * v * h / (ms * 1e-3) / 1e12}
+        out["gemm"][f"{n}x{v}x{h}"] = rec
         del a, w
     torch.cuda.synchronize()
     return out
@@ -519,6 +524,8 @@ def main():
             if gemm:
                 fused_roof["gemm_yardstick"] = gemm["TFLOP_per_s"]
                 fused_roof["frac_gemm_yardstick"] = tf / gemm["TFLOP_per_s"]
+                fused_roof["gemm_yardstick_bf16_out"] = gemm["bf16_out_w_rows"]["TFLOP_per_s"]
+                fused_roof["frac_gemm_yardstick_bf16_out"] = tf / gemm["bf16_out_w_rows"]["TFLOP_per_s"]
 
     cpu = None
     if not args.no_cpu_baseline and "logits_fwd" in legs:
