@@ -2,8 +2,9 @@
 the fp64 oracle: logits forward and backward, fused forward, recomputing and
 kept-logits backward, and the parameter gradients.  Each case draws N, V, H,
 a padded leading dimension (its padding filled with NaN, which must never be
-read), a mask and a logit scale; two of its rows are then recomputed alone
-and must give the same bits (the I-relation under population change).
+read), a mask and a logit scale; two of its rows are then recomputed alone,
+and for the fused path a random contiguous run of 2..160 rows as its own
+batch, and must give the same bits (the I-relation under population change).
 Gradient references are the oracle's, from the inputs alone (its own lse)."""
 import numpy as np
 import pytest
@@ -120,3 +121,14 @@ def test_fused_path_random_shape(dev, seed):
         assert torch.equal(f32bits(ls1), f32bits(lse[i:i + 1])), (what, i)
         assert torch.equal(f32bits(d1), f32bits(d[i:i + 1])), (what, i)
         assert torch.equal(f32bits(gh1), f32bits(gh[i:i + 1])), (what, i)
+    # a random contiguous sub-batch of 2..160 rows (any launch form of the fused kernels)
+    if n >= 2:
+        k = int(r.integers(2, min(n, 160) + 1))
+        s0 = int(r.integers(0, n - k + 1))
+        sl = slice(s0, s0 + k)
+        lpk, lsk = ilp.linear_logp(hid[sl], w, t[sl], mask[sl])
+        dkk = ilp.linear_logp_backward(hid[sl], w, t[sl], lsk, g[sl], mask[sl])
+        torch.cuda.synchronize()
+        assert torch.equal(f32bits(lpk), f32bits(logp[sl])), (what, s0, k)
+        assert torch.equal(f32bits(lsk), f32bits(lse[sl])), (what, s0, k)
+        assert torch.equal(f32bits(dkk), f32bits(d[sl])), (what, s0, k)
